@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module creates bf16 tensors (as uint16 bit arrays) of the lm_head shapes
+and value distributions the workloads use.  It holds none of the method's
+arithmetic: no scale, no rounding to E2M1/E4M3, no dequantization.  Its one
+numeric step is rounding float32 draws to bf16 (round to nearest even), which
+is how the synthetic weights and activations come into existence.
+
+Recipe (numpy PCG64 ``default_rng``):
+
+* The tiny weight uses ``default_rng(0)``; every other tensor uses
+  ``default_rng([cfg, stream])`` with cfg 1..5 and stream 0 = weight,
+  1 = outlier mask, 2 = activations, 3 = refresh noise, 4 = bias.
+* Normal draws are float32 ``standard_normal`` generated row chunk by row
+  chunk (``CHUNK_ROWS`` rows at a time, sequentially from one generator),
+  multiplied by the float32 standard deviation, then rounded to bf16.
+* Llama-3-8B shape: exactly ``round(0.001 * N * K)`` distinct positions, drawn
+  with ``choice(N * K, count, replace=False)``, are multiplied by 20 before the
+  bf16 rounding.
+* Heavy-tailed: ``0.01 * standard_t(3)`` drawn in float64, rounded to float32
+  then bf16; row 0 is all zero; row N-1 repeats a pattern of E2M1 grid values
+  in which every 16-block holds +-6 and both +0 and -0.
+* 70B refresh: ``W' = bf16(float32(W) + 1e-3 * standard_normal)``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+CHUNK_ROWS = 8192
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg: int            # seed namespace
+    n: int              # vocab rows
+    k: int              # hidden size
+    sigma: float        # weight standard deviation
+    ms: tuple           # activation row counts measured
+    m_draw: int         # activation rows drawn (x[:m] is used for each m)
+    kind: str = "normal"   # "normal" | "outliers" | "heavy"
+    description: str = ""
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1024, 512, 0.02, (4,), 4,
+                     description="weight 1024x512 N(0,0.02) seed 0; x 4x512 N(0,1)"),
+    "llama3_8b": Workload("llama3_8b", 2, 128256, 4096, 0.02, (1, 8, 32, 64), 64, "outliers",
+                          description="lm_head 128256x4096 N(0,0.02) + 0.1% entries x20; "
+                                      "decode M in {1,8,32,64}"),
+    "llama3_70b": Workload("llama3_70b", 3, 128256, 8192, 0.015, (1, 16, 64), 64,
+                           description="lm_head 128256x8192 N(0,0.015); M in {1,16,64}; "
+                                       "refresh after N(0,1e-3) noise"),
+    "qwen_prefill": Workload("qwen_prefill", 4, 151936, 5120, 0.02, (4096,), 4096,
+                             description="lm_head 151936x5120 N(0,0.02); prefill M=4096"),
+    "heavy_tail": Workload("heavy_tail", 5, 129280, 7168, 0.01, (8192, 1), 8192, "heavy",
+                           description="lm_head 129280x7168 0.01*t(3), zero row 0, "
+                                       "E2M1-grid row N-1; M=8192 and M=1"),
+}
+
+
+def f32_to_bf16_bits(f: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(f, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(cfg: int, stream: int, tiny_weight: bool = False) -> np.random.Generator:
+    if tiny_weight:
+        return np.random.default_rng(0)
+    return np.random.default_rng([cfg, stream])
+
+
+def normal_bits(n: int, k: int, sigma: float, rng: np.random.Generator) -> np.ndarray:
+    """bf16 bits of ``sigma * N(0,1)`` float32 draws, row chunk by row chunk."""
+    out = np.empty((n, k), dtype=np.uint16)
+    s = np.float32(sigma)
+    for r0 in range(0, n, CHUNK_ROWS):
+        r1 = min(n, r0 + CHUNK_ROWS)
+        out[r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, k), dtype=np.float32) * s)
+    return out
+
+
+def weight_bits(w: Workload) -> np.ndarray:
+    """The workload's bf16 weight [N, K] as uint16 bits."""
+    if w.kind == "heavy":
+        return _heavy_weight(w)
+    rng = _rng(w.cfg, 0, tiny_weight=(w.name == "tiny"))
+    if w.kind != "outliers":
+        return normal_bits(w.n, w.k, w.sigma, rng)
+    count = int(round(0.001 * w.n * w.k))
+    pos = np.sort(_rng(w.cfg, 1).choice(w.n * w.k, size=count, replace=False))
+    out = np.empty((w.n, w.k), dtype=np.uint16)
+    s = np.float32(w.sigma)
+    for r0 in range(0, w.n, CHUNK_ROWS):
+        r1 = min(w.n, r0 + CHUNK_ROWS)
+        f = rng.standard_normal((r1 - r0, w.k), dtype=np.float32) * s
+        lo, hi = np.searchsorted(pos, [r0 * w.k, r1 * w.k])
+        flat = f.reshape(-1)
+        flat[pos[lo:hi] - r0 * w.k] *= np.float32(20.0)
+        out[r0:r1] = f32_to_bf16_bits(f)
+    return out
+
+
+def grid_row_bits(k: int) -> np.ndarray:
+    """Row of E2M1 grid values: +G[k%8] for k%16 < 8, else -G[k%8] (with -0.0)."""
+    g = np.array([6.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 0.0], dtype=np.float32)
+    idx = np.arange(k)
+    vals = g[idx % 8]
+    vals = np.where(idx % 16 < 8, vals, -vals).astype(np.float32)
+    return f32_to_bf16_bits(vals)
+
+
+def _heavy_weight(w: Workload) -> np.ndarray:
+    rng = _rng(w.cfg, 0)
+    out = np.empty((w.n, w.k), dtype=np.uint16)
+    for r0 in range(0, w.n, CHUNK_ROWS):
+        r1 = min(w.n, r0 + CHUNK_ROWS)
+        t = rng.standard_t(3, size=(r1 - r0, w.k)) * w.sigma
+        out[r0:r1] = f32_to_bf16_bits(t.astype(np.float32))
+    out[0] = 0
+    out[w.n - 1] = grid_row_bits(w.k)
+    return out
+
+
+def activation_bits(w: Workload, m: int | None = None) -> np.ndarray:
+    """bf16 activations x[:m] of the workload's N(0,1) draw [m_draw, K]."""
+    rng = _rng(w.cfg, 2)
+    x = normal_bits(w.m_draw, w.k, 1.0, rng)
+    return x if m is None else x[:m]
+
+
+def refresh_weight_bits(w: Workload, w_bits: np.ndarray, sigma: float = 1e-3) -> np.ndarray:
+    """``bf16(float32(W) + sigma * N(0,1))`` for the in-place refresh workload."""
+    rng = _rng(w.cfg, 3)
+    out = np.empty_like(w_bits)
+    s = np.float32(sigma)
+    for r0 in range(0, w_bits.shape[0], CHUNK_ROWS):
+        r1 = min(w_bits.shape[0], r0 + CHUNK_ROWS)
+        noise = rng.standard_normal((r1 - r0, w_bits.shape[1]), dtype=np.float32) * s
+        out[r0:r1] = f32_to_bf16_bits(bf16_bits_to_f32(w_bits[r0:r1]) + noise)
+    return out
+
+
+def bias_bits(n: int, seed: int = 0, sigma: float = 1.0) -> np.ndarray:
+    return normal_bits(1, n, sigma, np.random.default_rng([seed, 4]))[0]
+
+
+def random_weight_bits(n: int, k: int, sigma: float = 0.02, seed: int = 0) -> np.ndarray:
+    """Ad-hoc shapes for edge-case tests (ragged N and K, tiny sizes)."""
+    return normal_bits(n, k, sigma, np.random.default_rng([100, seed, n, k]))
+
+
+def random_activation_bits(m: int, k: int, seed: int = 0) -> np.ndarray:
+    return normal_bits(m, k, 1.0, np.random.default_rng([101, seed, m, k]))
