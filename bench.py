@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 W4A16 lm_head hot path on one MI355X.
+
+One step = one pass of the whole path over the workload's synthetic inputs:
+an in-place NVFP4 re-quantization of the bf16 lm_head weight
+(nvfp4_refresh_inplace: amax, global scale, block scales, codes, packing)
+followed by the W4A16 GEMM at every activation row count M of the workload.
+Inputs are resident in HBM before timing starts.  Three copies of the
+quantized weight rotate so that every GEMM reads weights that were not just
+touched (the 8B-shape weights, 296 MB, would otherwise partly hit the
+256 MB last-level cache).
+
+Prints one JSON line: value = algorithmic bytes of the step / step time
+(TB/s), plus per-operation rates, the roofline of the dominant operation and
+the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 W4A16 lm_head GEMM: HBM TB/s at M=1..64, TFLOP/s at M=4096; quant GB/s"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+
+
+def quant_bytes(n: int, k: int) -> float:
+    """Read W twice (amax, encode), write codes (0.5 B) and scales (1/16 B) per weight."""
+    return n * k * (2 + 2 + 0.5 + 0.0625)
+
+
+def gemm_bytes(m: int, n: int, k: int) -> float:
+    return n * k * (0.5 + 0.0625) + 2 * m * k + 2 * m * n + 4
+
+
+def gemm_flops(m: int, n: int, k: int) -> float:
+    return 2.0 * m * n * k
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_w4a16_lm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(op: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("ops", {}).get(op)
+
+
+def cpu_baseline(wl, w, w_bits, x_bits, ms, rows: int):
+    """The oracle, as it stands, on the first ``rows`` weight rows (same step)."""
+    import numpy as np
+
+    import oracle.nvfp4_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:   # threadpoolctl missing: numpy elementwise work is single-threaded
+        blas = 1
+    sub = np.ascontiguousarray(w_bits[:rows])
+    t0 = time.perf_counter()
+    gs = O.global_scale(O.weight_amax(sub))
+    packed, scales = O.quantize_rows(sub, gs)
+    for m in ms:
+        O.gemm_ref(x_bits[:m], packed, scales, gs)
+    dt = time.perf_counter() - t0
+    nbytes = quant_bytes(rows, w.k) + sum(gemm_bytes(m, rows, w.k) for m in ms)
+    return {
+        "value": nbytes / dt / 1e12,
+        "unit": "TB/s",
+        "cores": int(blas),
+        "kind": "oracle",
+        "sample": (f"{rows} of {w.n} weight rows ({w.k} columns): amax + quantize, then fp64 GEMM at "
+                   f"M={list(ms)}; {dt:.1f} s; numpy elementwise on 1 thread, BLAS on {blas}"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b",
+                    help="llama3_8b (default), llama3_70b, qwen_prefill, heavy_tail, tiny")
+    ap.add_argument("--cpu-rows", type=int, default=24576, help="oracle sample size (weight rows)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=3, help="rotating quantized-weight copies")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (the path shards by "
+              "vocabulary rows; each GPU would run this same benchmark on its shard).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from nvfp4_w4a16_lm_amd import binding as B
+    from nvfp4_w4a16_lm_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    B.load_library()
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    n, k, ms = w.n, w.k, w.ms
+    t0 = time.perf_counter()
+    w_bits = wl.weight_bits(w)
+    x_bits = wl.activation_bits(w)
+    print(f"# inputs generated in {time.perf_counter() - t0:.1f} s: W {n}x{k}, x {x_bits.shape}",
+          file=sys.stderr, flush=True)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    W = to_dev(w_bits)
+    X = to_dev(x_bits)
+    copies = max(1, args.copies)
+    Q = [B.nvfp4_quantize(W) for _ in range(copies)]
+    Y = {m: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for m in ms}
+    xs = {m: X[:m] for m in ms}
+    torch.cuda.synchronize()
+
+    ops = ["quantize"] + [f"gemm_m{m}" for m in ms]
+    ev = {op: [] for op in ops}
+
+    def step(i: int, record: bool):
+        qi = i % copies
+        e0 = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            e0.record()
+        B.nvfp4_refresh_inplace(W, *Q[qi])
+        if record:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record()
+            ev["quantize"].append((e0, e1))
+            e0 = e1
+        for j, m in enumerate(ms):
+            qj = (qi + 1 + j % max(1, copies - 1)) % copies if copies > 1 else 0
+            B.nvfp4_w4a16_gemm(xs[m], *Q[qj], out=Y[m])
+            if record:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record()
+                ev[f"gemm_m{m}"].append((e0, e1))
+                e0 = e1
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    avg_ms = {op: float(np.mean([a.elapsed_time(b) for a, b in ev[op]])) for op in ops}
+    step_bytes = quant_bytes(n, k) + sum(gemm_bytes(m, n, k) for m in ms)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e12
+
+    per_op = {"quantize": {"ms": avg_ms["quantize"],
+                           "GB/s": quant_bytes(n, k) / (avg_ms["quantize"] * 1e-3) / 1e9}}
+    for m in ms:
+        t = avg_ms[f"gemm_m{m}"] * 1e-3
+        per_op[f"gemm_m{m}"] = {"ms": avg_ms[f"gemm_m{m}"],
+                                "TB/s": gemm_bytes(m, n, k) / t / 1e12,
+                                "TFLOP/s": gemm_flops(m, n, k) / t / 1e12}
+
+    dom = max(ops, key=lambda op: avg_ms[op])
+    if dom == "quantize":
+        achieved = quant_bytes(n, k) / (avg_ms[dom] * 1e-3) / 1e9
+        roof = {"op": "nvfp4_refresh_inplace", "kernels": "amax + quant_pack (+2 one-thread kernels)",
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic("quantize")}
+    else:
+        m = int(dom.split("_m")[1])
+        if m > 64:
+            achieved = gemm_flops(m, n, k) / (avg_ms[dom] * 1e-3) / 1e12
+            roof = {"op": f"nvfp4_w4a16_gemm M={m}", "kernels": "gemm_prefill_kernel", "bound": "mfma",
+                    "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": load_traffic(dom)}
+        else:
+            achieved = gemm_bytes(m, n, k) / (avg_ms[dom] * 1e-3) / 1e9
+            roof = {"op": f"nvfp4_w4a16_gemm M={m}", "kernels": "gemv_kernel", "bound": "hbm",
+                    "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(dom)}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x nvfp4 (fp32 accumulate)",
+        "data": "synthetic (seeded; no trained weights)",
+        "config": {"workload": w.name, "description": w.description, "N": n, "K": k, "M": list(ms),
+                   "step": "nvfp4_refresh_inplace + nvfp4_w4a16_gemm at each M", "weight_copies": copies},
+        "per_op": per_op,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, w, w_bits, x_bits, ms, min(args.cpu_rows, n))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

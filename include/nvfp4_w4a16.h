@@ -1,0 +1,129 @@
+/*
+ * nvfp4_w4a16.h -- C ABI of the NVFP4 W4A16 lm_head library for MI355X (gfx950).
+ *
+ * Three calls: quantize a bf16 lm_head weight to NVFP4, re-quantize it in
+ * place into the same buffers, and compute logits from the quantized weight
+ * with bf16 activations.  Everything runs in hand-written HIP kernels.
+ *
+ * The method is the one the vLLM API docs describe for
+ * vllm.model_executor.layers.quantization.online.lm_head (function
+ * _quantize_nvfp4, class _LMHeadNvfp4Method, refresh_quantized_lm_heads).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer is a DEVICE pointer on the current HIP device, except where
+ *    stated.  bf16 tensors are passed as raw 16-bit words (bfloat16 bits).
+ *  - All matrices are row-major and dense (row pitch = number of columns).
+ *  - The caller owns every buffer; the library allocates nothing and keeps no
+ *    state between calls, so calls are reentrant and can be captured into a
+ *    HIP graph.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *    call only enqueues work on it: no host<->device synchronisation.
+ *  - Arguments are validated on the host before any HIP API call.  A non-zero
+ *    status means nothing was enqueued, except NVFP4_ERR_LAUNCH, which reports
+ *    a HIP error raised while enqueueing (see nvfp4_last_hip_error()).
+ *  - Device faults surface as HIP errors at the caller's next synchronisation.
+ *  - Alignment: W, x and y must be 16-byte aligned; packed 16-byte aligned;
+ *    scales 4-byte aligned; global_scale 4-byte aligned; bias 2-byte aligned.
+ *  - Outputs may not overlap inputs or each other (NVFP4_ERR_ALIAS).
+ *  - Non-finite weights are outside the contract (results unspecified).
+ */
+#ifndef NVFP4_W4A16_H_
+#define NVFP4_W4A16_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,   /* a required pointer is NULL                                   */
+  NVFP4_ERR_SHAPE = 2,  /* N < 1, K < 16, K % 16 != 0, M < 0, or a size too large       */
+  NVFP4_ERR_ALIGN = 3,  /* a pointer breaks the alignment rules above                   */
+  NVFP4_ERR_ALIAS = 4,  /* an output byte range overlaps an input or another output     */
+  NVFP4_ERR_LAUNCH = 5  /* HIP reported an error while enqueueing                        */
+} nvfp4_status;
+
+/* Group size along K: one E4M3 scale per 16 consecutive weights of a row
+ * (vLLM modelopt.py, ModelOptNvFp4Config default group size; vLLM API docs,
+ * compressed_tensors.schemes, CompressedTensorsW4A16Fp4). */
+#define NVFP4_GROUP 16
+
+/*
+ * nvfp4_quantize -- online NVFP4 quantization of a bf16 weight.
+ * (vLLM API docs, quantization.online.lm_head, _quantize_nvfp4.)
+ *
+ *   W            in   bf16 [N, K]                the weight (e.g. a vocab shard of lm_head)
+ *   N, K         in   N >= 1 rows, K >= 16 columns, K % 16 == 0 (vLLM modelopt.py,
+ *                     KNvfp4Static rejects other K)
+ *   packed       out  uint8 [N, K/2]            E2M1 codes, two per byte, the even-k code
+ *                                               in the low nibble; bit 3 of a code = sign
+ *   scales       out  float8_e4m3fn bytes [N, K/16]   block scale of W[n, 16j : 16j+16]
+ *   global_scale out  1 float                   max(amax(|W|) / (6 * 448), 1e-12): the
+ *                                               dequantization-direction global scale
+ *                                               (ModelOpt's amax/2688, per modelopt.py
+ *                                               KNvfp4Static.process)
+ *
+ * Dequantization: w[n,k] ~= E2M1(code[n,k]) * e4m3(scales[n,k/16]) * global_scale.
+ * Per block: u = min((max|w| / 6) * (1/global_scale), 448) rounded to E4M3
+ * (nearest-even); each weight is multiplied by (1/global_scale)/scale and
+ * rounded to the E2M1 grid {0,.5,1,1.5,2,3,4,6} (nearest, ties to the even
+ * code, saturating at 6).  A zero block has scale 0 and codes 0; zero never
+ * carries a sign.  The global_scale word also serves as the amax accumulator
+ * while the call runs, so the outputs are only valid once the stream reaches
+ * the end of the call.
+ */
+nvfp4_status nvfp4_quantize(const void* W, int64_t N, int64_t K,
+                            uint8_t* packed, uint8_t* scales, float* global_scale,
+                            void* stream);
+
+/*
+ * nvfp4_refresh_inplace -- re-derive the quantized copy from an updated weight.
+ * (vLLM API docs, quantization.online.lm_head, refresh_quantized_lm_heads: the
+ * copy is rewritten in place so that captured graphs keep valid pointers.)
+ *
+ * Same arguments, computation and result as nvfp4_quantize, into buffers that
+ * already hold a quantization of a weight of the same (N, K).  It writes only
+ * the bytes of packed, scales and global_scale, allocates nothing and uses no
+ * memset nodes, so a HIP graph that captured nvfp4_w4a16_gemm on these
+ * pointers reads the new values on its next replay.  A refresh that overlaps
+ * a GEMM reading the same buffers on another stream is the caller's race.
+ */
+nvfp4_status nvfp4_refresh_inplace(const void* W, int64_t N, int64_t K,
+                                   uint8_t* packed, uint8_t* scales, float* global_scale,
+                                   void* stream);
+
+/*
+ * nvfp4_w4a16_gemm -- logits from bf16 activations and the NVFP4 weight.
+ * (vLLM API docs, quantization.online.lm_head, _LMHeadNvfp4Method.apply:
+ * weight-only NVFP4, activations stay in the model dtype.)
+ *
+ *   x            in   bf16 [M, K]     activations; M >= 0 (M == 0 enqueues nothing)
+ *   packed, scales, global_scale in  as produced by nvfp4_quantize for [N, K]
+ *   N            in   N >= 1
+ *   bias         in   bf16 [N] or NULL
+ *   y            out  bf16 [M, N]
+ *
+ *   y[m, n] = bf16_rne( global_scale * sum_k x[m,k] * E2M1(code[n,k]) * e4m3(scale[n,k/16])
+ *                       + bias[n] )
+ * with fp32 accumulation (products of a bf16 and a dequantized weight are
+ * exact in fp32; summation order is unspecified but deterministic).
+ * M <= 64 runs the streaming decode kernel, larger M the MFMA prefill kernel.
+ */
+nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t M, int64_t K,
+                              const uint8_t* packed, const uint8_t* scales,
+                              const float* global_scale, int64_t N,
+                              const void* bias, void* y, void* stream);
+
+/* Host-side helpers (no device work). */
+const char* nvfp4_status_string(int status);   /* static string for a status code        */
+const char* nvfp4_last_hip_error(void);        /* last HIP error text of this thread, or "" */
+int nvfp4_abi_version(void);                   /* bumps when a signature above changes   */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_W4A16_H_ */

@@ -6,7 +6,7 @@ its thin ctypes binding; it loads the library on first use of an entry point and
 raises if the library is missing (there is no fallback path).
 """
 
-_API = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
+_API = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm", "NVFP4ShapeError",
         "NVFP4Error", "library_path", "load_library", "STATUS_NAMES")
 
 

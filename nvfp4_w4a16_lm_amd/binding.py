@@ -1,0 +1,173 @@
+"""ctypes binding of ``libnvfp4_w4a16.so`` (argument marshalling only).
+
+Each function keeps the name of the C entry point it wraps.  torch is used for
+device memory (allocating outputs, taking data pointers) and for the current
+HIP stream; every step of the computation runs in the library's kernels.
+There is no fallback: a missing library raises at first use.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_NAME = "libnvfp4_w4a16.so"
+ABI_VERSION = 1
+
+STATUS_NAMES = {
+    0: "NVFP4_OK",
+    1: "NVFP4_ERR_NULL",
+    2: "NVFP4_ERR_SHAPE",
+    3: "NVFP4_ERR_ALIGN",
+    4: "NVFP4_ERR_ALIAS",
+    5: "NVFP4_ERR_LAUNCH",
+}
+
+#: Entry points declared in include/nvfp4_w4a16.h.
+EXPORTED = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
+            "nvfp4_status_string", "nvfp4_last_hip_error", "nvfp4_abi_version")
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        self.status = status
+        name = STATUS_NAMES.get(status, f"status {status}")
+        super().__init__(f"{fn}: {name}{': ' + detail if detail else ''}")
+
+
+class NVFP4ShapeError(NVFP4Error, ValueError):
+    """Bad shape (e.g. K not a multiple of 16), raised as a ValueError too."""
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("NVFP4_W4A16_LIB",
+                          os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises ImportError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m nvfp4_w4a16_lm_amd.build_lib` "
+                          "(the NVFP4 path has no fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    for name in ("nvfp4_quantize", "nvfp4_refresh_inplace"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        fn.restype = ctypes.c_int
+    lib.nvfp4_w4a16_gemm.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, vp, vp]
+    lib.nvfp4_w4a16_gemm.restype = ctypes.c_int
+    lib.nvfp4_status_string.argtypes = [ctypes.c_int]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_last_hip_error.argtypes = []
+    lib.nvfp4_last_hip_error.restype = ctypes.c_char_p
+    lib.nvfp4_abi_version.argtypes = []
+    lib.nvfp4_abi_version.restype = ctypes.c_int
+    if lib.nvfp4_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path}: ABI version {lib.nvfp4_abi_version()} != {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status == 0:
+        return
+    lib = load_library()
+    detail = lib.nvfp4_status_string(status).decode()
+    if status == 5:
+        detail += " -- " + lib.nvfp4_last_hip_error().decode()
+    if status == 2:
+        raise NVFP4ShapeError(fn, status, detail)
+    raise NVFP4Error(fn, status, detail)
+
+
+def _stream_of(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _as_bf16_2d(t: torch.Tensor, what: str) -> torch.Tensor:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{what} must be bfloat16, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    return t.contiguous()
+
+
+def _check_out(t: torch.Tensor, shape, dtypes, device, what: str) -> None:
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{what}: expected contiguous {shape} {dtypes[0]} on {device}, "
+                         f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+
+
+def nvfp4_quantize(weight: torch.Tensor, stream=None):
+    """bf16 [N, K] -> (packed uint8 [N, K/2], scales float8_e4m3fn [N, K/16], global_scale fp32 [])."""
+    w = _as_bf16_2d(weight, "weight")
+    n, k = w.shape
+    dev = w.device
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, k // 16), dtype=torch.float8_e4m3fn, device=dev)
+    gs = torch.empty((), dtype=torch.float32, device=dev)
+    lib = load_library()
+    _check("nvfp4_quantize", lib.nvfp4_quantize(_ptr(w), n, k, _ptr(packed), _ptr(scales), _ptr(gs),
+                                                _stream_of(w, stream)))
+    return packed, scales, gs
+
+
+def nvfp4_refresh_inplace(weight: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                          global_scale: torch.Tensor, stream=None) -> None:
+    """Re-quantize ``weight`` into the existing buffers (pointers unchanged)."""
+    w = _as_bf16_2d(weight, "weight")
+    n, k = w.shape
+    dev = w.device
+    _check_out(packed, (n, k // 2), (torch.uint8,), dev, "packed")
+    _check_out(scales, (n, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, "scales")
+    if global_scale.numel() != 1 or global_scale.dtype != torch.float32 or global_scale.device != dev:
+        raise ValueError("global_scale must be one float32 on the weight's device")
+    lib = load_library()
+    _check("nvfp4_refresh_inplace",
+           lib.nvfp4_refresh_inplace(_ptr(w), n, k, _ptr(packed), _ptr(scales), _ptr(global_scale),
+                                     _stream_of(w, stream)))
+
+
+def nvfp4_w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                     global_scale: torch.Tensor, bias: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 x [M, K] . dequant(W)^T (+ bias) -> bf16 [M, N]."""
+    x = _as_bf16_2d(x, "x")
+    m, k = x.shape
+    if packed.dim() != 2 or packed.shape[1] * 2 != k:
+        raise ValueError(f"packed shape {tuple(packed.shape)} does not match K={k}")
+    n = packed.shape[0]
+    dev = x.device
+    _check_out(packed, (n, k // 2), (torch.uint8,), dev, "packed")
+    _check_out(scales, (n, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, "scales")
+    if global_scale.numel() != 1 or global_scale.dtype != torch.float32 or global_scale.device != dev:
+        raise ValueError("global_scale must be one float32 on x's device")
+    if bias is not None:
+        _check_out(bias, (n,), (torch.bfloat16,), dev, "bias")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_out(out, (m, n), (torch.bfloat16,), dev, "out")
+    lib = load_library()
+    _check("nvfp4_w4a16_gemm",
+           lib.nvfp4_w4a16_gemm(_ptr(x), m, k, _ptr(packed), _ptr(scales), _ptr(global_scale), n,
+                                _ptr(bias), _ptr(out), _stream_of(x, stream)))
+    return out

@@ -1,0 +1,122 @@
+// C-ABI entry points: host-side validation, then stream-ordered launches.
+// No HIP API call happens before an argument check has passed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/nvfp4_w4a16.h"
+#include "nvfp4_launch.hpp"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;        // per-dimension bound (int32 kernel indexing)
+constexpr int64_t kMaxElems = (int64_t)1 << 40;      // N*K bound (64-bit flat offsets)
+constexpr int64_t kMaxPrefillM = (int64_t)65535 * 128;  // grid.y limit of the prefill kernel
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nvfp4_status check_weight_shape(int64_t N, int64_t K) {
+  if (N < 1 || K < NVFP4_GROUP || K % NVFP4_GROUP != 0) return NVFP4_ERR_SHAPE;
+  if (N > kMaxDim || K > kMaxDim || N * K > kMaxElems) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+nvfp4_status validate_quantize(const void* W, int64_t N, int64_t K, const uint8_t* packed,
+                               const uint8_t* scales, const float* gs) {
+  if (!W || !packed || !scales || !gs) return NVFP4_ERR_NULL;
+  const nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(gs, 4))
+    return NVFP4_ERR_ALIGN;
+  const Range rw = span(W, N * K * 2), rp = span(packed, N * K / 2), rs = span(scales, N * K / 16),
+              rg = span(gs, 4);
+  if (overlap(rw, rp) || overlap(rw, rs) || overlap(rw, rg) || overlap(rp, rs) || overlap(rp, rg) ||
+      overlap(rs, rg))
+    return NVFP4_ERR_ALIAS;
+  return NVFP4_OK;
+}
+
+nvfp4_status finish(hipError_t e) {
+  if (e == hipSuccess) return NVFP4_OK;
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status run_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed, uint8_t* scales,
+                          float* global_scale, void* stream) {
+  const nvfp4_status s = validate_quantize(W, N, K, packed, scales, global_scale);
+  if (s != NVFP4_OK) return s;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_quantize(W, N, K, packed, scales, global_scale, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed, uint8_t* scales,
+                            float* global_scale, void* stream) {
+  return run_quantize(W, N, K, packed, scales, global_scale, stream);
+}
+
+nvfp4_status nvfp4_refresh_inplace(const void* W, int64_t N, int64_t K, uint8_t* packed, uint8_t* scales,
+                                   float* global_scale, void* stream) {
+  // The same kernels write the same bytes; the sequence holds no allocation
+  // and no memset node, so graphs captured on these buffers stay valid.
+  return run_quantize(W, N, K, packed, scales, global_scale, stream);
+}
+
+nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t M, int64_t K, const uint8_t* packed,
+                              const uint8_t* scales, const float* global_scale, int64_t N,
+                              const void* bias, void* y, void* stream) {
+  if (!x || !packed || !scales || !global_scale || !y) return NVFP4_ERR_NULL;
+  nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (M < 0 || M > kMaxPrefillM || M * K > kMaxElems || M * N > kMaxElems) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(packed, 16) || !aligned(scales, 4) ||
+      !aligned(global_scale, 4) || (bias && !aligned(bias, 2)))
+    return NVFP4_ERR_ALIGN;
+  const Range ry = span(y, M * N * 2);
+  if (M > 0 && (overlap(ry, span(x, M * K * 2)) || overlap(ry, span(packed, N * K / 2)) ||
+                overlap(ry, span(scales, N * K / 16)) || overlap(ry, span(global_scale, 4)) ||
+                (bias && overlap(ry, span(bias, N * 2)))))
+    return NVFP4_ERR_ALIAS;
+  if (M == 0) return NVFP4_OK;
+  g_last_hip_error[0] = '\0';
+  const hipStream_t st = (hipStream_t)stream;
+  if (M <= nvfp4::kDecodeMaxM)
+    return finish(nvfp4::launch_gemv(x, M, K, packed, scales, global_scale, N, bias, y, st));
+  return finish(nvfp4::launch_gemm_prefill(x, M, K, packed, scales, global_scale, N, bias, y, st));
+}
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape (need N >= 1, K >= 16, K % 16 == 0, M >= 0, sizes in range)";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer (W, x, y, packed: 16 B; scales, global_scale: 4 B; bias: 2 B)";
+    case NVFP4_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case NVFP4_ERR_LAUNCH: return "HIP error while enqueueing (see nvfp4_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4_last_hip_error(void) { return g_last_hip_error; }
+
+int nvfp4_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal launch interface between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// hipLaunchKernel with a typed argument pack.  The argument types must match
+// the kernel's parameter types exactly (callers cast at the call site).
+template <typename... Args>
+inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  void* argv[] = {(void*)&args..., nullptr};
+  return hipLaunchKernel(fn, grid, block, argv, 0, stream);
+}
+
+// Quantization: amax -> global scale -> block scales + packed codes.
+hipError_t launch_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed, uint8_t* scales,
+                           float* global_scale, hipStream_t stream);
+
+// y[M,N] = x[M,K] . dequant(W)^T (+ bias); M <= 64 streaming decode kernel.
+hipError_t launch_gemv(const void* x, int64_t M, int64_t K, const uint8_t* packed, const uint8_t* scales,
+                       const float* global_scale, int64_t N, const void* bias, void* y, hipStream_t stream);
+
+// Same for M > 64: LDS-staged dequant + bf16 MFMA.
+hipError_t launch_gemm_prefill(const void* x, int64_t M, int64_t K, const uint8_t* packed,
+                               const uint8_t* scales, const float* global_scale, int64_t N,
+                               const void* bias, void* y, hipStream_t stream);
+
+constexpr int64_t kDecodeMaxM = 64;
+
+}  // namespace nvfp4

@@ -8,12 +8,14 @@ is how the synthetic weights and activations come into existence.
 
 Recipe (numpy PCG64 ``default_rng``):
 
-* The tiny weight uses ``default_rng(0)``; every other tensor uses
-  ``default_rng([cfg, stream])`` with cfg 1..5 and stream 0 = weight,
-  1 = outlier mask, 2 = activations, 3 = refresh noise, 4 = bias.
-* Normal draws are float32 ``standard_normal`` generated row chunk by row
-  chunk (``CHUNK_ROWS`` rows at a time, sequentially from one generator),
-  multiplied by the float32 standard deviation, then rounded to bf16.
+* Tensors are generated in row chunks of ``max(1, CHUNK_ELEMS // K)`` rows;
+  chunk ``c`` of stream ``s`` of config ``cfg`` draws from
+  ``default_rng([cfg, s, c])`` (independent chunks, generated on a thread
+  pool).  The tiny weight is one chunk drawn from ``default_rng(0)``.
+  Streams: 0 = weight, 1 = outlier mask, 2 = activations, 3 = refresh noise,
+  4 = bias.
+* Normal draws are float32 ``standard_normal`` multiplied by the float32
+  standard deviation, then rounded to bf16.
 * Llama-3-8B shape: exactly ``round(0.001 * N * K)`` distinct positions, drawn
   with ``choice(N * K, count, replace=False)``, are multiplied by 20 before the
   bf16 rounding.
@@ -25,11 +27,15 @@ Recipe (numpy PCG64 ``default_rng``):
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 
 import numpy as np
+import torch
 
-CHUNK_ROWS = 8192
+CHUNK_ELEMS = 1 << 23
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 @dataclasses.dataclass(frozen=True)
@@ -63,51 +69,70 @@ WORKLOADS = {
 
 
 def f32_to_bf16_bits(f: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
-    u = np.ascontiguousarray(f, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    """float32 -> bf16 bit patterns, round to nearest even (torch's CPU cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(f, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _rng(cfg: int, stream: int, tiny_weight: bool = False) -> np.random.Generator:
-    if tiny_weight:
-        return np.random.default_rng(0)
-    return np.random.default_rng([cfg, stream])
+def chunk_rows(k: int) -> int:
+    return max(1, CHUNK_ELEMS // k)
 
 
-def normal_bits(n: int, k: int, sigma: float, rng: np.random.Generator) -> np.ndarray:
-    """bf16 bits of ``sigma * N(0,1)`` float32 draws, row chunk by row chunk."""
+def _chunked(n: int, k: int, fill) -> np.ndarray:
+    """Run ``fill(chunk_index, r0, r1) -> uint16 [r1-r0, k]`` over row chunks in threads."""
     out = np.empty((n, k), dtype=np.uint16)
-    s = np.float32(sigma)
-    for r0 in range(0, n, CHUNK_ROWS):
-        r1 = min(n, r0 + CHUNK_ROWS)
-        out[r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, k), dtype=np.float32) * s)
+    rows = chunk_rows(k)
+    starts = list(range(0, n, rows))
+
+    def work(ci):
+        r0 = starts[ci]
+        r1 = min(n, r0 + rows)
+        out[r0:r1] = fill(ci, r0, r1)
+
+    if len(starts) == 1:
+        work(0)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(work, range(len(starts))))
     return out
+
+
+def normal_bits(n: int, k: int, sigma: float, seed: tuple) -> np.ndarray:
+    """bf16 bits of ``sigma * N(0,1)`` float32 draws; chunk c uses default_rng([*seed, c])."""
+    s = np.float32(sigma)
+
+    def fill(ci, r0, r1):
+        rng = np.random.default_rng([*seed, ci])
+        return f32_to_bf16_bits(rng.standard_normal((r1 - r0, k), dtype=np.float32) * s)
+
+    return _chunked(n, k, fill)
 
 
 def weight_bits(w: Workload) -> np.ndarray:
     """The workload's bf16 weight [N, K] as uint16 bits."""
     if w.kind == "heavy":
         return _heavy_weight(w)
-    rng = _rng(w.cfg, 0, tiny_weight=(w.name == "tiny"))
+    if w.name == "tiny":
+        f = np.random.default_rng(0).standard_normal((w.n, w.k), dtype=np.float32) * np.float32(w.sigma)
+        return f32_to_bf16_bits(f)
     if w.kind != "outliers":
-        return normal_bits(w.n, w.k, w.sigma, rng)
+        return normal_bits(w.n, w.k, w.sigma, (w.cfg, 0))
     count = int(round(0.001 * w.n * w.k))
-    pos = np.sort(_rng(w.cfg, 1).choice(w.n * w.k, size=count, replace=False))
-    out = np.empty((w.n, w.k), dtype=np.uint16)
+    pos = np.sort(np.random.default_rng([w.cfg, 1]).choice(w.n * w.k, size=count, replace=False))
     s = np.float32(w.sigma)
-    for r0 in range(0, w.n, CHUNK_ROWS):
-        r1 = min(w.n, r0 + CHUNK_ROWS)
-        f = rng.standard_normal((r1 - r0, w.k), dtype=np.float32) * s
+
+    def fill(ci, r0, r1):
+        f = np.random.default_rng([w.cfg, 0, ci]).standard_normal((r1 - r0, w.k), dtype=np.float32) * s
         lo, hi = np.searchsorted(pos, [r0 * w.k, r1 * w.k])
         flat = f.reshape(-1)
         flat[pos[lo:hi] - r0 * w.k] *= np.float32(20.0)
-        out[r0:r1] = f32_to_bf16_bits(f)
-    return out
+        return f32_to_bf16_bits(f)
+
+    return _chunked(w.n, w.k, fill)
 
 
 def grid_row_bits(k: int) -> np.ndarray:
@@ -120,12 +145,11 @@ def grid_row_bits(k: int) -> np.ndarray:
 
 
 def _heavy_weight(w: Workload) -> np.ndarray:
-    rng = _rng(w.cfg, 0)
-    out = np.empty((w.n, w.k), dtype=np.uint16)
-    for r0 in range(0, w.n, CHUNK_ROWS):
-        r1 = min(w.n, r0 + CHUNK_ROWS)
-        t = rng.standard_t(3, size=(r1 - r0, w.k)) * w.sigma
-        out[r0:r1] = f32_to_bf16_bits(t.astype(np.float32))
+    def fill(ci, r0, r1):
+        t = np.random.default_rng([w.cfg, 0, ci]).standard_t(3, size=(r1 - r0, w.k)) * w.sigma
+        return f32_to_bf16_bits(t.astype(np.float32))
+
+    out = _chunked(w.n, w.k, fill)
     out[0] = 0
     out[w.n - 1] = grid_row_bits(w.k)
     return out
@@ -133,31 +157,30 @@ def _heavy_weight(w: Workload) -> np.ndarray:
 
 def activation_bits(w: Workload, m: int | None = None) -> np.ndarray:
     """bf16 activations x[:m] of the workload's N(0,1) draw [m_draw, K]."""
-    rng = _rng(w.cfg, 2)
-    x = normal_bits(w.m_draw, w.k, 1.0, rng)
+    x = normal_bits(w.m_draw, w.k, 1.0, (w.cfg, 2))
     return x if m is None else x[:m]
 
 
 def refresh_weight_bits(w: Workload, w_bits: np.ndarray, sigma: float = 1e-3) -> np.ndarray:
     """``bf16(float32(W) + sigma * N(0,1))`` for the in-place refresh workload."""
-    rng = _rng(w.cfg, 3)
-    out = np.empty_like(w_bits)
     s = np.float32(sigma)
-    for r0 in range(0, w_bits.shape[0], CHUNK_ROWS):
-        r1 = min(w_bits.shape[0], r0 + CHUNK_ROWS)
-        noise = rng.standard_normal((r1 - r0, w_bits.shape[1]), dtype=np.float32) * s
-        out[r0:r1] = f32_to_bf16_bits(bf16_bits_to_f32(w_bits[r0:r1]) + noise)
-    return out
+    k = w_bits.shape[1]
+
+    def fill(ci, r0, r1):
+        noise = np.random.default_rng([w.cfg, 3, ci]).standard_normal((r1 - r0, k), dtype=np.float32) * s
+        return f32_to_bf16_bits(bf16_bits_to_f32(w_bits[r0:r1]) + noise)
+
+    return _chunked(w_bits.shape[0], k, fill)
 
 
 def bias_bits(n: int, seed: int = 0, sigma: float = 1.0) -> np.ndarray:
-    return normal_bits(1, n, sigma, np.random.default_rng([seed, 4]))[0]
+    return normal_bits(1, n, sigma, (seed, 4))[0]
 
 
 def random_weight_bits(n: int, k: int, sigma: float = 0.02, seed: int = 0) -> np.ndarray:
     """Ad-hoc shapes for edge-case tests (ragged N and K, tiny sizes)."""
-    return normal_bits(n, k, sigma, np.random.default_rng([100, seed, n, k]))
+    return normal_bits(n, k, sigma, (100, seed, n, k))
 
 
 def random_activation_bits(m: int, k: int, seed: int = 0) -> np.ndarray:
-    return normal_bits(m, k, 1.0, np.random.default_rng([101, seed, m, k]))
+    return normal_bits(m, k, 1.0, (101, seed, m, k))

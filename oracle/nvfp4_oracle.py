@@ -165,9 +165,12 @@ def check_weight(w_bits: np.ndarray) -> tuple[int, int]:
     return n, k
 
 
-def weight_amax(w_bits: np.ndarray) -> np.float32:
+def weight_amax(w_bits: np.ndarray, chunk_rows: int = 4096) -> np.float32:
     """Max |w| over the whole tensor (reading R6).  Exact: a max of bf16 values."""
-    return F32(np.max(np.abs(bf16_bits_to_f32(w_bits))))
+    best = F32(0.0)
+    for r0 in range(0, w_bits.shape[0], chunk_rows):
+        best = max(best, F32(np.max(np.abs(bf16_bits_to_f32(w_bits[r0:r0 + chunk_rows])))))
+    return best
 
 
 def global_scale(amax: np.float32) -> np.float32:

@@ -1,0 +1,112 @@
+"""Helpers for the GPU parity tests (host <-> device marshalling, comparisons)."""
+
+from __future__ import annotations
+
+import concurrent.futures
+
+import numpy as np
+import torch
+
+import oracle.nvfp4_oracle as O
+from nvfp4_w4a16_lm_amd import binding as B
+from nvfp4_w4a16_lm_amd import workloads as wl
+
+DEV = "cuda:0"
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def quantize_gpu(w_bits: np.ndarray):
+    p, s, g = B.nvfp4_quantize(dev_bf16(w_bits))
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), s.view(torch.uint8).cpu().numpy(), np.float32(g.cpu().item())
+
+
+def upload_quant(packed: np.ndarray, scales: np.ndarray, gs) -> tuple:
+    return (dev_u8(packed), dev_u8(scales),
+            torch.tensor(np.float32(gs), dtype=torch.float32, device=DEV))
+
+
+def f32_bits(v) -> int:
+    return int(np.float32(v).view(np.uint32))
+
+
+def assert_quant_equal(w_bits, got, want, label=""):
+    gp, gsb, ggs = got
+    wp, wsb, wgs = want
+    assert f32_bits(ggs) == f32_bits(wgs), f"{label}: global scale {ggs!r} != {wgs!r}"
+    bad_s = np.argwhere(gsb != wsb)
+    bad_p = np.argwhere(gp != wp)
+    if len(bad_s) or len(bad_p):
+        n, j = (bad_s[0] if len(bad_s) else (bad_p[0][0], bad_p[0][1] // 8))
+        blk = w_bits[n, 16 * j:16 * j + 16]
+        raise AssertionError(
+            f"{label}: {len(bad_s)} scale and {len(bad_p)} packed mismatches; first at row {n} block {j}: "
+            f"scale gpu={gsb[n, j]:#04x} oracle={wsb[n, j]:#04x}; packed gpu={gp[n, 8*j:8*j+8].tolist()} "
+            f"oracle={wp[n, 8*j:8*j+8].tolist()}; weights={wl.bf16_bits_to_f32(blk).tolist()}")
+
+
+def oracle_quantize_threaded(w_bits: np.ndarray, gs, rows: int = 2048):
+    """Oracle quantize_rows over row chunks on a thread pool (same arithmetic)."""
+    n, k = w_bits.shape
+    packed = np.empty((n, k // 2), np.uint8)
+    scales = np.empty((n, k // 16), np.uint8)
+
+    def work(r0):
+        p, s = O.quantize_rows(w_bits[r0:r0 + rows], gs)
+        packed[r0:r0 + rows] = p
+        scales[r0:r0 + rows] = s
+
+    with concurrent.futures.ThreadPoolExecutor(16) as ex:
+        list(ex.map(work, range(0, n, rows)))
+    return packed, scales
+
+
+def gemm_gpu(x_bits, qdev, bias_bits=None):
+    p, s, g = qdev
+    bias = None if bias_bits is None else dev_bf16(bias_bits)
+    y = B.nvfp4_w4a16_gemm(dev_bf16(x_bits), p, s, g, bias)
+    torch.cuda.synchronize()
+    return host_bits(y)
+
+
+def tight_tolerance(x_bits, packed, scales, gs, y64, bias_bits=None):
+    """fp32 accumulation of K exact products (any order) + one bf16 rounding."""
+    x = np.abs(wl.bf16_bits_to_f32(x_bits).astype(np.float64))
+    wd = np.abs(O.dequantize(packed, scales, gs))
+    k = x.shape[1]
+    s_abs = x @ wd.T
+    acc = (k + 2) * 2.0 ** -24 * s_abs
+    if bias_bits is not None:
+        acc = acc + 2.0 ** -24 * np.abs(wl.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
+    return 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
+
+
+def check_gemm(y_bits, x_bits, packed, scales, gs, bias_bits=None, label="", argmax_min=0.999,
+               y64=None):
+    y = wl.bf16_bits_to_f32(y_bits).astype(np.float64)
+    if y64 is None:
+        y64 = O.gemm_ref(x_bits, packed, scales, gs, bias_bits)
+    tol = O.gemm_tolerance(x_bits, packed, scales, gs, 1e-3, bias_bits)
+    err = np.abs(y - y64)
+    worst = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), (f"{label}: north-star bound broken at {worst}: y={y[worst]} "
+                                f"y64={y64[worst]} tol={tol[worst]}")
+    tight = tight_tolerance(x_bits, packed, scales, gs, y64, bias_bits)
+    worst = np.unravel_index(np.argmax(err - tight), err.shape)
+    assert np.all(err <= tight), (f"{label}: tight bound broken at {worst}: y={y[worst]} "
+                                  f"y64={y64[worst]} tight={tight[worst]}")
+    if y.shape[1] > 1:
+        tie, strict = O.argmax_agreement(y, y64)
+        assert tie >= argmax_min, f"{label}: tie-aware argmax agreement {tie} (strict {strict})"
+    return y64

@@ -1,0 +1,131 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every entry point the header declares, and
+reject bad arguments with the documented status before it makes any HIP call
+(so these calls are safe without a device; the pointers below are never
+dereferenced).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from nvfp4_w4a16_lm_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_w4a16.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS = 0, 1, 2, 3, 4
+
+# Fake, well-separated, 256-byte aligned addresses: only compared, never touched.
+W, P, S, G, X, Y, B = (0x10000000 * (i + 1) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|const char\*|int)\s+(nvfp4_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = binding.library_path()
+    if not os.path.exists(path):
+        pytest.fail(f"library not built: {path} (run __graft_entry__.build())")
+    return binding.load_library()
+
+
+def test_header_declares_the_three_calls():
+    fns = declared_functions()
+    for name in ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm"):
+        assert name in fns
+    assert set(fns) == set(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.nvfp4_abi_version() == binding.ABI_VERSION
+    for st in range(6):
+        assert lib.nvfp4_status_string(st).decode()
+    assert lib.nvfp4_status_string(99).decode() == "unknown status"
+    assert lib.nvfp4_last_hip_error().decode() == ""
+
+
+def q(lib, w=W, n=1024, k=512, p=P, s=S, g=G, fn="nvfp4_quantize"):
+    return getattr(lib, fn)(w, n, k, p, s, g, None)
+
+
+@pytest.mark.parametrize("fn", ["nvfp4_quantize", "nvfp4_refresh_inplace"])
+def test_quantize_validation(lib, fn):
+    assert q(lib, w=0, fn=fn) == ERR_NULL
+    assert q(lib, p=0, fn=fn) == ERR_NULL
+    assert q(lib, s=0, fn=fn) == ERR_NULL
+    assert q(lib, g=0, fn=fn) == ERR_NULL
+    # K must be a positive multiple of 16 (KNvfp4Static in vLLM modelopt.py rejects others)
+    for n, k in [(0, 512), (-1, 512), (4, 0), (4, 8), (4, 24), (4, 520), (4, -16), (1 << 31, 16)]:
+        assert q(lib, n=n, k=k, fn=fn) == ERR_SHAPE, (n, k)
+    assert q(lib, w=W + 8, fn=fn) == ERR_ALIGN
+    assert q(lib, p=P + 4, fn=fn) == ERR_ALIGN
+    assert q(lib, s=S + 2, fn=fn) == ERR_ALIGN
+    assert q(lib, g=G + 2, fn=fn) == ERR_ALIGN
+    # outputs overlapping the weight or each other
+    assert q(lib, p=W + 1024, fn=fn) == ERR_ALIAS
+    assert q(lib, s=P + 16, fn=fn) == ERR_ALIAS
+    assert q(lib, g=S + 64, fn=fn) == ERR_ALIAS
+    assert q(lib, g=P, fn=fn) == ERR_ALIAS
+    # the weight ends exactly where packed starts: no overlap, but we stop before HIP by
+    # making another argument invalid
+    assert q(lib, p=W + 1024 * 512 * 2, g=0, fn=fn) == ERR_NULL
+
+
+def gm(lib, x=X, m=4, k=512, p=P, s=S, g=G, n=1024, b=0, y=Y):
+    return lib.nvfp4_w4a16_gemm(x, m, k, p, s, g, n, b, y, None)
+
+
+def test_gemm_validation(lib):
+    assert gm(lib, x=0) == ERR_NULL
+    assert gm(lib, p=0) == ERR_NULL
+    assert gm(lib, s=0) == ERR_NULL
+    assert gm(lib, g=0) == ERR_NULL
+    assert gm(lib, y=0) == ERR_NULL
+    for m, k, n in [(-1, 512, 1024), (4, 8, 1024), (4, 40, 1024), (4, 512, 0), (4, 512, -3)]:
+        assert gm(lib, m=m, k=k, n=n) == ERR_SHAPE, (m, k, n)
+    assert gm(lib, x=X + 2) == ERR_ALIGN
+    assert gm(lib, y=Y + 8) == ERR_ALIGN
+    assert gm(lib, p=P + 8) == ERR_ALIGN
+    assert gm(lib, s=S + 1) == ERR_ALIGN
+    assert gm(lib, g=G + 1) == ERR_ALIGN
+    assert gm(lib, b=B + 1) == ERR_ALIGN
+    assert gm(lib, y=X) == ERR_ALIAS
+    assert gm(lib, y=P + 256) == ERR_ALIAS
+    assert gm(lib, y=S - 16) == ERR_ALIAS
+    assert gm(lib, y=G - 64) == ERR_ALIAS
+    assert gm(lib, b=B, y=B - 32) == ERR_ALIAS
+    # M == 0 is an empty GEMM: validated, nothing enqueued, no HIP call
+    assert gm(lib, m=0) == OK
+
+
+def test_binding_maps_shape_errors_to_valueerror(lib):
+    with pytest.raises(ValueError):
+        binding._check("nvfp4_quantize", ERR_SHAPE)
+    with pytest.raises(binding.NVFP4Error):
+        binding._check("nvfp4_quantize", ERR_ALIAS)
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the oracle and has no CPU path."""
+    pkg = os.path.join(ROOT, "nvfp4_w4a16_lm_amd")
+    for fname in os.listdir(pkg):
+        if fname.endswith(".py"):
+            text = open(os.path.join(pkg, fname)).read()
+            assert "oracle" not in text.replace("the oracle", ""), fname
