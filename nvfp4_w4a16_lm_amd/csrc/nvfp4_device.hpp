@@ -13,6 +13,7 @@ namespace nvfp4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -53,45 +54,43 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne(float u, float* value) {
   return sub ? (uint32_t)m : r - (120u << 3);
 }
 
-// E4M3 byte -> float (exact).  Sign honoured; 0x7F/0xFF (NaN) are not produced
-// by the quantizer and are outside the contract of the GEMM.
-__device__ __forceinline__ float e4m3_decode(uint32_t b) {
-  const uint32_t mag = b & 0x7Fu;
-  const float sub = (float)(mag & 7u) * 0.001953125f;
-  const float nrm = __uint_as_float((mag + 960u) << 20);
-  const float v = (mag < 8u) ? sub : nrm;
-  return (b & 0x80u) ? -v : v;
+// Two floats -> two E2M1 codes in byte SEL of `old` (gfx950 converter, scale 1).
+// The converter rounds the magnitude to nearest with ties to the even code and
+// saturates at 6; it copies the sign bit of its input even when the magnitude
+// rounds to zero, which fix_zero_signs() undoes.
+#define NVFP4_CVT_PK_FP4(old, a, b, SEL) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (SEL))
+
+// Clear the sign bit of every nibble whose magnitude bits are zero, so zero is
+// always code 0x0: adding 7 to a 3-bit magnitude sets bit 3 exactly when the
+// magnitude is nonzero, with no carry into the next nibble.
+__device__ __forceinline__ uint32_t fix_zero_signs(uint32_t w) {
+  const uint32_t mag = w & 0x77777777u;
+  const uint32_t nonzero = (mag + 0x77777777u) & 0x88888888u;
+  return mag | (w & nonzero);
 }
 
-// E2M1 magnitude code of 0 <= a <= 6: nearest grid value, ties to the even code.
-__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-         (uint32_t)(a > 5.0f);
-}
+// E4M3 byte SEL of a 32-bit word -> float (gfx950 converter, OCP e4m3fn).
+#define NVFP4_E4M3_TO_F32(word, SEL) __builtin_amdgcn_cvt_f32_fp8((int)(word), (SEL))
 
-// 4-bit code -> its value times the block scale s, as fp32 (exact: at most
-// 2 significant bits times at most 4).
-__device__ __forceinline__ float e2m1_scaled(uint32_t c, float s) {
-  const uint32_t mag = c & 7u;
-  const float big = __uint_as_float((mag << 22) + 0x3F000000u);  // mag >= 2: 2^(e-1)(1+m/2)
-  const float small = (mag == 1u) ? 0.5f : 0.0f;
-  float v = (mag >= 2u) ? big : small;
-  v = __uint_as_float(__float_as_uint(v) ^ ((c & 8u) << 28));
-  return v * s;
-}
+// Byte j of `w` (two codes, the low nibble first) -> the two values
+// code * s as a packed pair of bf16.  The converter gives the exact E2M1
+// values as fp32; code * s has at most 6 significant bits, so the fp32
+// product is exact and its upper half is the exact bf16.
+#define NVFP4_DEQ_PAIR(w, s, SEL)                                                         \
+  ([&]() {                                                                                \
+    const f32x2 d_ = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((w), 1.0f, (SEL));        \
+    return __builtin_amdgcn_perm(__float_as_uint(d_[1] * (s)), __float_as_uint(d_[0] * (s)), \
+                                 0x07060302u);                                            \
+  }())
 
 // Eight codes (one 32-bit word, code i in bits 4i..4i+3) -> eight bf16 values
-// of code * s.  The products are exact in bf16, so taking the upper 16 bits of
-// the fp32 product is exact.
+// of code * s.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
   u32x4 o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = __float_as_uint(e2m1_scaled((w >> (8 * j)) & 0xFu, s));
-    const uint32_t hi = __float_as_uint(e2m1_scaled((w >> (8 * j + 4)) & 0xFu, s));
-    o[j] = (lo >> 16) | (hi & 0xFFFF0000u);
-  }
+  o[0] = NVFP4_DEQ_PAIR(w, s, 0);
+  o[1] = NVFP4_DEQ_PAIR(w, s, 1);
+  o[2] = NVFP4_DEQ_PAIR(w, s, 2);
+  o[3] = NVFP4_DEQ_PAIR(w, s, 3);
   return __builtin_bit_cast(bf16x8, o);
 }
 

@@ -82,10 +82,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ 
         }
       }
     }
+    const float sv[4] = {NVFP4_E4M3_TO_F32(sc, 0), NVFP4_E4M3_TO_F32(sc, 1), NVFP4_E4M3_TO_F32(sc, 2),
+                         NVFP4_E4M3_TO_F32(sc, 3)};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const float s = e4m3_decode((sc >> (8 * (t >> 1))) & 0xFFu);
-      const bf16x8 a = dequant8(pw[t], s);
+      const bf16x8 a = dequant8(pw[t], sv[t >> 1]);
       const int k = kb + 8 * t;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -173,10 +174,10 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(const uint16_t* __res
       if (x_ok && (VEC || kk < K)) xv[j] = *reinterpret_cast<const u32x4*>(xrow + kk);
     }
     __syncthreads();   // the previous step's fragment reads are done
+    const float sv[2] = {NVFP4_E4M3_TO_F32(s01, 0), NVFP4_E4M3_TO_F32(s01, 1)};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float s = e4m3_decode((s01 >> (8 * (j >> 1))) & 0xFFu);
-      *reinterpret_cast<bf16x8*>(&Ws[lrow * kLdsPitch + 32 * lhalf + 8 * j]) = dequant8(pw[j], s);
+      *reinterpret_cast<bf16x8*>(&Ws[lrow * kLdsPitch + 32 * lhalf + 8 * j]) = dequant8(pw[j], sv[j >> 1]);
       *reinterpret_cast<u32x4*>(&Xs[lrow * kLdsPitch + 32 * lhalf + 8 * j]) = xv[j];
     }
     __syncthreads();

@@ -94,16 +94,22 @@ __device__ __forceinline__ void encode_block(const uint32_t d[8], float inv, uin
   float s;
   const uint32_t sbyte = e4m3_encode_rne(u, &s);
   const float r = (s > 0.0f) ? inv / s : 0.0f;   // fl32(inv / s); zero block -> codes 0
-  uint32_t o[2] = {0u, 0u};
+  float q[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float wv = (i & 1) ? bf16_hi(d[i >> 1]) : bf16_lo(d[i >> 1]);
-    const float q = wv * r;
-    const uint32_t c = e2m1_mag_code(fminf(fabsf(q), kE2m1Max));
-    const uint32_t code = c | ((q < 0.0f && c != 0u) ? 8u : 0u);
-    o[i >> 3] |= code << (4 * (i & 7));
+  for (int i = 0; i < 8; ++i) {
+    q[2 * i] = bf16_lo(d[i]) * r;       // fl32(w * r)
+    q[2 * i + 1] = bf16_hi(d[i]) * r;
   }
-  *out_codes = make_uint2(o[0], o[1]);
+  uint32_t lo = 0u, hi = 0u;
+  lo = NVFP4_CVT_PK_FP4(lo, q[0], q[1], 0);
+  lo = NVFP4_CVT_PK_FP4(lo, q[2], q[3], 1);
+  lo = NVFP4_CVT_PK_FP4(lo, q[4], q[5], 2);
+  lo = NVFP4_CVT_PK_FP4(lo, q[6], q[7], 3);
+  hi = NVFP4_CVT_PK_FP4(hi, q[8], q[9], 0);
+  hi = NVFP4_CVT_PK_FP4(hi, q[10], q[11], 1);
+  hi = NVFP4_CVT_PK_FP4(hi, q[12], q[13], 2);
+  hi = NVFP4_CVT_PK_FP4(hi, q[14], q[15], 3);
+  *out_codes = make_uint2(fix_zero_signs(lo), fix_zero_signs(hi));
   *out_scale = sbyte;
 }
 

@@ -303,6 +303,30 @@ def gemm_tolerance(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, g
     return tol
 
 
+def gemm_ref_with_norms(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, gs: float,
+                        bias_bits: np.ndarray | None = None, chunk_rows: int = 8192):
+    """One pass over the weight rows giving what a parity check needs.
+
+    Returns ``(y64, w_norm, abs_sum)``: the fp64 logits of ``gemm_ref``, the
+    2-norm of every dequantized weight row, and ``sum_k |x[m,k]| |w_deq[n,k]|``
+    (the magnitude that bounds any fp32 summation error).
+    """
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    xa = np.abs(x)
+    n = packed.shape[0]
+    y = np.empty((x.shape[0], n), dtype=np.float64)
+    s_abs = np.empty((x.shape[0], n), dtype=np.float64)
+    wn = np.empty(n, dtype=np.float64)
+    for r0 in range(0, n, chunk_rows):
+        wd = dequantize(packed[r0:r0 + chunk_rows], scales[r0:r0 + chunk_rows], gs)
+        y[:, r0:r0 + chunk_rows] = x @ wd.T
+        s_abs[:, r0:r0 + chunk_rows] = xa @ np.abs(wd).T
+        wn[r0:r0 + chunk_rows] = np.linalg.norm(wd, axis=1)
+    if bias_bits is not None:
+        y += bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    return y, wn, s_abs
+
+
 def bf16_round_rne(y: np.ndarray) -> np.ndarray:
     """float64 -> nearest bf16 value (ties to even) as float64, via exact float32 steps.
 

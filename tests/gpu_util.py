@@ -80,29 +80,43 @@ def gemm_gpu(x_bits, qdev, bias_bits=None):
     return host_bits(y)
 
 
-def tight_tolerance(x_bits, packed, scales, gs, y64, bias_bits=None):
-    """fp32 accumulation of K exact products (any order) + one bf16 rounding."""
-    x = np.abs(wl.bf16_bits_to_f32(x_bits).astype(np.float64))
-    wd = np.abs(O.dequantize(packed, scales, gs))
-    k = x.shape[1]
-    s_abs = x @ wd.T
-    acc = (k + 2) * 2.0 ** -24 * s_abs
-    if bias_bits is not None:
-        acc = acc + 2.0 ** -24 * np.abs(wl.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
-    return 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
+def half_ulp_bf16(v):
+    """Half a bf16 unit in the last place at |v| (0 for v == 0)."""
+    _, ex = np.frexp(np.abs(v))
+    return np.where(v == 0, 0.0, np.ldexp(1.0, ex - 9))
 
 
 def check_gemm(y_bits, x_bits, packed, scales, gs, bias_bits=None, label="", argmax_min=0.999,
-               y64=None):
+               pure_bound=None):
+    """Spec bound, tight fp32/bf16 bound and tie-aware argmax against the oracle.
+
+    The benchmark spec's bound 1e-3 * ||x_m|| * ||w_n|| is applied to the bf16 output,
+    so half a bf16 ulp of the exact logit (the rounding any bf16 result carries)
+    is added to it.  With ``pure_bound`` (default: K >= 512, where |cos(x_m, w_n)|
+    stays far below 0.25 for these inputs) the bound must also hold without it.
+    """
     y = wl.bf16_bits_to_f32(y_bits).astype(np.float64)
-    if y64 is None:
-        y64 = O.gemm_ref(x_bits, packed, scales, gs, bias_bits)
-    tol = O.gemm_tolerance(x_bits, packed, scales, gs, 1e-3, bias_bits)
+    y64, wn, s_abs = O.gemm_ref_with_norms(x_bits, packed, scales, gs, bias_bits)
+    xn = np.linalg.norm(wl.bf16_bits_to_f32(x_bits).astype(np.float64), axis=1)
+    bias_abs = 0.0 if bias_bits is None else np.abs(wl.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
+    # north-star bound: 1e-3 * ||x_m|| * ||w_n|| (+ bf16 rounding of a bias term)
+    tol = 1e-3 * xn[:, None] * wn[None, :] + 2.0 ** -8 * bias_abs
     err = np.abs(y - y64)
+    if pure_bound is None:
+        pure_bound = x_bits.shape[1] >= 512
+    if pure_bound:
+        worst = np.unravel_index(np.argmax(err - tol), err.shape)
+        assert np.all(err <= tol), (f"{label}: north-star bound (no output-rounding term) broken at "
+                                    f"{worst}: y={y[worst]} y64={y64[worst]} tol={tol[worst]}")
+    tol = tol + half_ulp_bf16(y64)
     worst = np.unravel_index(np.argmax(err - tol), err.shape)
     assert np.all(err <= tol), (f"{label}: north-star bound broken at {worst}: y={y[worst]} "
                                 f"y64={y64[worst]} tol={tol[worst]}")
-    tight = tight_tolerance(x_bits, packed, scales, gs, y64, bias_bits)
+    # tight bound: fp32 accumulation of K exact products in any order, the scale and
+    # bias operations, then one round-to-nearest to bf16
+    k = x_bits.shape[1]
+    acc = (k + 2) * 2.0 ** -24 * (s_abs + bias_abs)
+    tight = 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
     worst = np.unravel_index(np.argmax(err - tight), err.shape)
     assert np.all(err <= tight), (f"{label}: tight bound broken at {worst}: y={y[worst]} "
                                   f"y64={y64[worst]} tight={tight[worst]}")
