@@ -100,7 +100,8 @@ nvfp4_status nvfp4_refresh_inplace(const void* W, int64_t N, int64_t K,
  * (vLLM API docs, quantization.online.lm_head, _LMHeadNvfp4Method.apply:
  * weight-only NVFP4, activations stay in the model dtype.)
  *
- *   x            in   bf16 [M, K]     activations; M >= 0 (M == 0 enqueues nothing)
+ *   x            in   bf16 [M, K]     activations; M >= 0 (M == 0 enqueues nothing, and
+ *                                    x and y may then be NULL)
  *   packed, scales, global_scale in  as produced by nvfp4_quantize for [N, K]
  *   N            in   N >= 1
  *   bias         in   bf16 [N] or NULL

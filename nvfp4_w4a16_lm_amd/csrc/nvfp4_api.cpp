@@ -83,10 +83,12 @@ nvfp4_status nvfp4_refresh_inplace(const void* W, int64_t N, int64_t K, uint8_t*
 nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t M, int64_t K, const uint8_t* packed,
                               const uint8_t* scales, const float* global_scale, int64_t N,
                               const void* bias, void* y, void* stream) {
-  if (!x || !packed || !scales || !global_scale || !y) return NVFP4_ERR_NULL;
+  // x and y may be NULL when M == 0 (an empty activation tensor has no storage).
+  if (!packed || !scales || !global_scale || (M != 0 && (!x || !y))) return NVFP4_ERR_NULL;
   nvfp4_status s = check_weight_shape(N, K);
   if (s != NVFP4_OK) return s;
   if (M < 0 || M > kMaxPrefillM || M * K > kMaxElems || M * N > kMaxElems) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(packed, 16) || !aligned(scales, 4) ||
       !aligned(global_scale, 4) || (bias && !aligned(bias, 2)))
     return NVFP4_ERR_ALIGN;
@@ -95,7 +97,6 @@ nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t M, int64_t K, const uint8_t
                 overlap(ry, span(scales, N * K / 16)) || overlap(ry, span(global_scale, 4)) ||
                 (bias && overlap(ry, span(bias, N * 2)))))
     return NVFP4_ERR_ALIAS;
-  if (M == 0) return NVFP4_OK;
   g_last_hip_error[0] = '\0';
   const hipStream_t st = (hipStream_t)stream;
   if (M <= nvfp4::kDecodeMaxM)

@@ -111,8 +111,11 @@ def test_gemm_validation(lib):
     assert gm(lib, y=S - 16) == ERR_ALIAS
     assert gm(lib, y=G - 64) == ERR_ALIAS
     assert gm(lib, b=B, y=B - 32) == ERR_ALIAS
-    # M == 0 is an empty GEMM: validated, nothing enqueued, no HIP call
+    # M == 0 is an empty GEMM: validated, nothing enqueued, no HIP call; x and y
+    # may be NULL then (empty tensors have no storage)
     assert gm(lib, m=0) == OK
+    assert gm(lib, m=0, x=0, y=0) == OK
+    assert gm(lib, m=1, x=0) == ERR_NULL
 
 
 def test_binding_maps_shape_errors_to_valueerror(lib):
