@@ -1,0 +1,377 @@
+// Decode-side W4A16 NVFP4 GEMM for gfx950 (M <= 64 activation rows):
+// y[M,N] = x[M,K] . dequant(W)^T (+ bias), streaming the packed weight once.
+//
+// Method: vLLM API docs, quantization.online.lm_head, _LMHeadNvfp4Method.apply
+// (weight-only NVFP4; activations stay bf16).  Dequantized weight:
+// E2M1(code) * e4m3(scale) * global_scale; the global scale is applied once
+// per output in fp32.
+//
+// Two kernels, both HBM-bound by design (0.5625 B of weight per element):
+//
+// gemv_dot_kernel (M <= 2): one wavefront streams whole rows, each lane a
+//   fixed set of 16-byte segments (32 k) of every row, so the lane's slice of
+//   x stays in registers for the kernel's lifetime.  Per 16-block the E4M3
+//   scale is split into its power of two 2^e and its mantissa mu in [1, 2):
+//   the fp4->bf16 converter applies 2^e exactly (it only uses a scale's
+//   exponent), v_dot2_f32_bf16 accumulates a block partial, and mu is applied
+//   once per block.  About 1.4 VALU ops per weight at M = 1.
+//
+// gemv_mfma_kernel (M > 2): bf16 MFMA (v_mfma_f32_16x16x32_bf16) on weights
+//   dequantized in registers (exact code*scale in bf16).  A 256-thread
+//   workgroup stages each 256-k chunk of x (M rounded up to 16) in LDS once
+//   (double buffered), and each wavefront reuses those fragments for R tiles
+//   of 16 weight rows, with the next chunk's weights prefetched into
+//   registers while the current one computes.
+#include "nvfp4_device.hpp"
+#include "nvfp4_launch.hpp"
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t out_bf16(float acc, float gs, const uint16_t* __restrict__ bias, int n) {
+  float v = acc * gs;
+  if (bias != nullptr) v += __uint_as_float((uint32_t)bias[n] << 16);
+  return f32_to_bf16_rne(v);
+}
+
+// Sum over the 16 lanes of each DPP row (quad swaps, then half-row and row mirrors).
+__device__ __forceinline__ float dpp_row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half-row mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row mirror
+  return v;
+}
+
+// Four per-lane partials (rows 0..3 of a batch) -> full wavefront sums, with
+// row i ending up in every lane whose bits 5,4 equal (i >> 1, i & 1).
+__device__ __forceinline__ float wave_sum4(const float p[4], int lane) {
+  const bool h5 = lane & 32, h4 = lane & 16;
+  const float s0 = h5 ? p[0] : p[2], k0 = h5 ? p[2] : p[0];
+  const float s1 = h5 ? p[1] : p[3], k1 = h5 ? p[3] : p[1];
+  const float w0 = k0 + __shfl_xor(s0, 32, 64);
+  const float w1 = k1 + __shfl_xor(s1, 32, 64);
+  const float s = h4 ? w0 : w1, k = h4 ? w1 : w0;
+  return dpp_row_sum(k + __shfl_xor(s, 16, 64));
+}
+
+// ---------------------------------------------------------------------------
+// gemv_dot_kernel<MR, SEG>: M = MR (1 or 2) rows of x; SEG = 16-byte segments
+// per lane per row (K <= 2048 * SEG, K % 32 == 0).  Each wavefront owns
+// rows [w * rows_per_wave, ...), processed 4 at a time.
+// ---------------------------------------------------------------------------
+template <int MR, int SEG>
+__global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                       const uint8_t* __restrict__ packed,
+                                                       const uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ gs_ptr, int N,
+                                                       const uint16_t* __restrict__ bias,
+                                                       uint16_t* __restrict__ y, int rows_per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r_begin = wid * rows_per_wave;
+  if (r_begin >= N) return;
+  const int r_end = min(N, r_begin + rows_per_wave);
+  const int nseg = K >> 5;
+  const int64_t prow = K >> 1, srow = K >> 4;
+
+  // This lane's slice of x: segment j covers k = 32 * (lane + 64 j) .. + 32.
+  u32x4 xr[MR][SEG][4];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+      const int seg = lane + 64 * j;
+      const bool ok = (seg < nseg) && (m < M);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xr[m][j][q] = ok ? *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + 32 * seg + 8 * q)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+  const float gs = *gs_ptr;
+
+  for (int r0 = r_begin; r0 < r_end; r0 += 4) {
+    u32x4 pk[4][SEG];
+    uint32_t sc[4][SEG];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = min(r0 + i, r_end - 1);   // duplicates are computed, never stored
+#pragma unroll
+      for (int j = 0; j < SEG; ++j) {
+        const int seg = lane + 64 * j;
+        if (seg < nseg) {
+          pk[i][j] = load_stream16(packed + row * prow + 16 * seg);
+          sc[i][j] = *reinterpret_cast<const uint16_t*>(scales + row * srow + 2 * seg);
+        } else {
+          pk[i][j] = u32x4{0u, 0u, 0u, 0u};
+          sc[i][j] = 0u;
+        }
+      }
+    }
+    float p[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[m][i] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < SEG; ++j)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const float s = b ? NVFP4_E4M3_TO_F32(sc[i][j], 1) : NVFP4_E4M3_TO_F32(sc[i][j], 0);
+          const uint32_t sb = __float_as_uint(s);
+          const float e2 = __uint_as_float(sb & 0x7F800000u);                     // 2^e
+          const float mu = (s == 0.0f) ? 0.0f : __uint_as_float((sb & 0x807FFFFFu) | 0x3F800000u);
+          bf16x2 a[8];
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t w = pk[i][j][2 * b + d];
+            a[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, e2, 0);
+            a[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, e2, 1);
+            a[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, e2, 2);
+            a[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, e2, 3);
+          }
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            float blk = 0.0f;
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                blk = __builtin_amdgcn_fdot2_f32_bf16(
+                    a[4 * d + e], __builtin_bit_cast(bf16x2, xr[m][j][2 * b + d][e]), blk, false);
+            p[m][i] = fmaf(mu, blk, p[m][i]);
+          }
+        }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float tot = wave_sum4(p[m], lane);
+      const int row = r0 + ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+      if ((lane & 15) == 0 && row < r_end && m < M)
+        y[(int64_t)m * N + row] = (uint16_t)out_bf16(tot, gs, bias, row);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemv_mfma_kernel<MT, R, VEC>: MT = ceil(M/16) activation tiles, R weight
+// tiles of 16 rows per wavefront, 4 wavefronts per workgroup (64 R rows).
+// VEC: K % 256 == 0 (full chunks, 16-byte aligned weight rows).
+// Lane (r, g) = (lane % 16, lane / 16) owns k = c*256 + 64 g + [0, 64) of
+// weight row r of each tile; MFMA step t uses its k + 8 t .. + 8.
+// ---------------------------------------------------------------------------
+constexpr int kChunk = 256;
+constexpr int kXPitch = kChunk + 8;   // bf16 elements per LDS row (breaks bank alignment)
+
+template <int MT, int R, bool VEC>
+__global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                        const uint8_t* __restrict__ packed,
+                                                        const uint8_t* __restrict__ scales,
+                                                        const float* __restrict__ gs_ptr, int N,
+                                                        const uint16_t* __restrict__ bias,
+                                                        uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][16 * MT][kXPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n_base = blockIdx.x * (64 * R) + wave * (16 * R);
+  const int nchunks = (K + kChunk - 1) / kChunk;
+  const int64_t prow = K >> 1, srow = K >> 4;
+
+  const uint8_t* pr[R];
+  const uint8_t* sr[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    const int64_t row = min(n_base + 16 * t + r, N - 1);   // tail rows re-read row N-1, never stored
+    pr[t] = packed + row * prow;
+    sr[t] = scales + row * srow;
+  }
+
+  auto load_w = [&](int c, u32x4 (&wa)[R][2], uint32_t (&ws)[R]) {
+    const int kb = c * kChunk + 64 * g;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      if (VEC) {
+        wa[t][0] = load_stream16(pr[t] + kb / 2);
+        wa[t][1] = load_stream16(pr[t] + kb / 2 + 16);
+        ws[t] = *reinterpret_cast<const uint32_t*>(sr[t] + kb / 16);
+      } else {
+        ws[t] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kk = kb + 16 * j;
+          uint2 v = make_uint2(0u, 0u);
+          if (kk < K) {
+            v = *reinterpret_cast<const uint2*>(pr[t] + kk / 2);
+            ws[t] |= (uint32_t)sr[t][kk / 16] << (8 * j);
+          }
+          wa[t][j >> 1][2 * (j & 1)] = v.x;
+          wa[t][j >> 1][2 * (j & 1) + 1] = v.y;
+        }
+      }
+    }
+  };
+
+  // x staging: 16*MT rows x 256 k = 512*MT vectors of 8 bf16, 2*MT per thread.
+  auto load_x = [&](int c, u32x4 (&xv)[2 * MT]) {
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) {
+      const int v = tid + 256 * i;
+      const int m = v >> 5, k = c * kChunk + 8 * (v & 31);
+      xv[i] = (m < M && k < K) ? *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k)
+                               : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&](int buf, const u32x4 (&xv)[2 * MT]) {
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) {
+      const int v = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(&xs[buf][v >> 5][8 * (v & 31)]) = xv[i];
+    }
+  };
+
+  f32x4 acc[R][MT];
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf, const u32x4 (&wa)[R][2], const uint32_t (&ws)[R]) {
+    float sv[R][4];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      sv[t][0] = NVFP4_E4M3_TO_F32(ws[t], 0);
+      sv[t][1] = NVFP4_E4M3_TO_F32(ws[t], 1);
+      sv[t][2] = NVFP4_E4M3_TO_F32(ws[t], 2);
+      sv[t][3] = NVFP4_E4M3_TO_F32(ws[t], 3);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 bx[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        bx[mt] = *reinterpret_cast<const bf16x8*>(&xs[buf][16 * mt + r][64 * g + 8 * s]);
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const bf16x8 a = dequant8(wa[t][s >> 2][s & 3], sv[t][s >> 1]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[mt], acc[t][mt]);
+      }
+    }
+  };
+
+  u32x4 wa0[R][2], wa1[R][2];
+  uint32_t ws0[R], ws1[R];
+  u32x4 xv[2 * MT];
+  load_w(0, wa0, ws0);
+  load_x(0, xv);
+  store_x(0, xv);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    // even chunk c in buffer 0 / registers wa0; prefetch c + 1
+    const bool has1 = c + 1 < nchunks;
+    if (has1) {
+      load_w(c + 1, wa1, ws1);
+      load_x(c + 1, xv);
+    }
+    compute(0, wa0, ws0);
+    if (has1) store_x(1, xv);
+    __syncthreads();
+    if (!has1) break;
+    const bool has2 = c + 2 < nchunks;
+    if (has2) {
+      load_w(c + 2, wa0, ws0);
+      load_x(c + 2, xv);
+    }
+    compute(1, wa1, ws1);
+    if (has2) store_x(0, xv);
+    __syncthreads();
+  }
+
+  const float gs = *gs_ptr;
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    const int n0 = n_base + 16 * t + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + r;
+      if (m >= M) continue;
+      uint16_t* yrow = y + (int64_t)m * N;
+      if ((N & 3) == 0 && n0 + 3 < N) {
+        const uint32_t lo = out_bf16(acc[t][mt][0], gs, bias, n0) | (out_bf16(acc[t][mt][1], gs, bias, n0 + 1) << 16);
+        const uint32_t hi = out_bf16(acc[t][mt][2], gs, bias, n0 + 2) | (out_bf16(acc[t][mt][3], gs, bias, n0 + 3) << 16);
+        *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[t][mt][v], gs, bias, n0 + v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int MR, int SEG>
+static hipError_t dot_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
+                             const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
+  // ~16 resident wavefronts per CU on 256 CUs; rows per wavefront a multiple of 4.
+  const int target_waves = 256 * 16;
+  int rpw = (N + target_waves - 1) / target_waves;
+  rpw = (rpw + 3) & ~3;
+  const int waves = (N + rpw - 1) / rpw;
+  return launch_kernel((const void*)gemv_dot_kernel<MR, SEG>, dim3((waves + 3) / 4), dim3(256), stream,
+                       (const uint16_t*)x, M, K, packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y,
+                       rpw);
+}
+
+template <int MR>
+static hipError_t dot_dispatch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
+                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
+  switch ((K + 2047) / 2048) {
+    case 1: return dot_launch<MR, 1>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 2: return dot_launch<MR, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 3: return dot_launch<MR, 3>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    default: return dot_launch<MR, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+  }
+}
+
+template <int MT, int R>
+static hipError_t mfma_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
+                              const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
+  const dim3 grid((N + 64 * R - 1) / (64 * R));
+  const void* fn = (K % kChunk == 0) ? (const void*)gemv_mfma_kernel<MT, R, true>
+                                     : (const void*)gemv_mfma_kernel<MT, R, false>;
+  return launch_kernel(fn, grid, dim3(256), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
+                       (const uint16_t*)bias, (uint16_t*)y);
+}
+
+// The dot kernel keeps the lane's slice of x in registers (16 * ceil(K/2048)
+// VGPRs per activation row), so it takes M = 1 up to K = 8192 and M = 2 up to
+// K = 4096; everything else goes to the MFMA kernel.
+bool decode_uses_dot(int64_t M, int64_t K) {
+  return K % 32 == 0 && ((M == 1 && K <= 8192) || (M == 2 && K <= 4096));
+}
+
+hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* packed, const uint8_t* scales,
+                       const float* gs, int64_t N64, const void* bias, void* y, hipStream_t stream) {
+  const int M = (int)M64, K = (int)K64, N = (int)N64;
+  if (decode_uses_dot(M, K)) {
+    if (M == 1) return dot_dispatch<1>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    return dot_dispatch<2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+  }
+  switch ((M + 15) / 16) {
+    case 1: return mfma_launch<1, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 2: return mfma_launch<2, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 3: return mfma_launch<3, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    default: return mfma_launch<4, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+  }
+}
+
+}  // namespace nvfp4

@@ -1,19 +1,18 @@
-// W4A16 NVFP4 GEMM kernels for gfx950: y[M,N] = x[M,K] . dequant(W)^T (+ bias).
+// Prefill-side W4A16 NVFP4 GEMM for gfx950 (M > 64 activation rows):
+// y[M,N] = x[M,K] . dequant(W)^T (+ bias) on bf16 MFMA.
 //
 // Method: vLLM API docs, quantization.online.lm_head, _LMHeadNvfp4Method.apply
 // (weight-only NVFP4 on the platform's W4A16 kernel; activations stay bf16).
 // Dequantized weight: E2M1(code) * e4m3(scale) * global_scale.  code * scale
-// has at most 6 significant bits, so it is exact in bf16; the kernels feed it
-// to bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate) and apply the
+// has at most 6 significant bits, so it is exact in bf16; the kernel feeds it
+// to bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate) and applies the
 // global scale once per output in the fp32 epilogue.
 //
 // MFMA operand roles: the weight tile is the A operand (16 rows = 16 vocab
 // rows n), the activation tile the B operand (16 columns = 16 rows m of x).
 // Lane l holds row/column (l % 16) and 8 consecutive k of k-group (l / 16);
 // the accumulator lane l holds D[4*(l/16) + v][l % 16], v = 0..3, i.e. four
-// consecutive n for one m.  Any assignment of k to (k-group, element) works as
-// long as A and B use the same one, which lets each lane own a contiguous run
-// of packed bytes.
+// consecutive n for one m.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -28,86 +27,6 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ y, const uint16
   float v = acc * gs;
   if (bias != nullptr) v += __uint_as_float((uint32_t)bias[n] << 16);
   y[m * N + n] = (uint16_t)f32_to_bf16_rne(v);
-}
-
-// ---------------------------------------------------------------------------
-// Decode: M <= 64.  One wavefront per 16 weight rows, streaming the rows'
-// packed codes and scales once from HBM; MT = ceil(M / 16) activation tiles.
-// Per 256-k chunk each lane loads 32 packed bytes (64 k of one row) and the
-// 4 scale bytes of those k, dequantizes 8 k at a time in registers and issues
-// one MFMA per activation tile.
-// VEC: K % 256 == 0, so every chunk is full and rows are 16-byte aligned.
-// ---------------------------------------------------------------------------
-template <int MT, bool VEC>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ x, int M, int K,
-                                                   const uint8_t* __restrict__ packed,
-                                                   const uint8_t* __restrict__ scales,
-                                                   const float* __restrict__ gs_ptr, int N,
-                                                   const uint16_t* __restrict__ bias,
-                                                   uint16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * 4 + wave) * 16;
-  if (n0 >= N) return;
-  const int r = lane & 15, g = lane >> 4;
-  const int nrow = min(n0 + r, N - 1);          // tail rows re-read row N-1; never stored
-  const uint8_t* prow = packed + (int64_t)nrow * (K / 2);
-  const uint8_t* srow = scales + (int64_t)nrow * (K / 16);
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nchunks = (K + 255) / 256;
-  for (int c = 0; c < nchunks; ++c) {
-    const int kb = c * 256 + 64 * g;            // first k of this lane's 64
-    uint32_t pw[8];
-    uint32_t sc = 0;
-    if (VEC) {
-      const u32x4 a = load_stream16(prow + kb / 2);
-      const u32x4 b = load_stream16(prow + kb / 2 + 16);
-      pw[0] = a[0]; pw[1] = a[1]; pw[2] = a[2]; pw[3] = a[3];
-      pw[4] = b[0]; pw[5] = b[1]; pw[6] = b[2]; pw[7] = b[3];
-      sc = *reinterpret_cast<const uint32_t*>(srow + kb / 16);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = kb + 16 * j;
-        if (kk < K) {
-          const uint2 v = *reinterpret_cast<const uint2*>(prow + kk / 2);
-          pw[2 * j] = v.x;
-          pw[2 * j + 1] = v.y;
-          sc |= (uint32_t)srow[kk / 16] << (8 * j);
-        } else {
-          pw[2 * j] = 0u;
-          pw[2 * j + 1] = 0u;
-        }
-      }
-    }
-    const float sv[4] = {NVFP4_E4M3_TO_F32(sc, 0), NVFP4_E4M3_TO_F32(sc, 1), NVFP4_E4M3_TO_F32(sc, 2),
-                         NVFP4_E4M3_TO_F32(sc, 3)};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const bf16x8 a = dequant8(pw[t], sv[t >> 1]);
-      const int k = kb + 8 * t;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + r;
-        u32x4 xv = {0u, 0u, 0u, 0u};
-        if (m < M && (VEC || k < K)) xv = *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k);
-        acc[mt] = mfma16x16x32(a, __builtin_bit_cast(bf16x8, xv), acc[mt]);
-      }
-    }
-  }
-  const float gs = *gs_ptr;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + r;
-    if (m >= M) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int n = n0 + 4 * g + v;
-      if (n < N) store_out(y, bias, m, n, N, acc[mt][v], gs);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -212,36 +131,8 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// launchers
+// launcher
 // ---------------------------------------------------------------------------
-template <int MT, bool VEC>
-static hipError_t gemv_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
-                              const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  const int tiles = (N + 15) / 16;
-  const dim3 grid((tiles + 3) / 4);
-  return launch_kernel((const void*)gemv_kernel<MT, VEC>, grid, dim3(256), stream,
-                       (const uint16_t*)x, M, K, packed, scales, gs, N, (const uint16_t*)bias,
-                       (uint16_t*)y);
-}
-
-template <bool VEC>
-static hipError_t gemv_dispatch_m(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
-                                  const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  switch ((M + 15) / 16) {
-    case 1: return gemv_launch<1, VEC>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    case 2: return gemv_launch<2, VEC>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    case 3: return gemv_launch<3, VEC>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    default: return gemv_launch<4, VEC>(x, M, K, packed, scales, gs, N, bias, y, stream);
-  }
-}
-
-hipError_t launch_gemv(const void* x, int64_t M, int64_t K, const uint8_t* packed, const uint8_t* scales,
-                       const float* global_scale, int64_t N, const void* bias, void* y, hipStream_t stream) {
-  if (K % 256 == 0)
-    return gemv_dispatch_m<true>(x, (int)M, (int)K, packed, scales, global_scale, (int)N, bias, y, stream);
-  return gemv_dispatch_m<false>(x, (int)M, (int)K, packed, scales, global_scale, (int)N, bias, y, stream);
-}
-
 hipError_t launch_gemm_prefill(const void* x, int64_t M, int64_t K, const uint8_t* packed,
                                const uint8_t* scales, const float* global_scale, int64_t N,
                                const void* bias, void* y, hipStream_t stream) {
