@@ -143,9 +143,12 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
 #pragma unroll
             for (int d = 0; d < 2; ++d)
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                blk = __builtin_amdgcn_fdot2_f32_bf16(
-                    a[4 * d + e], __builtin_bit_cast(bf16x2, xr[m][j][2 * b + d][e]), blk, false);
+              for (int e = 0; e < 4; ++e) {
+                // copy the vector element to a scalar first: a bit_cast applied
+                // directly to an element of an ext_vector lvalue reads element 0
+                const uint32_t xe = xr[m][j][2 * b + d][e];
+                blk = __builtin_amdgcn_fdot2_f32_bf16(a[4 * d + e], __builtin_bit_cast(bf16x2, xe), blk, false);
+              }
             p[m][i] = fmaf(mu, blk, p[m][i]);
           }
         }
