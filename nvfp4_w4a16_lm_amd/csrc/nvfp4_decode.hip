@@ -63,7 +63,8 @@ __device__ __forceinline__ float wave_sum4(const float p[4], int lane) {
 // ---------------------------------------------------------------------------
 // gemv_dot_kernel<MR, SEG>: M = MR (1 or 2) rows of x; SEG = 16-byte segments
 // per lane per row (K <= 2048 * SEG, K % 32 == 0).  Each wavefront owns
-// rows [w * rows_per_wave, ...), processed 4 at a time.
+// rows [w * rows_per_wave, ...), processed 4 at a time with the next 4 in
+// flight; the grid holds one wavefront per resident slot.
 // ---------------------------------------------------------------------------
 template <int MR, int SEG>
 __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restrict__ x, int M, int K,
@@ -81,6 +82,10 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
   const int64_t prow = K >> 1, srow = K >> 4;
 
   // This lane's slice of x: segment j covers k = 32 * (lane + 64 j) .. + 32.
+  // Segments past the row end (seg >= nseg) hold zeros, so the duplicate
+  // weights the clamped loads below fetch for them contribute nothing.
+  // All loads are unconditional (clamped addresses, then a select): a
+  // branch around a load makes the compiler wait for it before going on.
   u32x4 xr[MR][SEG][4];
 #pragma unroll
   for (int m = 0; m < MR; ++m)
@@ -88,31 +93,29 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
     for (int j = 0; j < SEG; ++j) {
       const int seg = lane + 64 * j;
       const bool ok = (seg < nseg) && (m < M);
+      const int64_t base = (int64_t)min(m, M - 1) * K + 32 * min(seg, nseg - 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xr[m][j][q] = ok ? *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + 32 * seg + 8 * q)
-                         : u32x4{0u, 0u, 0u, 0u};
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(x + base + 8 * q);
+        xr[m][j][q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   const float gs = *gs_ptr;
 
-  for (int r0 = r_begin; r0 < r_end; r0 += 4) {
-    u32x4 pk[4][SEG];
-    uint32_t sc[4][SEG];
+  auto load_batch = [&](int r0, u32x4 (&pk)[4][SEG], uint32_t (&sc)[4][SEG]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = min(r0 + i, r_end - 1);   // duplicates are computed, never stored
 #pragma unroll
       for (int j = 0; j < SEG; ++j) {
-        const int seg = lane + 64 * j;
-        if (seg < nseg) {
-          pk[i][j] = load_stream16(packed + row * prow + 16 * seg);
-          sc[i][j] = *reinterpret_cast<const uint16_t*>(scales + row * srow + 2 * seg);
-        } else {
-          pk[i][j] = u32x4{0u, 0u, 0u, 0u};
-          sc[i][j] = 0u;
-        }
+        const int seg = min(lane + 64 * j, nseg - 1);
+        pk[i][j] = load_stream16(packed + row * prow + 16 * seg);
+        sc[i][j] = *reinterpret_cast<const uint16_t*>(scales + row * srow + 2 * seg);
       }
     }
+  };
+
+  auto compute_batch = [&](int r0, const u32x4 (&pk)[4][SEG], const uint32_t (&sc)[4][SEG]) {
     float p[MR][4];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
@@ -159,20 +162,45 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
       if ((lane & 15) == 0 && row < r_end && m < M)
         y[(int64_t)m * N + row] = (uint16_t)out_bf16(tot, gs, bias, row);
     }
+  };
+
+  // Two batches of 4 rows in flight: the next batch loads while this one computes.
+  u32x4 pkA[4][SEG], pkB[4][SEG];
+  uint32_t scA[4][SEG], scB[4][SEG];
+  load_batch(r_begin, pkA, scA);
+  for (int r0 = r_begin; r0 < r_end; r0 += 8) {
+    const bool hasB = r0 + 4 < r_end;
+    if (hasB) load_batch(r0 + 4, pkB, scB);
+    compute_batch(r0, pkA, scA);
+    if (!hasB) break;
+    if (r0 + 8 < r_end) load_batch(r0 + 8, pkA, scA);
+    compute_batch(r0 + 4, pkB, scB);
   }
 }
 
 // ---------------------------------------------------------------------------
-// gemv_mfma_kernel<MT, R, VEC>: MT = ceil(M/16) activation tiles, R weight
-// tiles of 16 rows per wavefront, 4 wavefronts per workgroup (64 R rows).
-// VEC: K % 256 == 0 (full chunks, 16-byte aligned weight rows).
-// Lane (r, g) = (lane % 16, lane / 16) owns k = c*256 + 64 g + [0, 64) of
-// weight row r of each tile; MFMA step t uses its k + 8 t .. + 8.
+// gemv_mfma_kernel<MT, R>: MT = ceil(M/16) activation tiles, R weight tiles
+// of 16 rows per wavefront, 4 wavefronts per workgroup (64 R rows per block).
+//
+// HBM streams at full rate only when every load instruction covers whole
+// 128-byte lines of a row (measured: ~7.5 TB/s with 8 lanes per row, ~4.5
+// TB/s with the 4 lanes per row the MFMA operand layout gives).  So weights
+// are loaded 8 lanes per row -- per 256-k chunk, a 16-row tile is two
+// instructions of 8 rows x 128 B -- and transposed through a per-wavefront
+// LDS region into the operand layout: lane (r, g) = (lane % 16, lane / 16)
+// reads row r, bytes [32 g, 32 g + 32) of the chunk, i.e. k = 256 c + 64 g
+// + [0, 64); MFMA step s uses k + 8 s .. + 8.  Scales come in whole lines
+// too (128 B = 8 chunks per row) and are staged the same way.  The chunk of
+// x (M rounded up to 16) is staged once per workgroup in double-buffered
+// LDS.  Needs K % 256 == 0 (whole lines per row); rows past N are read from
+// clamped addresses and their outputs are never stored.
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 256;
-constexpr int kXPitch = kChunk + 8;   // bf16 elements per LDS row (breaks bank alignment)
+constexpr int kXPitch = kChunk + 8;   // bf16 per LDS row of x (breaks bank alignment)
+constexpr int kWPitch = 128 + 16;     // bytes per LDS row of a weight tile
+constexpr int kSuper = 8;             // chunks per 128-byte line of scales
 
-template <int MT, int R, bool VEC>
+template <int MT, int R>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                         const uint8_t* __restrict__ packed,
                                                         const uint8_t* __restrict__ scales,
@@ -180,158 +208,240 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ bias,
                                                         uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][16 * MT][kXPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t wl[4][R][16][kWPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t sl[4][R][16][kWPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int n_base = blockIdx.x * (64 * R) + wave * (16 * R);
+  const int lr = lane >> 3, lq = lane & 7;          // loader: row within 8, 16-byte piece of the line
   const int nchunks = (K + kChunk - 1) / kChunk;
   const int64_t prow = K >> 1, srow = K >> 4;
+  const int nblocks = (N + 64 * R - 1) / (64 * R);
+  const float gs = *gs_ptr;
 
-  const uint8_t* pr[R];
-  const uint8_t* sr[R];
+  for (int rb = blockIdx.x; rb < nblocks; rb += gridDim.x) {
+    const int n_base = rb * (64 * R) + wave * (16 * R);
+    // loader row pointers: tile t, half j covers rows n_base + 16 t + 8 j + lr
+    const uint8_t* lp[R][2];
+    const uint8_t* ls[R][2];
 #pragma unroll
-  for (int t = 0; t < R; ++t) {
-    const int64_t row = min(n_base + 16 * t + r, N - 1);   // tail rows re-read row N-1, never stored
-    pr[t] = packed + row * prow;
-    sr[t] = scales + row * srow;
-  }
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t row = min(n_base + 16 * t + 8 * j + lr, N - 1);
+        lp[t][j] = packed + row * prow;
+        ls[t][j] = scales + row * srow;
+      }
+    auto load_w = [&](int c, u32x4 (&wr)[R][2]) {
+      const int64_t off = min((int64_t)128 * c + 16 * lq, prow - 16);
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wr[t][j] = load_stream16(lp[t][j] + off);
+    };
+    auto load_s = [&](int sc, u32x4 (&sr)[R][2]) {
+      const int64_t off = min((int64_t)128 * sc + 16 * lq, srow - 16);
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sr[t][j] = load_stream16(ls[t][j] + off);
+    };
+    auto stage = [&](const u32x4 (&v)[R][2], uint8_t (*dst)[16][kWPitch]) {
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&dst[t][8 * j + lr][16 * lq]) = v[t][j];
+    };
+    // x staging: 16*MT rows x 256 k = 512*MT vectors of 8 bf16, 2*MT per thread.
+    auto load_x = [&](int c, u32x4 (&xv)[2 * MT]) {
+#pragma unroll
+      for (int i = 0; i < 2 * MT; ++i) {
+        const int v = tid + 256 * i;
+        const int m = v >> 5, k = c * kChunk + 8 * (v & 31);
+        const u32x4 val = *reinterpret_cast<const u32x4*>(x + (int64_t)min(m, M - 1) * K + min(k, K - 8));
+        xv[i] = (m < M && k < K) ? val : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto store_x = [&](int buf, const u32x4 (&xv)[2 * MT]) {
+#pragma unroll
+      for (int i = 0; i < 2 * MT; ++i) {
+        const int v = tid + 256 * i;
+        *reinterpret_cast<u32x4*>(&xs[buf][v >> 5][8 * (v & 31)]) = xv[i];
+      }
+    };
 
-  auto load_w = [&](int c, u32x4 (&wa)[R][2], uint32_t (&ws)[R]) {
-    const int kb = c * kChunk + 64 * g;
+    f32x4 acc[R][MT];
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int c, int buf) {
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g]);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g + 16]);
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(&sl[wave][t][r][16 * (c % kSuper) + 4 * g]);
+        const float sv0 = NVFP4_E4M3_TO_F32(sw, 0), sv1 = NVFP4_E4M3_TO_F32(sw, 1);
+        const float sv2 = NVFP4_E4M3_TO_F32(sw, 2), sv3 = NVFP4_E4M3_TO_F32(sw, 3);
+        const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const float sv[4] = {sv0, sv1, sv2, sv3};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 a = dequant8(wd[s], sv[s >> 1]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const bf16x8 bx = *reinterpret_cast<const bf16x8*>(&xs[buf][16 * mt + r][64 * g + 8 * s]);
+            acc[t][mt] = mfma16x16x32(a, bx, acc[t][mt]);
+          }
+        }
+      }
+    };
+
+    u32x4 wr0[R][2], wr1[R][2], sr[R][2];
+    u32x4 xv[2 * MT];
+    load_x(0, xv);
+    load_s(0, sr);
+    load_w(0, wr0);
+    store_x(0, xv);
+    __syncthreads();
+    // one step: stage chunk c's weights (and, every kSuper chunks, a line of
+    // scales) into this wavefront's LDS, compute, stage the prefetched x
+    auto step = [&](int c, const u32x4 (&wcur)[R][2], u32x4 (&wnext)[R][2]) {
+      const bool has_next = c + 1 < nchunks;
+      if (has_next) {
+        load_x(c + 1, xv);          // x first: waiting on it must not wait on the weights
+        load_w(c + 1, wnext);
+      }
+      if (c % kSuper == 0) {
+        stage(sr, sl[wave]);
+        if (c + kSuper < nchunks) load_s(c / kSuper + 1, sr);
+      }
+      stage(wcur, wl[wave]);
+      compute(c, c & 1);
+      if (has_next) store_x((c + 1) & 1, xv);
+      __syncthreads();
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+      step(c, wr0, wr1);
+      if (c + 1 < nchunks) step(c + 1, wr1, wr0);
+    }
+
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-      if (VEC) {
-        wa[t][0] = load_stream16(pr[t] + kb / 2);
-        wa[t][1] = load_stream16(pr[t] + kb / 2 + 16);
-        ws[t] = *reinterpret_cast<const uint32_t*>(sr[t] + kb / 16);
-      } else {
-        ws[t] = 0u;
+      const int n0 = n_base + 16 * t + 4 * g;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kk = kb + 16 * j;
-          uint2 v = make_uint2(0u, 0u);
-          if (kk < K) {
-            v = *reinterpret_cast<const uint2*>(pr[t] + kk / 2);
-            ws[t] |= (uint32_t)sr[t][kk / 16] << (8 * j);
-          }
-          wa[t][j >> 1][2 * (j & 1)] = v.x;
-          wa[t][j >> 1][2 * (j & 1) + 1] = v.y;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + r;
+        if (m >= M) continue;
+        uint16_t* yrow = y + (int64_t)m * N;
+        if ((N & 3) == 0 && n0 + 3 < N) {
+          const uint32_t lo = out_bf16(acc[t][mt][0], gs, bias, n0) | (out_bf16(acc[t][mt][1], gs, bias, n0 + 1) << 16);
+          const uint32_t hi = out_bf16(acc[t][mt][2], gs, bias, n0 + 2) | (out_bf16(acc[t][mt][3], gs, bias, n0 + 3) << 16);
+          *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[t][mt][v], gs, bias, n0 + v);
         }
       }
     }
-  };
+  }  // row blocks
+}
 
-  // x staging: 16*MT rows x 256 k = 512*MT vectors of 8 bf16, 2*MT per thread.
-  auto load_x = [&](int c, u32x4 (&xv)[2 * MT]) {
+// ---------------------------------------------------------------------------
+// gemv_mfma_ragged_kernel<MT>: the same MFMA arithmetic for K % 256 != 0,
+// where rows are not whole 128-byte lines.  One wavefront per 16 rows, the x
+// chunk staged in LDS per workgroup, and per-block 8-byte weight loads from
+// clamped addresses; blocks past the row end get scale 0.  Kept simple: ragged
+// K does not occur in the lm_head shapes this path is tuned for.
+// ---------------------------------------------------------------------------
+template <int MT>
+__global__ __launch_bounds__(256) void gemv_mfma_ragged_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                               const uint8_t* __restrict__ packed,
+                                                               const uint8_t* __restrict__ scales,
+                                                               const float* __restrict__ gs_ptr, int N,
+                                                               const uint16_t* __restrict__ bias,
+                                                               uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[16 * MT][kXPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n_base = blockIdx.x * 64 + wave * 16;
+  const int64_t row = min(n_base + r, N - 1);
+  const uint8_t* pr = packed + row * (K >> 1);
+  const uint8_t* sr = scales + row * (K >> 4);
+  const int nchunks = (K + kChunk - 1) / kChunk;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nchunks; ++c) {
+    __syncthreads();   // the previous chunk's fragment reads are done
 #pragma unroll
     for (int i = 0; i < 2 * MT; ++i) {
       const int v = tid + 256 * i;
       const int m = v >> 5, k = c * kChunk + 8 * (v & 31);
-      xv[i] = (m < M && k < K) ? *reinterpret_cast<const u32x4*>(x + (int64_t)m * K + k)
-                               : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 val = *reinterpret_cast<const u32x4*>(x + (int64_t)min(m, M - 1) * K + min(k, K - 8));
+      *reinterpret_cast<u32x4*>(&xs[m][8 * (v & 31)]) = (m < M && k < K) ? val : u32x4{0u, 0u, 0u, 0u};
     }
-  };
-  auto store_x = [&](int buf, const u32x4 (&xv)[2 * MT]) {
+    __syncthreads();
+    const int kb = c * kChunk + 64 * g;
+    uint32_t pw[8], ws = 0u;
 #pragma unroll
-    for (int i = 0; i < 2 * MT; ++i) {
-      const int v = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(&xs[buf][v >> 5][8 * (v & 31)]) = xv[i];
+    for (int j = 0; j < 4; ++j) {
+      const int kk = kb + 16 * j;
+      const int kc = min(kk, K - 16);
+      const uint2 v = *reinterpret_cast<const uint2*>(pr + kc / 2);
+      const uint32_t sbyte = sr[kc / 16];
+      ws |= (kk < K ? sbyte : 0u) << (8 * j);
+      pw[2 * j] = v.x;
+      pw[2 * j + 1] = v.y;
     }
-  };
-
-  f32x4 acc[R][MT];
-#pragma unroll
-  for (int t = 0; t < R; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int buf, const u32x4 (&wa)[R][2], const uint32_t (&ws)[R]) {
-    float sv[R][4];
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      sv[t][0] = NVFP4_E4M3_TO_F32(ws[t], 0);
-      sv[t][1] = NVFP4_E4M3_TO_F32(ws[t], 1);
-      sv[t][2] = NVFP4_E4M3_TO_F32(ws[t], 2);
-      sv[t][3] = NVFP4_E4M3_TO_F32(ws[t], 3);
-    }
+    const float sv[4] = {NVFP4_E4M3_TO_F32(ws, 0), NVFP4_E4M3_TO_F32(ws, 1), NVFP4_E4M3_TO_F32(ws, 2),
+                         NVFP4_E4M3_TO_F32(ws, 3)};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      bf16x8 bx[MT];
+      const bf16x8 a = dequant8(pw[s], sv[s >> 1]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        bx[mt] = *reinterpret_cast<const bf16x8*>(&xs[buf][16 * mt + r][64 * g + 8 * s]);
-#pragma unroll
-      for (int t = 0; t < R; ++t) {
-        const bf16x8 a = dequant8(wa[t][s >> 2][s & 3], sv[t][s >> 1]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[mt], acc[t][mt]);
-      }
+        acc[mt] = mfma16x16x32(a, *reinterpret_cast<const bf16x8*>(&xs[16 * mt + r][64 * g + 8 * s]), acc[mt]);
     }
-  };
-
-  u32x4 wa0[R][2], wa1[R][2];
-  uint32_t ws0[R], ws1[R];
-  u32x4 xv[2 * MT];
-  load_w(0, wa0, ws0);
-  load_x(0, xv);
-  store_x(0, xv);
-  __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    // even chunk c in buffer 0 / registers wa0; prefetch c + 1
-    const bool has1 = c + 1 < nchunks;
-    if (has1) {
-      load_w(c + 1, wa1, ws1);
-      load_x(c + 1, xv);
-    }
-    compute(0, wa0, ws0);
-    if (has1) store_x(1, xv);
-    __syncthreads();
-    if (!has1) break;
-    const bool has2 = c + 2 < nchunks;
-    if (has2) {
-      load_w(c + 2, wa0, ws0);
-      load_x(c + 2, xv);
-    }
-    compute(1, wa1, ws1);
-    if (has2) store_x(0, xv);
-    __syncthreads();
   }
-
+  if (n_base >= N) return;
   const float gs = *gs_ptr;
+  const int n0 = n_base + 4 * g;
 #pragma unroll
-  for (int t = 0; t < R; ++t) {
-    const int n0 = n_base + 16 * t + 4 * g;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = 16 * mt + r;
+    if (m >= M) continue;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = 16 * mt + r;
-      if (m >= M) continue;
-      uint16_t* yrow = y + (int64_t)m * N;
-      if ((N & 3) == 0 && n0 + 3 < N) {
-        const uint32_t lo = out_bf16(acc[t][mt][0], gs, bias, n0) | (out_bf16(acc[t][mt][1], gs, bias, n0 + 1) << 16);
-        const uint32_t hi = out_bf16(acc[t][mt][2], gs, bias, n0 + 2) | (out_bf16(acc[t][mt][3], gs, bias, n0 + 3) << 16);
-        *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[t][mt][v], gs, bias, n0 + v);
-      }
-    }
+    for (int v = 0; v < 4; ++v)
+      if (n0 + v < N) y[(int64_t)m * N + n0 + v] = (uint16_t)out_bf16(acc[mt][v], gs, bias, n0 + v);
   }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Workgroups of 256 threads that fit on the device at once (occupancy x CUs).
+static int resident_workgroups(const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  return cus * per_cu;
+}
+
 template <int MR, int SEG>
 static hipError_t dot_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
                              const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  // ~16 resident wavefronts per CU on 256 CUs; rows per wavefront a multiple of 4.
-  const int target_waves = 256 * 16;
-  int rpw = (N + target_waves - 1) / target_waves;
-  rpw = (rpw + 3) & ~3;
-  const int waves = (N + rpw - 1) / rpw;
-  return launch_kernel((const void*)gemv_dot_kernel<MR, SEG>, dim3((waves + 3) / 4), dim3(256), stream,
-                       (const uint16_t*)x, M, K, packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y,
-                       rpw);
+  // One contiguous run of rows per resident wavefront, a multiple of 8 rows
+  // (two batches of 4), so every wavefront finishes in the same round.
+  const void* fn = (const void*)gemv_dot_kernel<MR, SEG>;
+  const int waves = 4 * resident_workgroups(fn);
+  int rpw = (N + waves - 1) / waves;
+  rpw = (rpw + 7) & ~7;
+  const int used = (N + rpw - 1) / rpw;
+  return launch_kernel(fn, dim3((used + 3) / 4), dim3(256), stream, (const uint16_t*)x, M, K, packed, scales, gs,
+                       N, (const uint16_t*)bias, (uint16_t*)y, rpw);
 }
 
 template <int MR>
@@ -348,9 +458,12 @@ static hipError_t dot_dispatch(const void* x, int M, int K, const uint8_t* packe
 template <int MT, int R>
 static hipError_t mfma_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  const dim3 grid((N + 64 * R - 1) / (64 * R));
-  const void* fn = (K % kChunk == 0) ? (const void*)gemv_mfma_kernel<MT, R, true>
-                                     : (const void*)gemv_mfma_kernel<MT, R, false>;
+  if (K % kChunk != 0)
+    return launch_kernel((const void*)gemv_mfma_ragged_kernel<MT>, dim3((N + 63) / 64), dim3(256), stream,
+                         (const uint16_t*)x, M, K, packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y);
+  const void* fn = (const void*)gemv_mfma_kernel<MT, R>;
+  const int nblocks = (N + 64 * R - 1) / (64 * R);
+  const dim3 grid(std::min(nblocks, resident_workgroups(fn)));
   return launch_kernel(fn, grid, dim3(256), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
                        (const uint16_t*)bias, (uint16_t*)y);
 }
@@ -370,7 +483,7 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     return dot_dispatch<2>(x, M, K, packed, scales, gs, N, bias, y, stream);
   }
   switch ((M + 15) / 16) {
-    case 1: return mfma_launch<1, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 1: return mfma_launch<1, 1>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 2: return mfma_launch<2, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 3: return mfma_launch<3, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
     default: return mfma_launch<4, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);

@@ -7,14 +7,26 @@
 // byte, low nibble first.
 //
 // Launch sequence on one stream (no host sync, no allocation, no memset node):
-//   1. amax_init     : global_scale word <- 0 (it accumulates |amax| bits)
-//   2. amax          : one integer atomic max per workgroup
-//   3. global_scale  : 1 thread turns the amax bits into the fp32 global scale
-//   4. quant_pack    : every thread re-derives 1/gs and encodes 16-weight blocks
+//   1. amax_init  : global_scale word <- 0x80000000 (a tagged amax of 0)
+//   2. amax       : integer atomic max of (0x80000000 | |w|max as fp32 bits),
+//                   one per workgroup
+//   3. quant_pack : every workgroup reads the word: tagged -> the amax, from
+//                   which it derives gs = max(amax/2688, 1e-12); untagged ->
+//                   gs itself.  Workgroup 0 stores the untagged gs.  Both
+//                   forms give the same gs, so the order of that store
+//                   against the other workgroups' reads does not matter.
+//
+// Memory access: HBM streams fastest when each workgroup walks a contiguous
+// span with every wavefront instruction covering 1 KiB (measured ~7 TB/s on
+// MI355X, against ~6 TB/s for grid-stride loops), so both streaming kernels
+// split the weight into one contiguous span per workgroup.  quant_pack walks
+// the spans in the reverse order of amax, so its first reads find the tail
+// of the weight that amax read last.
 //
 // The weight, packed codes and scales are viewed as flat arrays: with
-// K % 16 == 0 each 16-block lies inside one row and block b covers weights
-// [16b, 16b+16), packed bytes [8b, 8b+8) and scale byte b.
+// K % 16 == 0 each 16-block lies inside one row; 16-byte vector v holds
+// weights [8v, 8v+8), i.e. half of block v/2, whose codes are packed
+// 32-bit word v and whose scale is byte v/2.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -23,38 +35,34 @@
 namespace nvfp4 {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;                  // 16-byte vectors in flight per thread
+constexpr uint32_t kTag = 0x80000000u;      // marks the word as holding an amax
 
-__global__ void amax_init_kernel(uint32_t* __restrict__ amax_bits) {
-  if (threadIdx.x == 0) *amax_bits = 0u;
+__global__ void amax_init_kernel(uint32_t* __restrict__ word) {
+  if (threadIdx.x == 0) *word = kTag;
 }
 
-// Tensor-wide max |w|: bf16 magnitudes compared as unsigned 16-bit integers
-// (order-preserving for finite values), 4 x 16-byte loads in flight per
-// thread, then a wavefront butterfly and one atomic per workgroup.  The word
-// receives the magnitude as fp32 bits, which order like unsigned integers.
-__global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ w, int64_t n16,
-                                                        uint32_t* __restrict__ amax_bits) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+// Tensor-wide max |w| over workgroup span [b0, b1) of 16-byte vectors:
+// bf16 magnitudes compared as unsigned 16-bit integers (order-preserving for
+// finite values), a wavefront butterfly, then one atomic per workgroup.
+__global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ w, int64_t n16, int64_t per_wg,
+                                                        uint32_t* __restrict__ word) {
+  const int64_t b0 = (int64_t)blockIdx.x * per_wg;
+  const int64_t b1 = min(n16, b0 + per_wg);
   uint32_t m0 = 0, m1 = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = load_stream16(w + i);
-    const u32x4 b = load_stream16(w + i + stride);
-    const u32x4 c = load_stream16(w + i + 2 * stride);
-    const u32x4 d = load_stream16(w + i + 3 * stride);
-    m0 = pk_max_u16(m0, a.x & 0x7FFF7FFFu); m1 = pk_max_u16(m1, a.y & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, a.z & 0x7FFF7FFFu); m1 = pk_max_u16(m1, a.w & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, b.x & 0x7FFF7FFFu); m1 = pk_max_u16(m1, b.y & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, b.z & 0x7FFF7FFFu); m1 = pk_max_u16(m1, b.w & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, c.x & 0x7FFF7FFFu); m1 = pk_max_u16(m1, c.y & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, c.z & 0x7FFF7FFFu); m1 = pk_max_u16(m1, c.w & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, d.x & 0x7FFF7FFFu); m1 = pk_max_u16(m1, d.y & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, d.z & 0x7FFF7FFFu); m1 = pk_max_u16(m1, d.w & 0x7FFF7FFFu);
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 a = load_stream16(w + i);
-    m0 = pk_max_u16(m0, a.x & 0x7FFF7FFFu); m1 = pk_max_u16(m1, a.y & 0x7FFF7FFFu);
-    m0 = pk_max_u16(m0, a.z & 0x7FFF7FFFu); m1 = pk_max_u16(m1, a.w & 0x7FFF7FFFu);
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += kThreads * kUnroll) {
+    u32x4 v[kUnroll];
+    // clamped, unconditional loads (a branch around a load makes the compiler
+    // wait for it); a repeated vector cannot change the max
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_stream16(w + min(i + kThreads * u, b1 - 1));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      m0 = pk_max_u16(m0, v[u].x & 0x7FFF7FFFu);
+      m1 = pk_max_u16(m1, v[u].y & 0x7FFF7FFFu);
+      m0 = pk_max_u16(m0, v[u].z & 0x7FFF7FFFu);
+      m1 = pk_max_u16(m1, v[u].w & 0x7FFF7FFFu);
+    }
   }
   m0 = pk_max_u16(m0, m1);
   uint32_t r = max(m0 & 0xFFFFu, m0 >> 16);
@@ -68,96 +76,115 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict_
     uint32_t v = part[0];
 #pragma unroll
     for (int j = 1; j < kThreads / 64; ++j) v = max(v, part[j]);
-    atomicMax(amax_bits, v << 16);
+    atomicMax(word, kTag | (v << 16));
   }
 }
 
-// gs = max(fl32(amax / 2688), fl32(1e-12)); IEEE division (no fast-math).
-__global__ void global_scale_kernel(float* __restrict__ gs_word) {
-  if (threadIdx.x == 0) {
-    const float a = __uint_as_float(*reinterpret_cast<const uint32_t*>(gs_word));
-    const float gs = a / (kE2m1Max * kE4m3Max);
-    *gs_word = fmaxf(gs, 1e-12f);
-  }
+// fl32(b / 6) for b >= 0 from a multiply and two fused multiply-adds:
+// q0 = fl(b * fl(1/6)); the residual b - 6 q0 is exact in fp32, and one
+// correction step gives the correctly rounded quotient for every finite
+// bf16 b (checked exhaustively against exact rational arithmetic on the host).
+__device__ __forceinline__ float div6(float b) {
+  const float inv6 = 0.16666667163372039795f;    // fl32(1/6)
+  const float q0 = b * inv6;
+  const float r = __builtin_fmaf(-q0, 6.0f, b);
+  return __builtin_fmaf(r, inv6, q0);
 }
 
-// Encode one 16-weight block held in eight 32-bit words (weight i in the low
-// half of d[i/2] when i is even).  Writes 8 packed bytes and the scale byte.
-__device__ __forceinline__ void encode_block(const uint32_t d[8], float inv, uint2* out_codes,
-                                             uint32_t* out_scale) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = pk_max_u16(m, d[i] & 0x7FFF7FFFu);
-  const float bmax = __uint_as_float(max(m & 0xFFFFu, m >> 16) << 16);
-  const float t = bmax / kE2m1Max;       // fl32(b / 6)
-  const float u = fminf(t * inv, kE4m3Max);
+// Encode the 8 weights of one 16-byte vector (half a block).  The other half
+// of the block is in the neighbouring lane (lane ^ 1), which supplies its
+// half-block max through a DPP quad swap.  Returns the packed codes; *sbyte
+// receives the block's E4M3 scale byte.
+__device__ __forceinline__ uint32_t encode_half_block(const u32x4 v, float inv, const float* __restrict__ rlut,
+                                                      uint32_t* sbyte) {
+  const uint32_t m = pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
+                                pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu));
+  uint32_t mh = max(m & 0xFFFFu, m >> 16);
+  mh = max(mh, (uint32_t)__builtin_amdgcn_mov_dpp((int)mh, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+  const float bmax = __uint_as_float(mh << 16);
+  const float t = div6(bmax);                      // fl32(b / 6)
+  const float u = fminf(t * inv, kE4m3Max);        // fl32(t * inv), clamped to 448
   float s;
-  const uint32_t sbyte = e4m3_encode_rne(u, &s);
-  const float r = (s > 0.0f) ? inv / s : 0.0f;   // fl32(inv / s); zero block -> codes 0
-  float q[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    q[2 * i] = bf16_lo(d[i]) * r;       // fl32(w * r)
-    q[2 * i + 1] = bf16_hi(d[i]) * r;
-  }
-  uint32_t lo = 0u, hi = 0u;
-  lo = NVFP4_CVT_PK_FP4(lo, q[0], q[1], 0);
-  lo = NVFP4_CVT_PK_FP4(lo, q[2], q[3], 1);
-  lo = NVFP4_CVT_PK_FP4(lo, q[4], q[5], 2);
-  lo = NVFP4_CVT_PK_FP4(lo, q[6], q[7], 3);
-  hi = NVFP4_CVT_PK_FP4(hi, q[8], q[9], 0);
-  hi = NVFP4_CVT_PK_FP4(hi, q[10], q[11], 1);
-  hi = NVFP4_CVT_PK_FP4(hi, q[12], q[13], 2);
-  hi = NVFP4_CVT_PK_FP4(hi, q[14], q[15], 3);
-  *out_codes = make_uint2(fix_zero_signs(lo), fix_zero_signs(hi));
-  *out_scale = sbyte;
+  const uint32_t sb = e4m3_encode_rne(u, &s);
+  const float r = rlut[sb];                        // fl32(inv / s), 0 when s == 0
+  const float q0 = bf16_lo(v.x) * r, q1 = bf16_hi(v.x) * r;
+  const float q2 = bf16_lo(v.y) * r, q3 = bf16_hi(v.y) * r;
+  const float q4 = bf16_lo(v.z) * r, q5 = bf16_hi(v.z) * r;
+  const float q6 = bf16_lo(v.w) * r, q7 = bf16_hi(v.w) * r;
+  uint32_t c = 0u;
+  c = NVFP4_CVT_PK_FP4(c, q0, q1, 0);
+  c = NVFP4_CVT_PK_FP4(c, q2, q3, 1);
+  c = NVFP4_CVT_PK_FP4(c, q4, q5, 2);
+  c = NVFP4_CVT_PK_FP4(c, q6, q7, 3);
+  *sbyte = sb;
+  return fix_zero_signs(c);
 }
 
-// One thread per 16-weight block: two 16-byte loads, one 8-byte store of codes
-// and one scale byte.  Consecutive threads own consecutive blocks, so a
-// wavefront reads 2 KiB and writes 512 + 64 contiguous bytes.
-__global__ __launch_bounds__(kThreads) void quant_pack_kernel(const u32x4* __restrict__ w, int64_t nblocks,
-                                                              const float* __restrict__ gs_ptr,
-                                                              uint2* __restrict__ packed,
+__global__ __launch_bounds__(kThreads) void quant_pack_kernel(const u32x4* __restrict__ w, int64_t n16,
+                                                              int64_t per_wg, float* __restrict__ gs_word,
+                                                              uint32_t* __restrict__ packed,
                                                               uint8_t* __restrict__ scales) {
-  const float inv = 1.0f / *gs_ptr;     // fl32(1 / gs), IEEE division
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-    const u32x4 lo = load_stream16(w + 2 * b);
-    const u32x4 hi = load_stream16(w + 2 * b + 1);
-    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint2 codes;
-    uint32_t sb;
-    encode_block(d, inv, &codes, &sb);
-    packed[b] = codes;
-    scales[b] = (uint8_t)sb;
+  __shared__ float rlut[128];
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(gs_word);
+  float gs;
+  if (word & kTag) {
+    const float a = __uint_as_float(word & ~kTag);
+    gs = fmaxf(a / (kE2m1Max * kE4m3Max), 1e-12f);   // IEEE division
+  } else {
+    gs = __uint_as_float(word);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_word = gs;
+  const float inv = 1.0f / gs;                        // fl32(1 / gs)
+  if (threadIdx.x < 128) {
+    // r for E4M3 byte threadIdx.x (0..126 are the finite non-negative scales)
+    const float s = NVFP4_E4M3_TO_F32(threadIdx.x, 0);
+    rlut[threadIdx.x] = (threadIdx.x != 0x7F && s > 0.0f) ? inv / s : 0.0f;
+  }
+  __syncthreads();
+
+  const int64_t span = (int64_t)(gridDim.x - 1 - blockIdx.x);
+  const int64_t b0 = span * per_wg;
+  const int64_t b1 = min(n16, b0 + per_wg);
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += kThreads * kUnroll) {
+    u32x4 v[kUnroll];
+    // clamped, unconditional loads; vectors past the span end are encoded
+    // (from a repeated vector) but never stored
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_stream16(w + min(i + kThreads * u, b1 - 1));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t vi = i + kThreads * u;
+      uint32_t sb;
+      const uint32_t codes = encode_half_block(v[u], inv, rlut, &sb);
+      if (vi < b1) {
+        packed[vi] = codes;
+        if ((vi & 1) == 0) scales[vi >> 1] = (uint8_t)sb;
+      }
+    }
   }
 }
 
-static int grid_for(int64_t work_items, int per_thread, int max_blocks) {
-  const int64_t threads = (work_items + per_thread - 1) / per_thread;
-  int64_t blocks = (threads + kThreads - 1) / kThreads;
-  if (blocks < 1) blocks = 1;
-  if (blocks > max_blocks) blocks = max_blocks;
-  return (int)blocks;
-}
+static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 hipError_t launch_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed, uint8_t* scales,
                            float* global_scale, hipStream_t stream) {
-  const int64_t n16 = N * K / 8;        // 16-byte words of the weight
-  const int64_t nblocks = N * K / kGroup;
-  uint32_t* bits = reinterpret_cast<uint32_t*>(global_scale);
+  const int64_t n16 = N * K / 8;                 // 16-byte vectors of the weight (even: K % 16 == 0)
+  uint32_t* word = reinterpret_cast<uint32_t*>(global_scale);
+  // One contiguous span per workgroup; spans are a multiple of 512 vectors, so
+  // a block never straddles two workgroups and lane parity equals vector
+  // parity in every iteration (the two halves of a block sit in lanes 2j, 2j+1).
+  const int64_t target_wgs = 4096;
+  const int64_t per_wg = std::max<int64_t>(512, round_up((n16 + target_wgs - 1) / target_wgs, 512));
+  const int grid = (int)((n16 + per_wg - 1) / per_wg);
   hipError_t e;
-  e = launch_kernel((const void*)amax_init_kernel, dim3(1), dim3(64), stream, bits);
+  e = launch_kernel((const void*)amax_init_kernel, dim3(1), dim3(64), stream, word);
   if (e != hipSuccess) return e;
-  e = launch_kernel((const void*)amax_kernel, dim3(grid_for(n16, 4, 256 * 32)), dim3(kThreads), stream,
-                    reinterpret_cast<const u32x4*>(W), n16, bits);
+  e = launch_kernel((const void*)amax_kernel, dim3(grid), dim3(kThreads), stream,
+                    reinterpret_cast<const u32x4*>(W), n16, per_wg, word);
   if (e != hipSuccess) return e;
-  e = launch_kernel((const void*)global_scale_kernel, dim3(1), dim3(64), stream, global_scale);
-  if (e != hipSuccess) return e;
-  e = launch_kernel((const void*)quant_pack_kernel, dim3(grid_for(nblocks, 1, 256 * 64)), dim3(kThreads),
-                    stream, reinterpret_cast<const u32x4*>(W), nblocks, (const float*)global_scale,
-                    reinterpret_cast<uint2*>(packed), scales);
+  e = launch_kernel((const void*)quant_pack_kernel, dim3(grid), dim3(kThreads), stream,
+                    reinterpret_cast<const u32x4*>(W), n16, per_wg, global_scale,
+                    reinterpret_cast<uint32_t*>(packed), scales);
   return e;
 }
 
