@@ -1,10 +1,12 @@
-"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+"""GPU parity at the full workload sizes, through the same entry points and
+launch configurations bench.py times.
 
 Quantization: every byte of packed codes and scales and the global scale's bits
 against the oracle (quantized on a thread pool, same arithmetic).
-GEMM: every logit of each decode M against the fp64 oracle; for prefill sizes
-(M = 4096, 8192), a sample of activation rows against all N and all rows
-against a sample of vocabulary columns.  Each test prints its case first.
+GEMM: every logit of each decode M against the fp64 oracle; for the prefill
+sizes (M = 4096, 8192), a sample of activation rows against all N and all rows
+against a sample of vocabulary columns.  One test per workload, so each
+weight is generated and quantized once; each step prints its case first.
 """
 
 import numpy as np
@@ -20,86 +22,67 @@ from gpu_util import (DEV, assert_quant_equal, check_gemm, dev_bf16, host_bits,
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 
-_cache = {}
+
+def say(msg):
+    print(msg, flush=True)
 
 
-def prepared(name):
-    """Weight, activations, GPU quantization and oracle quantization of a workload."""
-    if name in _cache:
-        return _cache[name]
-    _cache.clear()
-    torch.cuda.empty_cache()
-    w = wl.WORKLOADS[name]
-    print(f"\n[{name}] generating {w.n}x{w.k}", flush=True)
-    wb = wl.weight_bits(w)
-    xb = wl.activation_bits(w)
+def quantize_both(w, wb):
     wd = dev_bf16(wb)
     p, s, g = B.nvfp4_quantize(wd)
     torch.cuda.synchronize()
     gs = O.global_scale(O.weight_amax(wb))
     op, os_ = oracle_quantize_threaded(wb, gs)
-    _cache[name] = dict(w=w, wb=wb, xb=xb, wd=wd, q=(p, s, g), oracle=(op, os_, gs))
-    return _cache[name]
-
-
-@pytest.mark.parametrize("name", ["llama3_8b", "llama3_70b", "qwen_prefill", "heavy_tail"])
-def test_quantize_full(name):
-    d = prepared(name)
-    print(f"[{name}] quantize parity", flush=True)
-    p, s, g = d["q"]
     got = (p.cpu().numpy(), s.view(torch.uint8).cpu().numpy(), np.float32(g.item()))
-    assert_quant_equal(d["wb"], got, d["oracle"], name)
-    if name == "heavy_tail":
-        # zero row -> zero codes and scales; grid row keeps the generator's codes
-        assert not got[0][0].any() and not got[1][0].any()
-        g_row = wl.bf16_bits_to_f32(wl.grid_row_bits(d["w"].k)).astype(np.float64)
-        mag = O.e2m1_magnitude_code(np.abs(g_row).astype(np.float32))
-        want = np.where((g_row < 0) & (mag != 0), mag | 8, mag).astype(np.uint8)
-        assert np.array_equal(O.unpack_codes(got[0][-1:])[0], want)
+    assert_quant_equal(wb, got, (op, os_, gs), w.name)
+    return wd, (p, s, g), (op, os_, gs), got
 
 
-DECODE = [("llama3_8b", m) for m in (1, 8, 32, 64)] + [("llama3_70b", m) for m in (1, 16, 64)] + \
-         [("heavy_tail", 1)]
+def decode_checks(w, xb, q, oq, ms):
+    for m in ms:
+        say(f"[{w.name}] decode GEMM M={m}")
+        x = xb[:m]
+        y = host_bits(B.nvfp4_w4a16_gemm(dev_bf16(x), *q))
+        check_gemm(y, x, *oq, label=f"{w.name} M={m}", argmax_min=0.999)
 
 
-@pytest.mark.parametrize("name,m", DECODE)
-def test_decode_gemm_full(name, m):
-    d = prepared(name)
-    print(f"[{name}] decode GEMM M={m}", flush=True)
-    x = d["xb"][:m]
-    y = host_bits(B.nvfp4_w4a16_gemm(dev_bf16(x), *d["q"]))
-    op, os_, gs = d["oracle"]
-    check_gemm(y, x, op, os_, gs, label=f"{name} M={m}", argmax_min=0.999)
-
-
-@pytest.mark.parametrize("name", ["qwen_prefill", "heavy_tail"])
-def test_prefill_gemm_sampled(name):
-    d = prepared(name)
-    w = d["w"]
-    m = w.ms[0]
-    print(f"[{name}] prefill GEMM M={m}", flush=True)
-    y_dev = B.nvfp4_w4a16_gemm(dev_bf16(d["xb"]), *d["q"])
+def prefill_checks(w, xb, q, oq, m):
+    say(f"[{w.name}] prefill GEMM M={m}")
+    y_dev = B.nvfp4_w4a16_gemm(dev_bf16(xb[:m]), *q)
     torch.cuda.synchronize()
-    op, os_, gs = d["oracle"]
+    op, os_, gs = oq
     rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 254, replace=False)]))
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 126, replace=False)]))
     y_rows = host_bits(y_dev[torch.from_numpy(rows).to(DEV)])
-    check_gemm(y_rows, d["xb"][rows], op, os_, gs, label=f"{name} rows", argmax_min=0.999)
+    check_gemm(y_rows, xb[rows], op, os_, gs, label=f"{w.name} rows", argmax_min=0.999)
     cols = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, 254, replace=False)]))
     y_cols = host_bits(y_dev[:, torch.from_numpy(cols).to(DEV)])
-    check_gemm(y_cols, d["xb"], op[cols], os_[cols], gs, label=f"{name} cols", argmax_min=0.0)
+    check_gemm(y_cols, xb[:m], op[cols], os_[cols], gs, label=f"{w.name} cols", argmax_min=0.0)
     del y_dev
 
 
-def test_refresh_70b_with_graph():
-    """70B shape: W' = W + N(0, 1e-3); in-place refresh; a GEMM graph captured
-    before the refresh computes the new logits on replay."""
-    d = prepared("llama3_70b")
-    w = d["w"]
-    print("[llama3_70b] refresh in place", flush=True)
-    p, s, g = d["q"]
+def test_llama3_8b():
+    w = wl.WORKLOADS["llama3_8b"]
+    say(f"[{w.name}] generating {w.n}x{w.k}")
+    wb, xb = wl.weight_bits(w), wl.activation_bits(w)
+    say(f"[{w.name}] quantize parity")
+    _, q, oq, _ = quantize_both(w, wb)
+    decode_checks(w, xb, q, oq, w.ms)
+
+
+def test_llama3_70b_with_refresh_and_graph():
+    """70B shape: decode parity, then W' = W + N(0, 1e-3), an in-place refresh,
+    and a GEMM graph captured before the refresh that computes the new logits."""
+    w = wl.WORKLOADS["llama3_70b"]
+    say(f"[{w.name}] generating {w.n}x{w.k}")
+    wb, xb = wl.weight_bits(w), wl.activation_bits(w)
+    say(f"[{w.name}] quantize parity")
+    wd, q, oq, _ = quantize_both(w, wb)
+    decode_checks(w, xb, q, oq, w.ms)
+    say(f"[{w.name}] refresh in place + graph replay")
+    p, s, g = q
     ptrs = (p.data_ptr(), s.data_ptr(), g.data_ptr())
-    x = d["xb"][:1]
+    x = xb[:1]
     xd = dev_bf16(x)
     out = torch.empty((1, w.n), dtype=torch.bfloat16, device=DEV)
     side = torch.cuda.Stream()
@@ -110,9 +93,9 @@ def test_refresh_70b_with_graph():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         B.nvfp4_w4a16_gemm(xd, p, s, g, out=out)
-    w2 = wl.refresh_weight_bits(w, d["wb"])
-    d["wd"].copy_(dev_bf16(w2))
-    B.nvfp4_refresh_inplace(d["wd"], p, s, g)
+    w2 = wl.refresh_weight_bits(w, wb)
+    wd.copy_(dev_bf16(w2))
+    B.nvfp4_refresh_inplace(wd, p, s, g)
     graph.replay()
     torch.cuda.synchronize()
     assert (p.data_ptr(), s.data_ptr(), g.data_ptr()) == ptrs
@@ -121,4 +104,28 @@ def test_refresh_70b_with_graph():
     got = (p.cpu().numpy(), s.view(torch.uint8).cpu().numpy(), np.float32(g.item()))
     assert_quant_equal(w2, got, (op2, os2, gs2), "70b refresh")
     check_gemm(host_bits(out), x, op2, os2, gs2, label="70b graph after refresh")
-    _cache.clear()
+
+
+def test_qwen_prefill():
+    w = wl.WORKLOADS["qwen_prefill"]
+    say(f"[{w.name}] generating {w.n}x{w.k}")
+    wb, xb = wl.weight_bits(w), wl.activation_bits(w)
+    say(f"[{w.name}] quantize parity")
+    _, q, oq, _ = quantize_both(w, wb)
+    prefill_checks(w, xb, q, oq, 4096)
+
+
+def test_heavy_tail():
+    w = wl.WORKLOADS["heavy_tail"]
+    say(f"[{w.name}] generating {w.n}x{w.k}")
+    wb, xb = wl.weight_bits(w), wl.activation_bits(w)
+    say(f"[{w.name}] quantize parity")
+    _, q, oq, got = quantize_both(w, wb)
+    # zero row -> zero codes and scales; grid row keeps the generator's codes
+    assert not got[0][0].any() and not got[1][0].any()
+    g_row = wl.bf16_bits_to_f32(wl.grid_row_bits(w.k)).astype(np.float64)
+    mag = O.e2m1_magnitude_code(np.abs(g_row).astype(np.float32))
+    want = np.where((g_row < 0) & (mag != 0), mag | 8, mag).astype(np.uint8)
+    assert np.array_equal(O.unpack_codes(got[0][-1:])[0], want)
+    decode_checks(w, xb, q, oq, (1,))
+    prefill_checks(w, xb, q, oq, 8192)
