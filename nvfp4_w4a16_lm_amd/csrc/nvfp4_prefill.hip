@@ -30,8 +30,8 @@ __device__ __forceinline__ void store_out(uint16_t* __restrict__ y, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// gemm_prefill_small_kernel: M > 64 with K % 64 != 0 (ragged K; not a shape
-// this path is tuned for).  128 (n) x 128 (m) output tile per 256-thread workgroup,
+// gemm_prefill_small_kernel: M > 64 with K % 128 != 0 (not a shape this path
+// is tuned for).  128 (n) x 128 (m) output tile per 256-thread workgroup,
 // 64-k steps.  Each step stages the packed weight tile (4 KiB + scales) and
 // the bf16 activation tile in registers, dequantizes the weights to bf16 into
 // LDS, and the four wavefronts (2 x 2, 64 x 64 each) run 4 x 4 MFMA tiles.
@@ -132,15 +132,35 @@ __global__ __launch_bounds__(256) void gemm_prefill_small_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
-// gemm_prefill_kernel: M > 64, K % 64 == 0.  256 (n) x 256 (m) output tile
-// per 256-thread workgroup, 64-k steps, v_mfma_f32_32x32x16_bf16.
+// gemm_prefill_kernel: M > 64, K % 128 == 0.  256 (n) x 256 (m) output tile
+// per 256-thread workgroup (one wavefront per SIMD), 64-k tiles,
+// v_mfma_f32_32x32x16_bf16.
 //
 // Each wavefront owns a 128 x 128 quarter of the tile: 4 x 4 MFMA tiles of
-// 32 x 32, 256 fp32 accumulators per lane.  Per 64-k step the workgroup
-// stages the next step's tiles in LDS (double buffered) around this step's
-// 64 MFMAs per wavefront: thread t dequantizes weight row n0 + t (64 codes
-// -> 64 exact bf16) and copies 8 pieces of the activation tile (each 16 B,
-// 8 threads per 128-byte row); the global loads are issued one step ahead.
+// 32 x 32, 256 fp32 accumulators per lane.  Both operand tiles are staged in
+// LDS as bf16, double buffered.
+//
+// Weight loads: a 64-k tile needs only 32 code bytes of each of 256 rows, so
+// rows are read in 128-k superblocks, 4 lanes per row (64 contiguous bytes),
+// two superblocks ahead.  Load i of a thread covers row n0 + (t >> 2) + 64 i;
+// lane t & 3 takes the 16-byte piece (t & 3) ^ 2 (i & 1), so for either
+// 64-k half of a superblock every thread holds exactly two pieces (loads
+// {0, 2} or {1, 3}), each 32 codes of one row and their 2 scale bytes, and
+// dequantizes them into the weight tile.  Activation loads: 8 threads per
+// 128-byte row, one tile ahead.
+//
+// Software pipeline, per 64-k tile kt (LDS buffer b = kt & 1):
+//   * 4 sub-steps of 16 k, 16 MFMAs each; the fragments of the next sub-step
+//     are read from LDS while the current one's MFMAs run;
+//   * between the MFMAs of sub-steps 0..2, tile kt + 1 (in registers) is
+//     dequantized and written to buffer b ^ 1 piece by piece, and each
+//     activation piece's registers are refilled with tile kt + 2;
+//   * one barrier, after sub-step 2's MFMAs: every wavefront has finished
+//     reading buffer b (its last fragments are in registers) and writing
+//     buffer b ^ 1, so sub-step 3 runs on registers while the fragments of
+//     tile kt + 1 are read.
+// Loads past the last tile re-read in-bounds data and rows past M or N repeat
+// the last row (no branches around loads); those results are never stored.
 //
 // 32x32x16 operand layout: lane l supplies row/column l % 32 and 8
 // consecutive k of k-group l / 32; accumulator v of lane l holds
@@ -152,13 +172,28 @@ __global__ __launch_bounds__(256) void gemm_prefill_small_kernel(const uint16_t*
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPT = 256;             // tile rows (n) and columns (m)
-constexpr int kPK = 64;              // k per step
+constexpr int kPK = 64;              // k per tile
 constexpr int kPP = kPK + 8;         // bf16 per LDS row of an operand tile
 constexpr int kOP = kPT + 8;         // bf16 per LDS row of the output tile
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+// weight superblock registers of one thread: 4 code pieces and their scale pairs
+struct WSuper {
+  u32x4 c[4];
+  uint32_t s[4];
+};
+
+// order of one tile's 18 staging items: 0, 1 = select weight piece 0 / 1;
+// 2..9 = dequantize + store 8 weights (piece (id - 2) / 4, chunk (id - 2) % 4);
+// 10..17 = store activation piece id - 10 and reload it
+__device__ constexpr int kItemOrder[18] = {0, 2, 10, 3, 11, 4, 12, 5, 13, 1, 6, 14, 7, 15, 8, 16, 9, 17};
 
 __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                               const uint8_t* __restrict__ packed,
@@ -174,43 +209,54 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
   const int n0 = nt * kPT, m0 = mt * kPT;
   const int nk = K / kPK;
 
-  // weight loader: thread t -> row n0 + t: 32 packed bytes + 4 scale bytes per step
-  const int64_t wrow = min(n0 + tid, N - 1);
-  const uint8_t* wp = packed + wrow * (K >> 1);
-  const uint8_t* wsp = scales + wrow * (K >> 4);
-  // activation loader: thread t -> rows (t >> 3) + 32 i, 16-byte piece t & 7
+  // weight loader (see above)
+  const int wg = tid >> 2, wj = tid & 3, wa = wj >> 1, wh = wj & 1;
+  const uint8_t* wpp[4];
+  const uint8_t* wsp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = min(n0 + wg + 64 * i, N - 1);
+    wpp[i] = packed + row * (K >> 1);
+    wsp[i] = scales + row * (K >> 4);
+  }
+  const int kpiece0 = 32 * wj, kpiece1 = 32 * (wj ^ 2);   // k offset in a superblock, loads i even / odd
+  auto wsuper_load = [&](int sb, WSuper& w) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ko = min(sb * 2 * kPK + ((i & 1) ? kpiece1 : kpiece0), K - 32);
+      w.c[i] = load_stream16(wpp[i] + (ko >> 1));
+      w.s[i] = *reinterpret_cast<const uint16_t*>(wsp[i] + (ko >> 4));
+    }
+  };
+  // for half q of a superblock this thread's pieces are loads q ^ wa and (q ^ wa) + 2
+  const bool wodd[2] = {wa != 0, wa != 1};
+  const int wrow[2][2] = {{wg + 64 * (0 ^ wa), wg + 64 * ((0 ^ wa) + 2)},
+                          {wg + 64 * (1 ^ wa), wg + 64 * ((1 ^ wa) + 2)}};
+  // activation loader: thread t -> rows (t >> 3) + 32 p, 16-byte piece t & 7
   const int xc = tid & 7, xr = tid >> 3;
-
-  struct Stage {
-    u32x4 w0, w1;
-    uint32_t ws;
-    u32x4 xv[8];
-  };
-  auto gload = [&](int kt, Stage& st) __attribute__((always_inline)) {
-    const int k0 = kt * kPK;
-    st.w0 = load_stream16(wp + k0 / 2);
-    st.w1 = load_stream16(wp + k0 / 2 + 16);
-    st.ws = *reinterpret_cast<const uint32_t*>(wsp + k0 / 16);
+  const uint16_t* xp = x + (int64_t)min(m0 + xr, M - 1) * K + 8 * xc;
+  int64_t xoff[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + xr + 32 * i;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(x + (int64_t)min(m, M - 1) * K + k0 + 8 * xc);
-      st.xv[i] = m < M ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  // dequantize the weight row into 8 pieces of 8 bf16 and store them and the
-  // 8 activation pieces into LDS buffer buf
-  auto lstore = [&](const Stage& st, int buf) __attribute__((always_inline)) {
-    const float sc[4] = {NVFP4_E4M3_TO_F32(st.ws, 0), NVFP4_E4M3_TO_F32(st.ws, 1), NVFP4_E4M3_TO_F32(st.ws, 2),
-                         NVFP4_E4M3_TO_F32(st.ws, 3)};
-    const uint32_t dw[8] = {st.w0.x, st.w0.y, st.w0.z, st.w0.w, st.w1.x, st.w1.y, st.w1.z, st.w1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      *reinterpret_cast<bf16x8*>(&lds[buf][0][tid][8 * j]) = dequant8(dw[j], sc[j >> 1]);
-      *reinterpret_cast<u32x4*>(&lds[buf][1][xr + 32 * j][8 * xc]) = st.xv[j];
-    }
+  for (int p = 0; p < 8; ++p) xoff[p] = ((int64_t)min(m0 + xr + 32 * p, M - 1) - min(m0 + xr, M - 1)) * K;
+  auto xload = [&](int kt, int p) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(xp + xoff[p] + kt * kPK);
   };
 
+  // Per-lane LDS element offsets (within one buffer).  They pass through an
+  // empty asm at the start of every tile so the compiler rebuilds the
+  // addresses there as base + immediate instead of keeping dozens of
+  // loop-invariant addresses live in registers.
+  constexpr int kOpElems = kPT * kPP, kBufElems = 2 * kOpElems;
+  int fa_off = (128 * wn + (lane & 31)) * kPP + 8 * (lane >> 5);
+  int fb_off = kOpElems + (128 * wm + (lane & 31)) * kPP + 8 * (lane >> 5);
+  int ws_off[2][2] = {{wrow[0][0] * kPP + 32 * wh, wrow[0][1] * kPP + 32 * wh},
+                      {wrow[1][0] * kPP + 32 * wh, wrow[1][1] * kPP + 32 * wh}};
+  int xs_off = kOpElems + xr * kPP + 8 * xc;
+  uint16_t* const lbase = &lds[0][0][0][0];
+  auto launder = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(fa_off), "+v"(fb_off), "+v"(xs_off));
+    asm volatile("" : "+v"(ws_off[0][0]), "+v"(ws_off[0][1]), "+v"(ws_off[1][0]), "+v"(ws_off[1][1]));
+  };
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -219,39 +265,86 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // The 64 MFMAs of one step, 16 per 16-k sub-step.
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    const int row = lane & 31, kg = 8 * (lane >> 5);
+  WSuper wcur, wnext;
+  u32x4 xv[8];
+  u32x4 pc[2];          // selected code pieces
+  float psc[2][2];      // their two block scales
+  // staging item `id` of the tile in superblock half q, into LDS buffer nb;
+  // activation pieces are reloaded from tile kn
+  auto stage_item = [&](int id, int q, const WSuper& w, int nb, int kn) __attribute__((always_inline)) {
+    if (id < 2) {
+      const int pi = id;
+      const bool o = wodd[q];
 #pragma unroll
-    for (int k16 = 0; k16 < kPK / 16; ++k16) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&lds[buf][0][128 * wn + 32 * i + row][16 * k16 + kg]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&lds[buf][1][128 * wm + 32 * j + row][16 * k16 + kg]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      for (int e = 0; e < 4; ++e) pc[pi][e] = o ? w.c[2 * pi + 1][e] : w.c[2 * pi][e];
+      const uint32_t sp = o ? w.s[2 * pi + 1] : w.s[2 * pi];
+      psc[pi][0] = NVFP4_E4M3_TO_F32(sp, 0);
+      psc[pi][1] = NVFP4_E4M3_TO_F32(sp, 1);
+    } else if (id < 10) {
+      const int pi = (id - 2) >> 2, c = (id - 2) & 3;
+      *reinterpret_cast<bf16x8*>(lbase + nb * kBufElems + ws_off[q][pi] + 8 * c) = dequant8(pc[pi][c], psc[pi][c >> 1]);
+    } else {
+      const int p = id - 10;
+      *reinterpret_cast<u32x4*>(lbase + nb * kBufElems + xs_off + 32 * p * kPP) = xv[p];
+      xv[p] = xload(kn, p);
     }
   };
-
-  // One step ahead: the next step's global loads are issued before this
-  // step's MFMAs and land in LDS (the other buffer) after them.
-  Stage st;
-  gload(0, st);
-  lstore(st, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1, st);
-    compute(buf);
-    if (more) lstore(st, buf ^ 1);
+  // One 16-k sub-step: 16 MFMAs on fc.  After MFMA i: fragment i of the next
+  // sub-step (rb, rk16), then staging items [it0 + i*n/16, it0 + (i+1)*n/16)
+  // of the tile being staged.  The compiler may not reorder across the slots.
+  auto substep = [&](const Frags& fc, Frags& fn, int rb, int rk16, int it0, int n, int q, const WSuper& w, int nb,
+                     int kn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc[i >> 2][i & 3] = mfma32x32x16(fc.a[i >> 2], fc.b[i & 3], acc[i >> 2][i & 3]);
+      if (i < 4)
+        fn.a[i] = *reinterpret_cast<const bf16x8*>(lbase + rb * kBufElems + fa_off + 32 * i * kPP + 16 * rk16);
+      else if (i < 8)
+        fn.b[i - 4] = *reinterpret_cast<const bf16x8*>(lbase + rb * kBufElems + fb_off + 32 * (i - 4) * kPP + 16 * rk16);
+#pragma unroll
+      for (int it = it0 + i * n / 16; it < it0 + (i + 1) * n / 16; ++it) stage_item(kItemOrder[it], q, w, nb, kn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  Frags fa, fb;
+  // One 64-k tile kt on buffer kt & 1; stages tile kt + 1 (superblock half q
+  // of w) into the other buffer.
+  auto tile = [&](int kt, int q, const WSuper& w) __attribute__((always_inline)) {
+    const int b = kt & 1;
+    const int kn = min(kt + 2, nk - 1);
+    launder();
+    substep(fa, fb, b, 1, 0, 6, q, w, b ^ 1, kn);
+    substep(fb, fa, b, 2, 6, 6, q, w, b ^ 1, kn);
+    substep(fa, fb, b, 3, 12, 6, q, w, b ^ 1, kn);
+    // every wavefront has read buffer b and written buffer b ^ 1
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    substep(fb, fa, b ^ 1, 0, 0, 0, q, w, b, kn);
+  };
+
+  // prologue: tile 0 into buffer 0; tile 1's activations and superblocks 0, 1 in registers
+  wsuper_load(0, wcur);
+  wsuper_load(1, wnext);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) xv[p] = xload(0, p);
+  const int k1 = min(1, nk - 1);
+#pragma unroll
+  for (int it = 0; it < 18; ++it) stage_item(kItemOrder[it], 0, wcur, 0, k1);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa.a[i] = *reinterpret_cast<const bf16x8*>(lbase + fa_off + 32 * i * kPP);
+    fa.b[i] = *reinterpret_cast<const bf16x8*>(lbase + fb_off + 32 * i * kPP);
   }
+
+  for (int kt = 0; kt < nk; kt += 2) {
+    tile(kt, 1, wcur);              // stages tile kt + 1: second half of superblock kt / 2
+    wcur = wnext;
+    wsuper_load(kt / 2 + 2, wnext);
+    tile(kt + 1, 0, wcur);          // stages tile kt + 2: first half of superblock kt / 2 + 1 (nk is even)
+  }
+  __syncthreads();
 
   // epilogue: y[m][n] = bf16(acc * gs + bias[n]) through an LDS tile [m][n]
   const float gs = *gs_ptr;
@@ -300,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 hipError_t launch_gemm_prefill(const void* x, int64_t M, int64_t K, const uint8_t* packed,
                                const uint8_t* scales, const float* global_scale, int64_t N,
                                const void* bias, void* y, hipStream_t stream) {
-  if (K % kPK != 0) {
+  if (K % (2 * kPK) != 0) {
     const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
     return launch_kernel((const void*)gemm_prefill_small_kernel<false>, grid, dim3(256), stream,
                          (const uint16_t*)x, (int)M, (int)K, packed, scales, global_scale, (int)N,
