@@ -140,27 +140,36 @@ __global__ __launch_bounds__(256) void gemm_prefill_small_kernel(const uint16_t*
 // 32 x 32, 256 fp32 accumulators per lane.  Both operand tiles are staged in
 // LDS as bf16, double buffered.
 //
-// Weight loads: a 64-k tile needs only 32 code bytes of each of 256 rows, so
-// rows are read in 128-k superblocks, 4 lanes per row (64 contiguous bytes),
-// two superblocks ahead.  Load i of a thread covers row n0 + (t >> 2) + 64 i;
-// lane t & 3 takes the 16-byte piece (t & 3) ^ 2 (i & 1), so for either
-// 64-k half of a superblock every thread holds exactly two pieces (loads
-// {0, 2} or {1, 3}), each 32 codes of one row and their 2 scale bytes, and
-// dequantizes them into the weight tile.  Activation loads: 8 threads per
-// 128-byte row, one tile ahead.
+// Activation tiles go from global memory straight into LDS (buffer loads with
+// the LDS flag; rows past M read as zero): each wavefront instruction fills
+// 1 KiB = 8 unpadded 128-byte rows, and the 16-byte pieces of row r are
+// stored XOR-swizzled (piece c at slot c ^ (r & 7) ^ ((r >> 3) & 1)) so that
+// the fragment reads of 8 (and of 16) consecutive rows hit distinct banks.
 //
-// Software pipeline, per 64-k tile kt (LDS buffer b = kt & 1):
+// Weight tiles are dequantized by the threads: a 64-k tile needs only 32 code
+// bytes of each of 256 rows, so rows are read in 128-k superblocks, 4 lanes
+// per row (64 contiguous bytes), two superblocks ahead.  Load i of a thread
+// covers row n0 + 2 (t >> 2) + (i & 1) + 128 (i >> 1); lane t & 3 takes the
+// 16-byte piece (t & 3) ^ 2 (i & 1), so for either 64-k half of a superblock
+// every thread holds exactly two pieces (loads {0, 2} or {1, 3}), each 32
+// codes of one row and their 2 scale bytes, and writes them to the (padded)
+// weight tile.  With this row map the 8 lanes of each LDS store group write 4
+// rows with distinct residues mod 4, i.e. distinct banks.
+//
+// Software pipeline, per 64-k tile kt (LDS buffers b = kt & 1):
 //   * 4 sub-steps of 16 k, 16 MFMAs each; the fragments of the next sub-step
 //     are read from LDS while the current one's MFMAs run;
-//   * between the MFMAs of sub-steps 0..2, tile kt + 1 (in registers) is
-//     dequantized and written to buffer b ^ 1 piece by piece, and each
-//     activation piece's registers are refilled with tile kt + 2;
-//   * one barrier, after sub-step 2's MFMAs: every wavefront has finished
-//     reading buffer b (its last fragments are in registers) and writing
-//     buffer b ^ 1, so sub-step 3 runs on registers while the fragments of
-//     tile kt + 1 are read.
-// Loads past the last tile re-read in-bounds data and rows past M or N repeat
-// the last row (no branches around loads); those results are never stored.
+//   * between the MFMAs of sub-steps 0..2 the weights of tile kt + 1 are
+//     dequantized into weight buffer b ^ 1 (activation tile kt + 1 is already
+//     on its way into activation buffer b ^ 1);
+//   * one barrier, after sub-step 2's MFMAs (each wavefront first waits for
+//     its own activation loads of tile kt + 1): buffer b is no longer read
+//     and buffer b ^ 1 is complete, so sub-step 3 runs on registers while the
+//     fragments of tile kt + 1 are read and the activation loads of tile
+//     kt + 2 into buffer b are issued.
+// Loads past the last tile re-read in-bounds data and weight rows past N
+// repeat the last row (no branches around loads); those results are never
+// stored.
 //
 // 32x32x16 operand layout: lane l supplies row/column l % 32 and 8
 // consecutive k of k-group l / 32; accumulator v of lane l holds
@@ -170,11 +179,20 @@ __global__ __launch_bounds__(256) void gemm_prefill_small_kernel(const uint16_t*
 // through LDS and writes whole 16-byte pieces of y rows.
 // ---------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kPT = 256;             // tile rows (n) and columns (m)
 constexpr int kPK = 64;              // k per tile
-constexpr int kPP = kPK + 8;         // bf16 per LDS row of an operand tile
+constexpr int kPP = kPK + 8;         // bf16 per LDS row of a weight tile
 constexpr int kOP = kPT + 8;         // bf16 per LDS row of the output tile
+constexpr int kXBytes = kPT * kPK * 2;            // one activation tile (unpadded)
+constexpr int kWBytes = kPT * kPP * 2;            // one weight tile (padded rows)
+constexpr int kWBase = 2 * kXBytes;               // LDS: activation buffers 0, 1, then weight buffers 0, 1
+constexpr int kLdsBytes = kWBase + 2 * kWBytes;
+static_assert(kPT * kOP * 2 <= kLdsBytes, "output tile must fit in the operand buffers");
+constexpr int kMaxPrefillK = 1 << 21;             // keeps 32-bit buffer offsets in range
+// s_waitcnt immediates (gfx9 encoding): vmcnt(0) / vmcnt(8), other counters not waited for
+constexpr int kWaitVm0 = 0x0F70, kWaitVm8 = 0x0F78;
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -190,10 +208,10 @@ struct WSuper {
   uint32_t s[4];
 };
 
-// order of one tile's 18 staging items: 0, 1 = select weight piece 0 / 1;
-// 2..9 = dequantize + store 8 weights (piece (id - 2) / 4, chunk (id - 2) % 4);
-// 10..17 = store activation piece id - 10 and reload it
-__device__ constexpr int kItemOrder[18] = {0, 2, 10, 3, 11, 4, 12, 5, 13, 1, 6, 14, 7, 15, 8, 16, 9, 17};
+// One tile's 18 weight staging items, in issue order: 0, 1 = select piece 0 / 1;
+// 2..17 = half of an 8-weight chunk: id - 2 = 8 piece + 2 chunk + half, where
+// half 0 converts code pairs 0, 1 and half 1 pairs 2, 3 and stores the chunk.
+__device__ constexpr int kItemOrder[18] = {0, 2, 3, 4, 5, 6, 7, 8, 9, 1, 10, 11, 12, 13, 14, 15, 16, 17};
 
 __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                               const uint8_t* __restrict__ packed,
@@ -201,8 +219,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
                                                               const float* __restrict__ gs_ptr, int N,
                                                               const uint16_t* __restrict__ bias,
                                                               uint16_t* __restrict__ y, int m_tiles) {
-  // [buffer][0 = weight, 1 = activation][row][k]; reused as the output tile at the end
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kPT][kPP];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int mt = blockIdx.x % m_tiles, nt = blockIdx.x / m_tiles;
@@ -215,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
   const uint8_t* wsp[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = min(n0 + wg + 64 * i, N - 1);
+    const int64_t row = min(n0 + 2 * wg + (i & 1) + 128 * (i >> 1), N - 1);
     wpp[i] = packed + row * (K >> 1);
     wsp[i] = scales + row * (K >> 4);
   }
@@ -230,33 +247,48 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
   };
   // for half q of a superblock this thread's pieces are loads q ^ wa and (q ^ wa) + 2
   const bool wodd[2] = {wa != 0, wa != 1};
-  const int wrow[2][2] = {{wg + 64 * (0 ^ wa), wg + 64 * ((0 ^ wa) + 2)},
-                          {wg + 64 * (1 ^ wa), wg + 64 * ((1 ^ wa) + 2)}};
-  // activation loader: thread t -> rows (t >> 3) + 32 p, 16-byte piece t & 7
-  const int xc = tid & 7, xr = tid >> 3;
-  const uint16_t* xp = x + (int64_t)min(m0 + xr, M - 1) * K + 8 * xc;
-  int64_t xoff[8];
+
+  // activation loader: instruction p of wavefront w fills rows 8 (4 p + w) .. + 7;
+  // lane l fills slot l & 7 of row r = 8 (4 p + w) + (l >> 3), i.e. logical
+  // piece (l & 7) ^ (r & 7) ^ ((r >> 3) & 1) = (l & 7) ^ (l >> 3) ^ (w & 1)
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (int64_t)m0 * K), (short)0, min(M - m0, kPT) * K * 2, 0x00020000);
+  uint32_t xdv[8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) xoff[p] = ((int64_t)min(m0 + xr + 32 * p, M - 1) - min(m0 + xr, M - 1)) * K;
-  auto xload = [&](int kt, int p) __attribute__((always_inline)) {
-    return *reinterpret_cast<const u32x4*>(xp + xoff[p] + kt * kPK);
+  for (int p = 0; p < 8; ++p)
+    xdv[p] = (uint32_t)((8 * (4 * p + wave) + (lane >> 3)) * K * 2 + 16 * ((lane & 7) ^ (lane >> 3) ^ (wave & 1)));
+  auto xdma = [&](int kt, int nb, int p) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_ptr_t)(lds + nb * kXBytes + (4 * p + wave) * 1024), 16,
+                                             xdv[p], kt * kPK * 2, 0, 0);
   };
 
-  // Per-lane LDS element offsets (within one buffer).  They pass through an
-  // empty asm at the start of every tile so the compiler rebuilds the
-  // addresses there as base + immediate instead of keeping dozens of
-  // loop-invariant addresses live in registers.
-  constexpr int kOpElems = kPT * kPP, kBufElems = 2 * kOpElems;
-  int fa_off = (128 * wn + (lane & 31)) * kPP + 8 * (lane >> 5);
-  int fb_off = kOpElems + (128 * wm + (lane & 31)) * kPP + 8 * (lane >> 5);
-  int ws_off[2][2] = {{wrow[0][0] * kPP + 32 * wh, wrow[0][1] * kPP + 32 * wh},
-                      {wrow[1][0] * kPP + 32 * wh, wrow[1][1] * kPP + 32 * wh}};
-  int xs_off = kOpElems + xr * kPP + 8 * xc;
-  uint16_t* const lbase = &lds[0][0][0][0];
+  // Per-lane LDS byte offsets.  They pass through an empty asm at the start
+  // of every tile so the compiler rebuilds addresses there as base +
+  // immediate instead of keeping dozens of loop-invariant addresses live.
+  int fw_off = kWBase + ((128 * wn + (lane & 31)) * kPP + 8 * (lane >> 5)) * 2;
+  int fx_off[4];
+#pragma unroll
+  for (int k16 = 0; k16 < 4; ++k16)
+    fx_off[k16] = (128 * wm + (lane & 31)) * 128 + 16 * ((2 * k16 + (lane >> 5)) ^ (lane & 7) ^ ((lane >> 3) & 1));
+  int ws_off[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int pi = 0; pi < 2; ++pi) {
+      const int i = (q ^ wa) + 2 * pi;
+      ws_off[q][pi] = kWBase + ((2 * wg + (i & 1) + 128 * (i >> 1)) * kPP + 32 * wh) * 2;
+    }
   auto launder = [&]() __attribute__((always_inline)) {
-    asm volatile("" : "+v"(fa_off), "+v"(fb_off), "+v"(xs_off));
+    asm volatile("" : "+v"(fw_off), "+v"(fx_off[0]), "+v"(fx_off[1]), "+v"(fx_off[2]), "+v"(fx_off[3]));
     asm volatile("" : "+v"(ws_off[0][0]), "+v"(ws_off[0][1]), "+v"(ws_off[1][0]), "+v"(ws_off[1][1]));
   };
+  auto frag_w = [&](int buf, int i, int k16) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(lds + fw_off + buf * kWBytes + i * 32 * kPP * 2 + k16 * 32);
+  };
+  auto frag_x = [&](int buf, int j, int k16) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(lds + fx_off[k16] + buf * kXBytes + j * 32 * 128);
+  };
+
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -265,13 +297,11 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  WSuper wcur, wnext;
-  u32x4 xv[8];
+  WSuper wA, wB;
   u32x4 pc[2];          // selected code pieces
   float psc[2][2];      // their two block scales
-  // staging item `id` of the tile in superblock half q, into LDS buffer nb;
-  // activation pieces are reloaded from tile kn
-  auto stage_item = [&](int id, int q, const WSuper& w, int nb, int kn) __attribute__((always_inline)) {
+  u32x4 dq;             // chunk being converted
+  auto stage_item = [&](int id, int q, const WSuper& w, int nb) __attribute__((always_inline)) {
     if (id < 2) {
       const int pi = id;
       const bool o = wodd[q];
@@ -280,75 +310,104 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
       const uint32_t sp = o ? w.s[2 * pi + 1] : w.s[2 * pi];
       psc[pi][0] = NVFP4_E4M3_TO_F32(sp, 0);
       psc[pi][1] = NVFP4_E4M3_TO_F32(sp, 1);
-    } else if (id < 10) {
-      const int pi = (id - 2) >> 2, c = (id - 2) & 3;
-      *reinterpret_cast<bf16x8*>(lbase + nb * kBufElems + ws_off[q][pi] + 8 * c) = dequant8(pc[pi][c], psc[pi][c >> 1]);
     } else {
-      const int p = id - 10;
-      *reinterpret_cast<u32x4*>(lbase + nb * kBufElems + xs_off + 32 * p * kPP) = xv[p];
-      xv[p] = xload(kn, p);
+      const int pi = (id - 2) >> 3, c = ((id - 2) >> 1) & 3, half = (id - 2) & 1;
+      const uint32_t d = pc[pi][c];
+      const float sc = psc[pi][c >> 1];
+      if (half == 0) {
+        dq[0] = NVFP4_DEQ_PAIR(d, sc, 0);
+        dq[1] = NVFP4_DEQ_PAIR(d, sc, 1);
+      } else {
+        dq[2] = NVFP4_DEQ_PAIR(d, sc, 2);
+        dq[3] = NVFP4_DEQ_PAIR(d, sc, 3);
+        *reinterpret_cast<u32x4*>(lds + ws_off[q][pi] + nb * kWBytes + 16 * c) = dq;
+      }
     }
   };
   // One 16-k sub-step: 16 MFMAs on fc.  After MFMA i: fragment i of the next
-  // sub-step (rb, rk16), then staging items [it0 + i*n/16, it0 + (i+1)*n/16)
-  // of the tile being staged.  The compiler may not reorder across the slots.
+  // sub-step (rb, rk16); then weight staging items [it0 + i*n/16,
+  // it0 + (i+1)*n/16) of the tile being staged, or (dma) the activation load
+  // i - 8 of tile dkt into buffer rb ^ 1.  The compiler may not reorder
+  // across the slots.
   auto substep = [&](const Frags& fc, Frags& fn, int rb, int rk16, int it0, int n, int q, const WSuper& w, int nb,
-                     int kn) __attribute__((always_inline)) {
+                     bool dma, int dkt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       acc[i >> 2][i & 3] = mfma32x32x16(fc.a[i >> 2], fc.b[i & 3], acc[i >> 2][i & 3]);
       if (i < 4)
-        fn.a[i] = *reinterpret_cast<const bf16x8*>(lbase + rb * kBufElems + fa_off + 32 * i * kPP + 16 * rk16);
+        fn.a[i] = frag_w(rb, i, rk16);
       else if (i < 8)
-        fn.b[i - 4] = *reinterpret_cast<const bf16x8*>(lbase + rb * kBufElems + fb_off + 32 * (i - 4) * kPP + 16 * rk16);
+        fn.b[i - 4] = frag_x(rb, i - 4, rk16);
+      else if (dma)
+        xdma(dkt, rb ^ 1, i - 8);
 #pragma unroll
-      for (int it = it0 + i * n / 16; it < it0 + (i + 1) * n / 16; ++it) stage_item(kItemOrder[it], q, w, nb, kn);
+      for (int it = it0 + i * n / 16; it < it0 + (i + 1) * n / 16; ++it) stage_item(kItemOrder[it], q, w, nb);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   Frags fa, fb;
-  // One 64-k tile kt on buffer kt & 1; stages tile kt + 1 (superblock half q
-  // of w) into the other buffer.
-  auto tile = [&](int kt, int q, const WSuper& w) __attribute__((always_inline)) {
+  // One 64-k tile kt on buffers kt & 1; stages the weights of tile kt + 1
+  // (superblock half q of w) and issues the activation loads of tile kt + 2.
+  // vm8: 8 weight loads were issued after the activation loads of tile kt + 1
+  // (so the wait before the barrier leaves those 8 outstanding)
+  auto tile = [&](int kt, int q, const WSuper& w, bool vm8) __attribute__((always_inline)) {
     const int b = kt & 1;
-    const int kn = min(kt + 2, nk - 1);
     launder();
-    substep(fa, fb, b, 1, 0, 6, q, w, b ^ 1, kn);
-    substep(fb, fa, b, 2, 6, 6, q, w, b ^ 1, kn);
-    substep(fa, fb, b, 3, 12, 6, q, w, b ^ 1, kn);
-    // every wavefront has read buffer b and written buffer b ^ 1
+    substep(fa, fb, b, 1, 0, 6, q, w, b ^ 1, false, 0);
+    substep(fb, fa, b, 2, 6, 6, q, w, b ^ 1, false, 0);
+    substep(fa, fb, b, 3, 12, 6, q, w, b ^ 1, false, 0);
+    // this wavefront's activation loads of tile kt + 1 have landed; after the
+    // barrier every wavefront has read buffer b and filled buffer b ^ 1
     __builtin_amdgcn_sched_barrier(0);
+    if (vm8)
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    substep(fb, fa, b ^ 1, 0, 0, 0, q, w, b, kn);
+    substep(fb, fa, b ^ 1, 0, 0, 0, q, w, b, true, min(kt + 2, nk - 1));
   };
 
-  // prologue: tile 0 into buffer 0; tile 1's activations and superblocks 0, 1 in registers
-  wsuper_load(0, wcur);
-  wsuper_load(1, wnext);
+  // prologue: superblocks 0, 1 and activation tiles 0, 1 in flight; weight tile 0 staged
+  wsuper_load(0, wA);
+  wsuper_load(1, wB);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) xv[p] = xload(0, p);
-  const int k1 = min(1, nk - 1);
+  for (int p = 0; p < 8; ++p) xdma(0, 0, p);
 #pragma unroll
-  for (int it = 0; it < 18; ++it) stage_item(kItemOrder[it], 0, wcur, 0, k1);
+  for (int p = 0; p < 8; ++p) xdma(min(1, nk - 1), 1, p);
+#pragma unroll
+  for (int it = 0; it < 18; ++it) stage_item(kItemOrder[it], 0, wA, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm8);     // activation tile 0 (tile 1's 8 loads may be pending)
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    fa.a[i] = *reinterpret_cast<const bf16x8*>(lbase + fa_off + 32 * i * kPP);
-    fa.b[i] = *reinterpret_cast<const bf16x8*>(lbase + fb_off + 32 * i * kPP);
+    fa.a[i] = frag_w(0, i, 0);
+    fa.b[i] = frag_x(0, i, 0);
   }
 
-  for (int kt = 0; kt < nk; kt += 2) {
-    tile(kt, 1, wcur);              // stages tile kt + 1: second half of superblock kt / 2
-    wcur = wnext;
-    wsuper_load(kt / 2 + 2, wnext);
-    tile(kt + 1, 0, wcur);          // stages tile kt + 2: first half of superblock kt / 2 + 1 (nk is even)
+  // Superblock s lives in wA for even s, wB for odd s: four tiles per pass so
+  // that the two register sets never need copying (a copy would wait for
+  // loads still in flight).
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    tile(kt, 1, wA, false);           // stages tile kt + 1: superblock kt / 2, second half
+    wsuper_load(kt / 2 + 2, wA);
+    tile(kt + 1, 0, wB, true);        // tile kt + 2: superblock kt / 2 + 1, first half
+    tile(kt + 2, 1, wB, false);       // tile kt + 3: second half
+    wsuper_load(kt / 2 + 3, wB);
+    tile(kt + 3, 0, wA, true);        // tile kt + 4: superblock kt / 2 + 2, first half
   }
+  if (kt < nk) {                      // nk % 4 == 2
+    tile(kt, 1, wA, false);
+    tile(kt + 1, 0, wB, false);       // stages past the end (never read)
+  }
+  // the last activation loads (re-reads of the last tile) land before LDS is reused
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 
   // epilogue: y[m][n] = bf16(acc * gs + bias[n]) through an LDS tile [m][n]
   const float gs = *gs_ptr;
-  uint16_t (*out)[kOP] = reinterpret_cast<uint16_t (*)[kOP]>(&lds[0][0][0][0]);
+  uint16_t (*out)[kOP] = reinterpret_cast<uint16_t (*)[kOP]>(lds);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -393,7 +452,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 hipError_t launch_gemm_prefill(const void* x, int64_t M, int64_t K, const uint8_t* packed,
                                const uint8_t* scales, const float* global_scale, int64_t N,
                                const void* bias, void* y, hipStream_t stream) {
-  if (K % (2 * kPK) != 0) {
+  if (K % (2 * kPK) != 0 || K > kMaxPrefillK) {
     const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
     return launch_kernel((const void*)gemm_prefill_small_kernel<false>, grid, dim3(256), stream,
                          (const uint16_t*)x, (int)M, (int)K, packed, scales, global_scale, (int)N,
