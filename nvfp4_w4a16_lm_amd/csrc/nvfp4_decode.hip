@@ -275,24 +275,33 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // MFMA step s (k = 64 g + 8 s .. + 8 of the chunk) reads its MT activation
+    // fragments once and applies them to all R weight tiles.
     auto compute = [&](int c, int buf) {
+      u32x4 wd[R][2];
+      float sv[R][4];
 #pragma unroll
       for (int t = 0; t < R; ++t) {
-        const u32x4 w0 = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g]);
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g + 16]);
+        wd[t][0] = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g]);
+        wd[t][1] = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g + 16]);
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(&sl[wave][t][r][16 * (c % kSuper) + 4 * g]);
-        const float sv0 = NVFP4_E4M3_TO_F32(sw, 0), sv1 = NVFP4_E4M3_TO_F32(sw, 1);
-        const float sv2 = NVFP4_E4M3_TO_F32(sw, 2), sv3 = NVFP4_E4M3_TO_F32(sw, 3);
-        const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        const float sv[4] = {sv0, sv1, sv2, sv3};
+        sv[t][0] = NVFP4_E4M3_TO_F32(sw, 0);
+        sv[t][1] = NVFP4_E4M3_TO_F32(sw, 1);
+        sv[t][2] = NVFP4_E4M3_TO_F32(sw, 2);
+        sv[t][3] = NVFP4_E4M3_TO_F32(sw, 3);
+      }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 a = dequant8(wd[s], sv[s >> 1]);
+      for (int s = 0; s < 8; ++s) {
+        bf16x8 bx[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const bf16x8 bx = *reinterpret_cast<const bf16x8*>(&xs[buf][16 * mt + r][64 * g + 8 * s]);
-            acc[t][mt] = mfma16x16x32(a, bx, acc[t][mt]);
-          }
+        for (int mt = 0; mt < MT; ++mt)
+          bx[mt] = *reinterpret_cast<const bf16x8*>(&xs[buf][16 * mt + r][64 * g + 8 * s]);
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          const uint32_t w = wd[t][s >> 2][s & 3];
+          const bf16x8 a = dequant8(w, sv[t][s >> 1]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[mt], acc[t][mt]);
         }
       }
     };
@@ -486,7 +495,7 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     case 1: return mfma_launch<1, 1>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 2: return mfma_launch<2, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 3: return mfma_launch<3, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    default: return mfma_launch<4, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    default: return mfma_launch<4, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
   }
 }
 
