@@ -46,6 +46,13 @@ def gemm_flops(m: int, n: int, k: int) -> float:
     return 2.0 * m * n * k
 
 
+def decode_kernel_name(m: int, k: int) -> str:
+    """Which decode kernel the library dispatches for (M, K) (mirrors its dispatch rule)."""
+    if k % 32 == 0 and ((m == 1 and k <= 8192) or (m == 2 and k <= 4096)):
+        return "gemv_dot_kernel"
+    return "gemv_mfma_kernel" if k % 256 == 0 else "gemv_mfma_ragged_kernel"
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_w4a16_lm_amd", "csrc")
@@ -55,8 +62,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(op: str):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if current."""
+def load_traffic(workload: str, op: str):
+    """HBM bytes per launch of ``op`` (FETCH_SIZE and WRITE_SIZE counter runs,
+    scaled by a plain-copy calibration; profiles/hbm_traffic.md), or None when
+    the kernels have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))
@@ -64,11 +73,13 @@ def load_traffic(op: str):
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("ops", {}).get(op)
+    return rec.get("ops", {}).get(f"{workload}/{op}")
 
 
-def cpu_baseline(wl, w, w_bits, x_bits, ms, rows: int):
-    """The oracle, as it stands, on the first ``rows`` weight rows (same step)."""
+def cpu_baseline(wl, w, w_bits, x_bits, ms, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same step: the first
+    ``rows`` weight rows, sized from a short calibration run so that the timed
+    sample takes about ``budget_s`` seconds of CPU work."""
     import numpy as np
 
     import oracle.nvfp4_oracle as O
@@ -78,13 +89,20 @@ def cpu_baseline(wl, w, w_bits, x_bits, ms, rows: int):
         blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:   # threadpoolctl missing: numpy elementwise work is single-threaded
         blas = 1
-    sub = np.ascontiguousarray(w_bits[:rows])
-    t0 = time.perf_counter()
-    gs = O.global_scale(O.weight_amax(sub))
-    packed, scales = O.quantize_rows(sub, gs)
-    for m in ms:
-        O.gemm_ref(x_bits[:m], packed, scales, gs)
-    dt = time.perf_counter() - t0
+
+    def step(rows):
+        sub = np.ascontiguousarray(w_bits[:rows])
+        t0 = time.perf_counter()
+        gs = O.global_scale(O.weight_amax(sub))
+        packed, scales = O.quantize_rows(sub, gs)
+        for m in ms:
+            O.gemm_ref(x_bits[:m], packed, scales, gs)
+        return time.perf_counter() - t0
+
+    probe = min(1024, w.n)
+    rate = probe / max(step(probe), 1e-6)                 # rows per second
+    rows = int(min(w.n, max(probe, rate * budget_s)))
+    dt = step(rows)
     nbytes = quant_bytes(rows, w.k) + sum(gemm_bytes(m, rows, w.k) for m in ms)
     return {
         "value": nbytes / dt / 1e12,
@@ -103,9 +121,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b",
                     help="llama3_8b (default), llama3_70b, qwen_prefill, heavy_tail, tiny")
-    ap.add_argument("--cpu-rows", type=int, default=24576, help="oracle sample size (weight rows)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=3, help="rotating quantized-weight copies")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -122,6 +142,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_probe:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch, 5 launches
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_launch": src.numel() * 4, "launches": 5}))
+        return 0
     B.load_library()
     dev = torch.device("cuda:0")
     w = wl.WORKLOADS[args.workload]
@@ -194,21 +224,22 @@ def main() -> int:
     dom = max(ops, key=lambda op: avg_ms[op])
     if dom == "quantize":
         achieved = quant_bytes(n, k) / (avg_ms[dom] * 1e-3) / 1e9
-        roof = {"op": "nvfp4_refresh_inplace", "kernels": "amax + quant_pack (+2 one-thread kernels)",
+        roof = {"op": "nvfp4_refresh_inplace",
+                "kernels": "amax_init (1 thread) + amax + quant_pack, back to back on one stream",
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic("quantize")}
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(w.name, "quantize")}
     else:
         m = int(dom.split("_m")[1])
         if m > 64:
             achieved = gemm_flops(m, n, k) / (avg_ms[dom] * 1e-3) / 1e12
             roof = {"op": f"nvfp4_w4a16_gemm M={m}", "kernels": "gemm_prefill_kernel", "bound": "mfma",
                     "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": load_traffic(dom)}
+                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": load_traffic(w.name, dom)}
         else:
             achieved = gemm_bytes(m, n, k) / (avg_ms[dom] * 1e-3) / 1e9
-            roof = {"op": f"nvfp4_w4a16_gemm M={m}", "kernels": "gemv_kernel", "bound": "hbm",
+            roof = {"op": f"nvfp4_w4a16_gemm M={m}", "kernels": decode_kernel_name(m, k), "bound": "hbm",
                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(dom)}
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(w.name, dom)}
 
     out = {
         "metric": METRIC,
@@ -230,7 +261,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, w, w_bits, x_bits, ms, min(args.cpu_rows, n))
+        out["cpu_baseline"] = cpu_baseline(wl, w, w_bits, x_bits, ms, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
