@@ -33,6 +33,31 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// E4M3 scale s (as fp32) = e2 * mu: e2 = 2^e (its exponent field), mu in
+// [1, 2) (its significand, 3 fraction bits) as an f16 pair; s = 0 gives mu 0.
+__device__ __forceinline__ void split_scale(float s, float* e2, f16x2* mu) {
+  const uint32_t b = __float_as_uint(s);
+  *e2 = __uint_as_float(b & 0x7F800000u);
+  const _Float16 m = (s == 0.0f) ? (_Float16)0.0f : (_Float16)__uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
+  *mu = f16x2{m, m};
+}
+
+// Codes 0..7 of w (low nibble first) times e2 * mu, exact in f16.
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float e2, f16x2 mu) {
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 0) * mu;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 1) * mu;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 2) * mu;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 3) * mu;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
 __device__ __forceinline__ uint32_t out_bf16(float acc, float gs, const uint16_t* __restrict__ bias, int n) {
   float v = acc * gs;
   if (bias != nullptr) v += __uint_as_float((uint32_t)bias[n] << 16);
@@ -189,8 +214,9 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
 // instructions of 8 rows x 128 B -- and transposed through a per-wavefront
 // LDS region into the operand layout: lane (r, g) = (lane % 16, lane / 16)
 // reads row r, bytes [32 g, 32 g + 32) of the chunk, i.e. k = 256 c + 64 g
-// + [0, 64); MFMA step s uses k + 8 s .. + 8.  Scales come in whole lines
-// too (128 B = 8 chunks per row) and are staged the same way.  The chunk of
+// + [0, 64); MFMA step s uses k + 8 s .. + 8.  Each lane loads the 4 scale
+// bytes of its own k range directly (they are 1/9 of the bytes, and the rest
+// of each 128-byte scale line is used by the next 7 chunks).  The chunk of
 // x (M rounded up to 16) is staged once per workgroup in double-buffered
 // LDS.  Needs K % 256 == 0 (whole lines per row); rows past N are read from
 // clamped addresses and their outputs are never stored.
@@ -198,7 +224,14 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
 constexpr int kChunk = 256;
 constexpr int kXPitch = kChunk + 8;   // bf16 per LDS row of x (breaks bank alignment)
 constexpr int kWPitch = 128 + 16;     // bytes per LDS row of a weight tile
-constexpr int kSuper = 8;             // chunks per 128-byte line of scales
+
+// one wavefront's weights of a 256-k chunk: R tiles x 2 loader pieces, and
+// the operand-layout scale word of each tile
+template <int R>
+struct WChunk {
+  u32x4 w[R][2];
+  uint32_t s[R];
+};
 
 template <int MT, int R>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restrict__ x, int M, int K,
@@ -209,7 +242,6 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
                                                         uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][16 * MT][kXPitch];
   __shared__ __attribute__((aligned(16))) uint8_t wl[4][R][16][kWPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t sl[4][R][16][kWPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int lr = lane >> 3, lq = lane & 7;          // loader: row within 8, 16-byte piece of the line
@@ -222,28 +254,23 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
     const int n_base = rb * (64 * R) + wave * (16 * R);
     // loader row pointers: tile t, half j covers rows n_base + 16 t + 8 j + lr
     const uint8_t* lp[R][2];
-    const uint8_t* ls[R][2];
 #pragma unroll
     for (int t = 0; t < R; ++t)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t row = min(n_base + 16 * t + 8 * j + lr, N - 1);
-        lp[t][j] = packed + row * prow;
-        ls[t][j] = scales + row * srow;
-      }
-    auto load_w = [&](int c, u32x4 (&wr)[R][2]) {
+      for (int j = 0; j < 2; ++j) lp[t][j] = packed + (int64_t)min(n_base + 16 * t + 8 * j + lr, N - 1) * prow;
+    // scale words in operand layout: lane (r, g) of tile t needs the 4 block
+    // scales of k = 64 g .. + 64 of row n_base + 16 t + r, i.e. bytes 16 c + 4 g
+    const uint8_t* lsc[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) lsc[t] = scales + (int64_t)min(n_base + 16 * t + r, N - 1) * srow + 4 * g;
+    auto load_w = [&](int c, WChunk<R>& wc) {
       const int64_t off = min((int64_t)128 * c + 16 * lq, prow - 16);
 #pragma unroll
-      for (int t = 0; t < R; ++t)
+      for (int t = 0; t < R; ++t) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) wr[t][j] = load_stream16(lp[t][j] + off);
-    };
-    auto load_s = [&](int sc, u32x4 (&sr)[R][2]) {
-      const int64_t off = min((int64_t)128 * sc + 16 * lq, srow - 16);
-#pragma unroll
-      for (int t = 0; t < R; ++t)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) sr[t][j] = load_stream16(ls[t][j] + off);
+        for (int j = 0; j < 2; ++j) wc.w[t][j] = load_stream16(lp[t][j] + off);
+        wc.s[t] = *reinterpret_cast<const uint32_t*>(lsc[t] + 16 * min(c, nchunks - 1));
+      }
     };
     auto stage = [&](const u32x4 (&v)[R][2], uint8_t (*dst)[16][kWPitch]) {
 #pragma unroll
@@ -277,14 +304,14 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
 
     // MFMA step s (k = 64 g + 8 s .. + 8 of the chunk) reads its MT activation
     // fragments once and applies them to all R weight tiles.
-    auto compute = [&](int c, int buf) {
+    auto compute = [&](const WChunk<R>& wc, int buf) {
       u32x4 wd[R][2];
       float sv[R][4];
 #pragma unroll
       for (int t = 0; t < R; ++t) {
         wd[t][0] = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g]);
         wd[t][1] = *reinterpret_cast<const u32x4*>(&wl[wave][t][r][32 * g + 16]);
-        const uint32_t sw = *reinterpret_cast<const uint32_t*>(&sl[wave][t][r][16 * (c % kSuper) + 4 * g]);
+        const uint32_t sw = wc.s[t];
         sv[t][0] = NVFP4_E4M3_TO_F32(sw, 0);
         sv[t][1] = NVFP4_E4M3_TO_F32(sw, 1);
         sv[t][2] = NVFP4_E4M3_TO_F32(sw, 2);
@@ -306,33 +333,28 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
       }
     };
 
-    u32x4 wr0[R][2], wr1[R][2], sr[R][2];
+    WChunk<R> wc0, wc1;
     u32x4 xv[2 * MT];
     load_x(0, xv);
-    load_s(0, sr);
-    load_w(0, wr0);
+    load_w(0, wc0);
     store_x(0, xv);
     __syncthreads();
-    // one step: stage chunk c's weights (and, every kSuper chunks, a line of
-    // scales) into this wavefront's LDS, compute, stage the prefetched x
-    auto step = [&](int c, const u32x4 (&wcur)[R][2], u32x4 (&wnext)[R][2]) {
+    // one step: stage chunk c's weights into this wavefront's LDS, compute,
+    // stage the prefetched x
+    auto step = [&](int c, const WChunk<R>& wcur, WChunk<R>& wnext) {
       const bool has_next = c + 1 < nchunks;
       if (has_next) {
         load_x(c + 1, xv);          // x first: waiting on it must not wait on the weights
         load_w(c + 1, wnext);
       }
-      if (c % kSuper == 0) {
-        stage(sr, sl[wave]);
-        if (c + kSuper < nchunks) load_s(c / kSuper + 1, sr);
-      }
-      stage(wcur, wl[wave]);
-      compute(c, c & 1);
+      stage(wcur.w, wl[wave]);
+      compute(wcur, c & 1);
       if (has_next) store_x((c + 1) & 1, xv);
       __syncthreads();
     };
     for (int c = 0; c < nchunks; c += 2) {
-      step(c, wr0, wr1);
-      if (c + 1 < nchunks) step(c + 1, wr1, wr0);
+      step(c, wc0, wc1);
+      if (c + 1 < nchunks) step(c + 1, wc1, wc0);
     }
 
 #pragma unroll
@@ -355,6 +377,141 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
       }
     }
   }  // row blocks
+}
+
+// ---------------------------------------------------------------------------
+// gemv_xres_kernel<NW>: 2 < M <= 16 with the whole activation resident in LDS
+// (M * (2K + 16) bytes; K % 256 == 0).  NW wavefronts per workgroup; x is
+// copied into LDS once, then every wavefront streams whole 16-row weight
+// tiles over all of K with no further synchronisation.  Weights arrive 8
+// lanes per 128-byte line and are transposed through a per-wavefront LDS
+// tile into the 16x16x32 operand layout, as in gemv_mfma_kernel.  MFMA
+// columns m >= M read row M - 1 of x and are never stored.
+//
+// The arithmetic is f16 MFMA with fp32 accumulation:
+//  * weights: code * s is exact in f16 (at most 6 significant bits, within
+//    [2^-10, 2688]).  With s = 2^e * mu (mu in [1, 2), 3 fraction bits),
+//    v_cvt_scalef32_pk_f16_fp4 applies 2^e exactly and one packed f16
+//    multiply applies mu: 8 VALU ops per 8 weights instead of 20 on the fp32
+//    route (exactness checked on the GPU for all code pairs and scales);
+//  * activations: row m is stored as x * 2^-p_m in f16, with p_m set from the
+//    row's largest |x| so that it lands in [2^14, 2^15).  Every x with
+//    |x| >= 2^-28 max|x_m| converts exactly (bf16's 8 significant bits fit);
+//    smaller ones become f16 subnormals or zero, an error below
+//    2^-38 max|x_m| per element.  The epilogue multiplies by 2^p_m.
+// ---------------------------------------------------------------------------
+constexpr int kXresLdsMax = 160 * 1024;
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                          const uint8_t* __restrict__ packed,
+                                                          const uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ gs_ptr, int N,
+                                                          const uint16_t* __restrict__ bias,
+                                                          uint16_t* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int xpitch = 2 * K + 16;                    // bytes per x row (the pad spreads rows over banks)
+  uint8_t* const xl = lds;
+  uint8_t (*const wl)[16][kWPitch] = reinterpret_cast<uint8_t (*)[16][kWPitch]>(lds + M * xpitch);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int lr = lane >> 3, lq = lane & 7;          // loader: row within 8, 16-byte piece of the line
+  const int nchunks = K / kChunk;
+  const int64_t prow = K >> 1, srow = K >> 4;
+
+  // x -> f16 rows in LDS: wavefront w handles rows w, w + NW, ...: the row's
+  // largest |x| (bf16 magnitudes compare as integers), then x * 2^-p_m
+  float* const xup = reinterpret_cast<float*>(lds + M * xpitch + NW * 16 * kWPitch);   // 2^p_m
+  const int xvec = K / 8;                           // 16-byte vectors per x row
+  for (int m = wave; m < M; m += NW) {
+    const uint16_t* xr = x + (int64_t)m * K;
+    uint32_t mx = 0;
+    for (int kv = lane; kv < xvec; kv += 64) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * kv);
+      mx = pk_max_u16(mx, pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
+                                     pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu)));
+    }
+    mx = max(mx & 0xFFFFu, mx >> 16);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    const int p = (mx == 0u) ? 0 : max(-126, (int)(mx >> 7) - 141);   // biased exponent - 127 - 14
+    const float down = __uint_as_float((uint32_t)(127 - p) << 23);
+    if (lane == 0) xup[m] = __uint_as_float((uint32_t)(127 + p) << 23);
+    for (int kv = lane; kv < xvec; kv += 64) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * kv);
+      u32x4 h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 pair = {(_Float16)(bf16_lo(v[e]) * down), (_Float16)(bf16_hi(v[e]) * down)};
+        h[e] = __builtin_bit_cast(uint32_t, pair);
+      }
+      *reinterpret_cast<u32x4*>(xl + m * xpitch + 16 * kv) = h;
+    }
+  }
+  __syncthreads();
+  const float gs = *gs_ptr;
+  const float up = xup[min(r, M - 1)];
+  const uint8_t* const xrow = xl + min(r, M - 1) * xpitch + 128 * g;   // this lane's k-group, chunk 0
+
+  const int ntiles = (N + 15) / 16;
+  for (int tile = blockIdx.x * NW + wave; tile < ntiles; tile += gridDim.x * NW) {
+    const int n_base = tile * 16;
+    const uint8_t* lp[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lp[j] = packed + (int64_t)min(n_base + 8 * j + lr, N - 1) * prow + 16 * lq;
+    const uint8_t* const lsc = scales + (int64_t)min(n_base + r, N - 1) * srow + 4 * g;
+    auto load_w = [&](int c, WChunk<1>& wc) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wc.w[0][j] = load_stream16(lp[j] + 128 * c);
+      wc.s[0] = *reinterpret_cast<const uint32_t*>(lsc + 16 * c);
+    };
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto chunk = [&](int c, const WChunk<1>& wc) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&wl[wave][8 * j + lr][16 * lq]) = wc.w[0][j];
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(&wl[wave][r][32 * g]);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(&wl[wave][r][32 * g + 16]);
+      const uint32_t sw = wc.s[0];
+      float e2[4];
+      f16x2 mu[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float sb = b == 0 ? NVFP4_E4M3_TO_F32(sw, 0) : b == 1 ? NVFP4_E4M3_TO_F32(sw, 1)
+                       : b == 2 ? NVFP4_E4M3_TO_F32(sw, 2) : NVFP4_E4M3_TO_F32(sw, 3);
+        split_scale(sb, &e2[b], &mu[b]);
+      }
+      const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const uint8_t* const xc = xrow + 2 * kChunk * c;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
+        acc = mfma16x16x32_f16(dequant8_f16(wd[s], e2[s >> 1], mu[s >> 1]), bx, acc);
+      }
+    };
+    WChunk<1> wa, wb;
+    load_w(0, wa);
+    for (int c = 0; c < nchunks; c += 2) {
+      if (c + 1 < nchunks) load_w(c + 1, wb);
+      chunk(c, wa);
+      if (c + 1 >= nchunks) break;
+      if (c + 2 < nchunks) load_w(c + 2, wa);
+      chunk(c + 1, wb);
+    }
+    if (r < M) {
+      acc *= up;
+      const int n0 = n_base + 4 * g;
+      uint16_t* yrow = y + (int64_t)r * N;
+      if ((N & 3) == 0 && n0 + 3 < N) {
+        const uint32_t lo = out_bf16(acc[0], gs, bias, n0) | (out_bf16(acc[1], gs, bias, n0 + 1) << 16);
+        const uint32_t hi = out_bf16(acc[2], gs, bias, n0 + 2) | (out_bf16(acc[3], gs, bias, n0 + 3) << 16);
+        *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[v], gs, bias, n0 + v);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -480,6 +637,44 @@ static hipError_t mfma_launch(const void* x, int M, int K, const uint8_t* packed
 // The dot kernel keeps the lane's slice of x in registers (16 * ceil(K/2048)
 // VGPRs per activation row), so it takes M = 1 up to K = 8192 and M = 2 up to
 // K = 4096; everything else goes to the MFMA kernel.
+// Dynamic LDS of gemv_xres_kernel<NW> for (M, K): x rows, NW per-wavefront
+// weight tiles, 16 row scales.
+static int64_t xres_lds_bytes(int64_t M, int64_t K, int nw) {
+  return M * (2 * K + 16) + (int64_t)nw * 16 * kWPitch + 16 * sizeof(float);
+}
+
+template <int NW>
+static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
+                              const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
+  const void* fn = (const void*)gemv_xres_kernel<NW>;
+  const int lds = (int)xres_lds_bytes(M, K, NW);
+  // raise the dynamic LDS limit once per kernel (the default allows less than the hardware's 160 KiB)
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kXresLdsMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const int ntiles = (N + 15) / 16;
+  const int grid = std::max(1, std::min((ntiles + NW - 1) / NW, cus * per_cu));
+  hipLaunchKernelGGL((gemv_xres_kernel<NW>), dim3(grid), dim3(64 * NW), lds, stream, (const uint16_t*)x, M, K,
+                     packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y);
+  return hipGetLastError();
+}
+
+// 0 = the activation does not fit in LDS; else the wavefronts per workgroup
+static int xres_waves(int64_t M, int64_t K) {
+  if (M < 3 || M > 16 || K % kChunk != 0) return 0;
+  if (xres_lds_bytes(M, K, 16) <= kXresLdsMax) return 16;
+  if (xres_lds_bytes(M, K, 8) <= kXresLdsMax) return 8;
+  return 0;
+}
+
 bool decode_uses_dot(int64_t M, int64_t K) {
   return K % 32 == 0 && ((M == 1 && K <= 8192) || (M == 2 && K <= 4096));
 }
@@ -490,6 +685,11 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
   if (decode_uses_dot(M, K)) {
     if (M == 1) return dot_dispatch<1>(x, M, K, packed, scales, gs, N, bias, y, stream);
     return dot_dispatch<2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+  }
+  switch (xres_waves(M, K)) {
+    case 16: return xres_launch<16>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 8: return xres_launch<8>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    default: break;
   }
   switch ((M + 15) / 16) {
     case 1: return mfma_launch<1, 1>(x, M, K, packed, scales, gs, N, bias, y, stream);

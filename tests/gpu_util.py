@@ -113,9 +113,14 @@ def check_gemm(y_bits, x_bits, packed, scales, gs, bias_bits=None, label="", arg
     assert np.all(err <= tol), (f"{label}: north-star bound broken at {worst}: y={y[worst]} "
                                 f"y64={y64[worst]} tol={tol[worst]}")
     # tight bound: fp32 accumulation of K exact products in any order, the scale and
-    # bias operations, then one round-to-nearest to bf16
+    # bias operations, then one round-to-nearest to bf16.  The f16 decode route
+    # stores each activation row as x * 2^-p with max |x * 2^-p| in [2^14, 2^15):
+    # an activation may then move by at most max(2^-39 max|x_m|, 2^-151) (f16
+    # subnormal spacing), i.e. by at most that times sum_k |w_k| <= sqrt(K) ||w_n||.
     k = x_bits.shape[1]
-    acc = (k + 2) * 2.0 ** -24 * (s_abs + bias_abs)
+    xmax = np.max(np.abs(wl.bf16_bits_to_f32(x_bits).astype(np.float64)), axis=1)
+    conv = (2.0 ** -39 * xmax + 2.0 ** -151)[:, None] * np.sqrt(k) * wn[None, :]
+    acc = (k + 2) * 2.0 ** -24 * (s_abs + bias_abs) + conv
     tight = 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
     worst = np.unravel_index(np.argmax(err - tight), err.shape)
     assert np.all(err <= tight), (f"{label}: tight bound broken at {worst}: y={y[worst]} "

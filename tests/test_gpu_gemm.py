@@ -149,3 +149,22 @@ def test_gpu_quantized_buffers_match_oracle_buffers_in_gemm():
     p, s, g = B.nvfp4_quantize(dev_bf16(w))
     y_gpu_buf = gemm_gpu(x, (p, s, g))
     assert np.array_equal(y_oracle_buf, y_gpu_buf)
+
+
+def test_decode_activation_rows_of_extreme_magnitude():
+    """Decode rows whose magnitudes span the bf16 range: zeros, ~2^100, ~2^-100,
+    a mix of 2^20 and 2^-20 within one row, one huge element among tiny ones."""
+    n, k, m = 1027, 1024, 8
+    _, packed, scales, gs, q = setup(n, k, seed=12)
+    rng = np.random.default_rng(13)
+    xf = rng.standard_normal((m, k)).astype(np.float32)
+    xf[0] = 0.0
+    xf[1] *= np.float32(2.0 ** 100)
+    xf[2] *= np.float32(2.0 ** -100)
+    xf[3] *= np.where(rng.random(k) < 0.5, np.float32(2.0 ** 20), np.float32(2.0 ** -20))
+    xf[4] *= np.float32(2.0 ** -60)
+    xf[4, 17] = np.float32(3.0e4)
+    x = torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    y = gemm_gpu(x, q)
+    assert not np.any(y[0] & 0x7FFF), "zero row must give zero logits"
+    check_gemm(y, x, packed, scales, gs, label="extreme rows", argmax_min=0.0)
