@@ -29,6 +29,9 @@ namespace nvfp4 {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// s_waitcnt immediates (gfx9 encoding): vmcnt(0) alone / lgkmcnt(0) alone
+constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -515,6 +518,162 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
+// gemv_panel_kernel<MT, NW, R>: 2 < M <= 64 when the activation does not fit
+// in LDS whole; K % 512 == 0.  A workgroup of NW wavefronts owns blocks of
+// 16 NW R weight rows (R tiles of 16 rows per wavefront; 8 x 4 is used: two
+// wavefronts per SIMD) with the accumulators of the whole block in registers,
+// and walks K in panels of `pk` columns:
+//  * each panel of x (M rows x pk bf16, at most 65 KiB) is copied into LDS
+//    once per workgroup by direct-to-LDS loads, between two barriers;
+//  * each 256-k chunk of a wavefront's 16 R weight rows is copied by
+//    direct-to-LDS loads into the wavefront's own 2 R KiB region, 8 rows x 128 B
+//    per instruction, the 16-byte pieces of row q stored at slot
+//    piece ^ (q & 7) so that the operand-layout reads below hit distinct banks;
+//    the next chunk's copy is issued as soon as this chunk's words are in
+//    registers, and each lane loads its 4 scale bytes per tile directly;
+//  * the activation fragments of each MFMA step serve all R tiles.
+// Rows past N are copied from row N - 1 and never stored; MFMA columns past M
+// read row M - 1 of x and are never stored.
+// ---------------------------------------------------------------------------
+constexpr int kPanelXBytes = 64 * (2 * 512 + 16);       // x panel: M * (2 pk + 16) bytes at most
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int MT, int NW, int kPanelR>
+__global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                         const uint8_t* __restrict__ packed,
+                                                         const uint8_t* __restrict__ scales,
+                                                         const float* __restrict__ gs_ptr, int N,
+                                                         const uint16_t* __restrict__ bias,
+                                                         uint16_t* __restrict__ y, int pk) {
+  __shared__ __attribute__((aligned(16))) uint8_t xp[kPanelXBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wl[NW][kPanelR * 16 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nchunks = K / kChunk, pchunks = pk / kChunk;
+  const int npanels = (nchunks + pchunks - 1) / pchunks;
+  const int xpitch = 2 * pk + 16;
+  const int64_t prow = K >> 1, srow = K >> 4;
+  const float gs = *gs_ptr;
+  const int nblocks = (N + 16 * NW * kPanelR - 1) / (16 * NW * kPanelR);
+  // weight copy: lane fills slot lane & 7 of row 8 j + (lane >> 3), i.e. piece (lane & 7) ^ (lane >> 3)
+  const int wpiece = (lane & 7) ^ (lane >> 3);
+  // operand reads: row 16 t + r, pieces 2 g and 2 g + 1
+  const int wrd0 = r * 128 + 16 * ((2 * g) ^ (r & 7)), wrd1 = r * 128 + 16 * ((2 * g + 1) ^ (r & 7));
+  uint8_t* const wmine = wl[wave];
+
+  for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const int n_wave = blk * (16 * NW * kPanelR) + wave * (16 * kPanelR);
+    auto w_copy = [&](int c) {
+#pragma unroll
+      for (int j = 0; j < 2 * kPanelR; ++j) {
+        const int64_t row = min(n_wave + 8 * j + (lane >> 3), N - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(packed + row * prow + 128 * c + 16 * wpiece),
+                                         (lds_ptr_t)(wmine + 1024 * j), 16, 0, 0);
+      }
+    };
+    auto s_load = [&](int c, uint32_t (&sw)[kPanelR]) {
+#pragma unroll
+      for (int t = 0; t < kPanelR; ++t)
+        sw[t] = *reinterpret_cast<const uint32_t*>(scales + (int64_t)min(n_wave + 16 * t + r, N - 1) * srow +
+                                                   16 * c + 4 * g);
+    };
+    auto x_copy = [&](int p) {
+      const int per_row = min(pk, K - p * pk) / 512;   // 1 KiB copies per row of this panel
+      for (int i = wave; i < M * per_row; i += NW) {
+        const int m = i / per_row, h = i - m * per_row;
+        __builtin_amdgcn_global_load_lds((const void*)(x + (int64_t)m * K + p * pk + 512 * h + 8 * lane),
+                                         (lds_ptr_t)(xp + m * xpitch + 1024 * h), 16, 0, 0);
+      }
+    };
+
+    f32x4 acc[kPanelR][MT];
+#pragma unroll
+    for (int t = 0; t < kPanelR; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int xrow[MT];                                       // LDS byte offsets of this lane's x rows
+
+    // chunk c (local chunk cc of the panel): this chunk's weights are in wmine
+    // and its scale words in sw; the next chunk's copy and scales go to swn
+    auto chunk = [&](int c, int cc, const uint32_t (&sw)[kPanelR], uint32_t (&swn)[kPanelR]) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);            // this chunk's weight copy has landed
+      u32x4 wd[kPanelR][2];
+#pragma unroll
+      for (int t = 0; t < kPanelR; ++t) {
+        wd[t][0] = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + wrd0);
+        wd[t][1] = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + wrd1);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);          // the region may now be overwritten
+      const int cn = min(c + 1, nchunks - 1);
+      w_copy(cn);
+      s_load(cn, swn);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        bf16x8 bx[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          bx[mt] = *reinterpret_cast<const bf16x8*>(xp + xrow[mt] + 2 * kChunk * cc + 16 * s);
+#pragma unroll
+        for (int t = 0; t < kPanelR; ++t) {
+          const float sv = (s >> 1) == 0 ? NVFP4_E4M3_TO_F32(sw[t], 0) : (s >> 1) == 1 ? NVFP4_E4M3_TO_F32(sw[t], 1)
+                         : (s >> 1) == 2 ? NVFP4_E4M3_TO_F32(sw[t], 2) : NVFP4_E4M3_TO_F32(sw[t], 3);
+          const bf16x8 a = dequant8(wd[t][s >> 2][s & 3], sv);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[mt], acc[t][mt]);
+        }
+      }
+    };
+
+    uint32_t swa[kPanelR], swb[kPanelR];
+    w_copy(0);
+    s_load(0, swa);
+    int c = 0;
+    for (int p = 0; p < npanels; ++p) {
+      __syncthreads();                                  // the previous panel's reads are done
+      x_copy(p);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();                                  // the panel is in LDS
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xrow[mt] = min(16 * mt + r, M - 1) * xpitch + 128 * g;
+      const int c1 = min(nchunks, c + pchunks);
+      const int c0 = c;
+      for (; c + 1 < c1; c += 2) {
+        chunk(c, c - c0, swa, swb);
+        chunk(c + 1, c + 1 - c0, swb, swa);
+      }
+      if (c < c1) {                                     // odd chunk count: keep the scale roles
+        chunk(c, c - c0, swa, swb);
+#pragma unroll
+        for (int t = 0; t < kPanelR; ++t) swa[t] = swb[t];
+        ++c;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);               // the last (re-read) copy has landed
+
+#pragma unroll
+    for (int t = 0; t < kPanelR; ++t) {
+      const int n0 = n_wave + 16 * t + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + r;
+        if (m >= M) continue;
+        uint16_t* yrow = y + (int64_t)m * N;
+        if ((N & 3) == 0 && n0 + 3 < N) {
+          const uint32_t lo = out_bf16(acc[t][mt][0], gs, bias, n0) | (out_bf16(acc[t][mt][1], gs, bias, n0 + 1) << 16);
+          const uint32_t hi = out_bf16(acc[t][mt][2], gs, bias, n0 + 2) | (out_bf16(acc[t][mt][3], gs, bias, n0 + 3) << 16);
+          *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[t][mt][v], gs, bias, n0 + v);
+        }
+      }
+    }
+    __syncthreads();                                    // the x region is reused by the next block
+  }
+}
+
+// ---------------------------------------------------------------------------
 // gemv_mfma_ragged_kernel<MT>: the same MFMA arithmetic for K % 256 != 0,
 // where rows are not whole 128-byte lines.  One wavefront per 16 rows, the x
 // chunk staged in LDS per workgroup, and per-block 8-byte weight loads from
@@ -667,6 +826,28 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
   return hipGetLastError();
 }
 
+// Panel width for gemv_panel_kernel: the widest multiple of 512 columns whose
+// M rows (plus 16 bytes of padding each) fit in the x panel region.
+static int panel_columns(int M, int K) {
+  const int pk = ((kPanelXBytes / M - 16) / 2) / 512 * 512;
+  return std::min(pk, K);
+}
+
+template <int MT, int NW, int R>
+static hipError_t panel_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
+                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
+  const void* fn = (const void*)gemv_panel_kernel<MT, NW, R>;
+  const int nblocks = (N + 16 * NW * R - 1) / (16 * NW * R);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const dim3 grid(std::min(nblocks, cus * per_cu));
+  return launch_kernel(fn, grid, dim3(64 * NW), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
+                       (const uint16_t*)bias, (uint16_t*)y, panel_columns(M, K));
+}
+
 // 0 = the activation does not fit in LDS; else the wavefronts per workgroup
 static int xres_waves(int64_t M, int64_t K) {
   if (M < 3 || M > 16 || K % kChunk != 0) return 0;
@@ -690,6 +871,14 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     case 16: return xres_launch<16>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 8: return xres_launch<8>(x, M, K, packed, scales, gs, N, bias, y, stream);
     default: break;
+  }
+  if (K % 512 == 0) {
+    switch ((M + 15) / 16) {
+      case 1: return panel_launch<1, 8, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+      case 2: return panel_launch<2, 8, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+      case 3: return panel_launch<3, 8, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+      default: return panel_launch<4, 8, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    }
   }
   switch ((M + 15) / 16) {
     case 1: return mfma_launch<1, 1>(x, M, K, packed, scales, gs, N, bias, y, stream);
