@@ -19,7 +19,7 @@
 // Memory access: HBM streams fastest when each workgroup walks a contiguous
 // span with every wavefront instruction covering 1 KiB (measured ~7 TB/s on
 // MI355X, against ~6 TB/s for grid-stride loops), so both streaming kernels
-// split the weight into one contiguous span per workgroup (amax: ~4096 long
+// split the weight into one contiguous span per workgroup (amax: ~1024 long
 // spans; quant_pack: 64 KiB spans).
 // quant_pack walks the tensor from its end, so its first reads find the tail
 // of the weight that amax read last; it collects each 64 KiB span's codes and
@@ -38,7 +38,7 @@ namespace nvfp4 {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;                  // 16-byte vectors in flight per thread
-constexpr int kSpan = 4096;                 // 16-byte vectors per workgroup span (64 KiB of weights)
+constexpr int kSpan = 4096;                 // 16-byte vectors per quant_pack span (64 KiB of weights)
 constexpr uint32_t kTag = 0x80000000u;      // marks the word as holding an amax
 
 __global__ void amax_init_kernel(uint32_t* __restrict__ word) {
@@ -123,8 +123,10 @@ __device__ __forceinline__ uint32_t encode_half_block(const u32x4 v, float inv, 
   return fix_zero_signs(c);
 }
 
+// One kSpan-vector span per workgroup, taken from the end of the tensor
+// (workgroup 0 gets the last span).
 __global__ __launch_bounds__(kThreads) void quant_pack_kernel(const u32x4* __restrict__ w, int64_t n16,
-                                                              int64_t per_wg, float* __restrict__ gs_word,
+                                                              float* __restrict__ gs_word,
                                                               uint32_t* __restrict__ packed,
                                                               uint8_t* __restrict__ scales) {
   __shared__ float rlut[128];
@@ -149,8 +151,8 @@ __global__ __launch_bounds__(kThreads) void quant_pack_kernel(const u32x4* __res
   __syncthreads();
 
   const int64_t span = (int64_t)(gridDim.x - 1 - blockIdx.x);
-  const int64_t b0 = span * per_wg;
-  const int64_t b1 = min(n16, b0 + per_wg);
+  const int64_t b0 = span * kSpan;
+  const int64_t b1 = min(n16, b0 + kSpan);
   for (int64_t i = b0 + threadIdx.x; i < b1; i += kThreads * kUnroll) {
     u32x4 v[kUnroll];
     // clamped, unconditional loads; vectors past the span end are encoded
@@ -196,12 +198,13 @@ hipError_t launch_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed,
                            float* global_scale, hipStream_t stream) {
   const int64_t n16 = N * K / 8;                 // 16-byte vectors of the weight (even: K % 16 == 0)
   uint32_t* word = reinterpret_cast<uint32_t*>(global_scale);
-  // amax: about 4096 workgroups, each one contiguous span of a multiple of
-  // 512 vectors (long spans stream best).  quant_pack: spans of kSpan
-  // vectors, whose codes and scales fit its LDS staging (a multiple of 512,
-  // so a block never straddles two workgroups and lane parity equals vector
-  // parity in every iteration: the two halves of a block sit in lanes 2j, 2j+1).
-  const int64_t amax_span = std::max<int64_t>(512, ((n16 + 4095) / 4096 + 511) / 512 * 512);
+  // amax: about 1024 workgroups, each one contiguous span of a multiple of
+  // 512 vectors (long spans stream best: 1024 spans beat 4096 by ~11 %).
+  // quant_pack: one span of kSpan vectors per workgroup, whose codes and
+  // scales fit its LDS staging.  Both span sizes are multiples of 512, so a
+  // block never straddles two workgroups and lane parity equals vector parity
+  // in every iteration (the two halves of a block sit in lanes 2j, 2j+1).
+  const int64_t amax_span = std::max<int64_t>(512, ((n16 + 1023) / 1024 + 511) / 512 * 512);
   const int amax_grid = (int)((n16 + amax_span - 1) / amax_span);
   const int pack_grid = (int)((n16 + kSpan - 1) / kSpan);
   hipError_t e;
@@ -211,8 +214,8 @@ hipError_t launch_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed,
                     reinterpret_cast<const u32x4*>(W), n16, amax_span, word);
   if (e != hipSuccess) return e;
   e = launch_kernel((const void*)quant_pack_kernel, dim3(pack_grid), dim3(kThreads), stream,
-                    reinterpret_cast<const u32x4*>(W), n16, (int64_t)kSpan, global_scale,
-                    reinterpret_cast<uint32_t*>(packed), scales);
+                    reinterpret_cast<const u32x4*>(W), n16, global_scale, reinterpret_cast<uint32_t*>(packed),
+                    scales);
   return e;
 }
 
