@@ -50,7 +50,11 @@ def decode_kernel_name(m: int, k: int) -> str:
     """Which decode kernel the library dispatches for (M, K) (mirrors its dispatch rule)."""
     if k % 32 == 0 and ((m == 1 and k <= 8192) or (m == 2 and k <= 4096)):
         return "gemv_dot_kernel"
-    return "gemv_mfma_kernel" if k % 256 == 0 else "gemv_mfma_ragged_kernel"
+    if k % 256 != 0:
+        return "gemv_mfma_ragged_kernel"
+    if 3 <= m <= 16 and m * (2 * k + 16) + 8 * 16 * 144 + 64 <= 160 * 1024:
+        return "gemv_xres_kernel"
+    return "gemv_panel_kernel" if k % 512 == 0 else "gemv_mfma_kernel"
 
 
 def kernel_source_hash() -> str:
