@@ -31,6 +31,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0) alone / lgkmcnt(0) alone
 constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
+constexpr int kCachePolicyNT = 2;   // cache-policy operand of direct-to-LDS loads: nontemporal
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -523,19 +524,24 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
 // 16 NW R weight rows (R tiles of 16 rows per wavefront; 8 x 4 is used: two
 // wavefronts per SIMD) with the accumulators of the whole block in registers,
 // and walks K in panels of `pk` columns:
-//  * each panel of x (M rows x pk bf16, at most 65 KiB) is copied into LDS
+//  * each panel of x (M rows x pk bf16, at most 64 KiB) is copied into LDS
 //    once per workgroup by direct-to-LDS loads, between two barriers;
 //  * each 256-k chunk of a wavefront's 16 R weight rows is copied by
-//    direct-to-LDS loads into the wavefront's own 2 R KiB region, 8 rows x 128 B
-//    per instruction, the 16-byte pieces of row q stored at slot
-//    piece ^ (q & 7) so that the operand-layout reads below hit distinct banks;
-//    the next chunk's copy is issued as soon as this chunk's words are in
-//    registers, and each lane loads its 4 scale bytes per tile directly;
+//    direct-to-LDS loads (nontemporal) into the wavefront's own 2 R KiB
+//    region, 8 rows x 128 B per instruction, one chunk ahead;
+//  * every 4 chunks, the 64 scale bytes of each of those rows are copied the
+//    same way into a 64 R-byte-per-row region (the scale lines would otherwise
+//    be fetched 16 bytes at a time and evicted by the weight stream between
+//    uses);
 //  * the activation fragments of each MFMA step serve all R tiles.
-// Rows past N are copied from row N - 1 and never stored; MFMA columns past M
-// read row M - 1 of x and are never stored.
+// LDS rows are unpadded; 16-byte pieces are XOR-swizzled by row so that the
+// operand-layout reads hit distinct banks: weight piece q of row j at slot
+// q ^ (j & 7), x piece q of row m at q ^ (m & 7), scale piece q of row j at
+// q ^ ((j >> 1) & 3).  Rows past N are copied from row N - 1 and never
+// stored; MFMA columns past M read row M - 1 of x and are never stored.
 // ---------------------------------------------------------------------------
-constexpr int kPanelXBytes = 64 * (2 * 512 + 16);       // x panel: M * (2 pk + 16) bytes at most
+constexpr int kPanelXBytes = 64 * 1024;                 // x panel: M * 2 pk bytes at most
+constexpr int kScaleGroup = 4;                          // chunks per scale copy
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int MT, int NW, int kPanelR>
@@ -545,43 +551,53 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
                                                          const float* __restrict__ gs_ptr, int N,
                                                          const uint16_t* __restrict__ bias,
                                                          uint16_t* __restrict__ y, int pk) {
+  constexpr int kRows = 16 * kPanelR;                   // weight rows per wavefront
   __shared__ __attribute__((aligned(16))) uint8_t xp[kPanelXBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t wl[NW][kPanelR * 16 * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t wl[NW][kRows * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t sl[NW][kRows * 16 * kScaleGroup];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nchunks = K / kChunk, pchunks = pk / kChunk;
   const int npanels = (nchunks + pchunks - 1) / pchunks;
-  const int xpitch = 2 * pk + 16;
+  const int xpitch = 2 * pk;
   const int64_t prow = K >> 1, srow = K >> 4;
   const float gs = *gs_ptr;
-  const int nblocks = (N + 16 * NW * kPanelR - 1) / (16 * NW * kPanelR);
+  const int nblocks = (N + NW * kRows - 1) / (NW * kRows);
   // weight copy: lane fills slot lane & 7 of row 8 j + (lane >> 3), i.e. piece (lane & 7) ^ (lane >> 3)
   const int wpiece = (lane & 7) ^ (lane >> 3);
   // operand reads: row 16 t + r, pieces 2 g and 2 g + 1
   const int wrd0 = r * 128 + 16 * ((2 * g) ^ (r & 7)), wrd1 = r * 128 + 16 * ((2 * g + 1) ^ (r & 7));
+  // scale copy: lane fills slot lane & 3 of row 16 i + (lane >> 2), i.e. piece (lane & 3) ^ ((lane >> 3) & 3)
+  const int spiece = (lane & 3) ^ ((lane >> 3) & 3);
+  const int skey = (r >> 1) & 3;                        // scale swizzle of rows 16 t + r
   uint8_t* const wmine = wl[wave];
+  uint8_t* const smine = sl[wave];
 
   for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
-    const int n_wave = blk * (16 * NW * kPanelR) + wave * (16 * kPanelR);
+    const int n_wave = blk * (NW * kRows) + wave * kRows;
     auto w_copy = [&](int c) {
 #pragma unroll
-      for (int j = 0; j < 2 * kPanelR; ++j) {
+      for (int j = 0; j < kRows / 8; ++j) {
         const int64_t row = min(n_wave + 8 * j + (lane >> 3), N - 1);
         __builtin_amdgcn_global_load_lds((const void*)(packed + row * prow + 128 * c + 16 * wpiece),
-                                         (lds_ptr_t)(wmine + 1024 * j), 16, 0, 0);
+                                         (lds_ptr_t)(wmine + 1024 * j), 16, 0, kCachePolicyNT);
       }
     };
-    auto s_load = [&](int c, uint32_t (&sw)[kPanelR]) {
+    auto s_copy = [&](int grp) {                        // scales of chunks 4 grp .. 4 grp + 3
+      const int64_t off = min((int64_t)16 * (kScaleGroup * grp + spiece), srow - 16);   // past the row end: unused
 #pragma unroll
-      for (int t = 0; t < kPanelR; ++t)
-        sw[t] = *reinterpret_cast<const uint32_t*>(scales + (int64_t)min(n_wave + 16 * t + r, N - 1) * srow +
-                                                   16 * c + 4 * g);
+      for (int i = 0; i < kRows / 16; ++i) {
+        const int64_t row = min(n_wave + 16 * i + (lane >> 2), N - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(scales + row * srow + off),
+                                         (lds_ptr_t)(smine + 1024 * i), 16, 0, 0);
+      }
     };
     auto x_copy = [&](int p) {
       const int per_row = min(pk, K - p * pk) / 512;   // 1 KiB copies per row of this panel
       for (int i = wave; i < M * per_row; i += NW) {
         const int m = i / per_row, h = i - m * per_row;
-        __builtin_amdgcn_global_load_lds((const void*)(x + (int64_t)m * K + p * pk + 512 * h + 8 * lane),
+        const int piece = 64 * h + (lane ^ (m & 7));
+        __builtin_amdgcn_global_load_lds((const void*)(x + (int64_t)m * K + p * pk + 8 * piece),
                                          (lds_ptr_t)(xp + m * xpitch + 1024 * h), 16, 0, 0);
       }
     };
@@ -591,28 +607,32 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
     for (int t = 0; t < kPanelR; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int xrow[MT];                                       // LDS byte offsets of this lane's x rows
+    int xrow[MT], xkey[MT];                             // LDS row offsets and swizzle keys of this lane's x rows
 
-    // chunk c (local chunk cc of the panel): this chunk's weights are in wmine
-    // and its scale words in sw; the next chunk's copy and scales go to swn
-    auto chunk = [&](int c, int cc, const uint32_t (&sw)[kPanelR], uint32_t (&swn)[kPanelR]) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);            // this chunk's weight copy has landed
+    // chunk c (local chunk cc of the panel); its weights are in wmine and its
+    // scales in smine, both copied while the previous chunk computed
+    auto chunk = [&](int c, int cc) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);            // this chunk's copies have landed
       u32x4 wd[kPanelR][2];
+      uint32_t sw[kPanelR];
+      const int c4 = c % kScaleGroup;
 #pragma unroll
       for (int t = 0; t < kPanelR; ++t) {
         wd[t][0] = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + wrd0);
         wd[t][1] = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + wrd1);
+        sw[t] = *reinterpret_cast<const uint32_t*>(smine + 64 * (16 * t + r) + 16 * (c4 ^ skey) + 4 * g);
       }
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);          // the region may now be overwritten
-      const int cn = min(c + 1, nchunks - 1);
-      w_copy(cn);
-      s_load(cn, swn);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);          // the regions may now be overwritten
+      if (c + 1 < nchunks) {
+        w_copy(c + 1);
+        if (c4 == kScaleGroup - 1) s_copy((c + 1) / kScaleGroup);
+      }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         bf16x8 bx[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          bx[mt] = *reinterpret_cast<const bf16x8*>(xp + xrow[mt] + 2 * kChunk * cc + 16 * s);
+          bx[mt] = *reinterpret_cast<const bf16x8*>(xp + xrow[mt] + 512 * cc + 16 * (s ^ xkey[mt]));
 #pragma unroll
         for (int t = 0; t < kPanelR; ++t) {
           const float sv = (s >> 1) == 0 ? NVFP4_E4M3_TO_F32(sw[t], 0) : (s >> 1) == 1 ? NVFP4_E4M3_TO_F32(sw[t], 1)
@@ -624,9 +644,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
       }
     };
 
-    uint32_t swa[kPanelR], swb[kPanelR];
     w_copy(0);
-    s_load(0, swa);
+    s_copy(0);
     int c = 0;
     for (int p = 0; p < npanels; ++p) {
       __syncthreads();                                  // the previous panel's reads are done
@@ -634,21 +653,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();                                  // the panel is in LDS
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xrow[mt] = min(16 * mt + r, M - 1) * xpitch + 128 * g;
-      const int c1 = min(nchunks, c + pchunks);
-      const int c0 = c;
-      for (; c + 1 < c1; c += 2) {
-        chunk(c, c - c0, swa, swb);
-        chunk(c + 1, c + 1 - c0, swb, swa);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = min(16 * mt + r, M - 1);
+        xrow[mt] = m * xpitch + 128 * g;
+        xkey[mt] = m & 7;
       }
-      if (c < c1) {                                     // odd chunk count: keep the scale roles
-        chunk(c, c - c0, swa, swb);
-#pragma unroll
-        for (int t = 0; t < kPanelR; ++t) swa[t] = swb[t];
-        ++c;
-      }
+      const int c0 = c, c1 = min(nchunks, c + pchunks);
+      for (; c < c1; ++c) chunk(c, c - c0);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);               // the last (re-read) copy has landed
 
 #pragma unroll
     for (int t = 0; t < kPanelR; ++t) {
@@ -827,9 +839,9 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
 }
 
 // Panel width for gemv_panel_kernel: the widest multiple of 512 columns whose
-// M rows (plus 16 bytes of padding each) fit in the x panel region.
+// M rows fit in the x panel region.
 static int panel_columns(int M, int K) {
-  const int pk = ((kPanelXBytes / M - 16) / 2) / 512 * 512;
+  const int pk = (kPanelXBytes / M / 2) / 512 * 512;
   return std::min(pk, K);
 }
 
