@@ -52,7 +52,7 @@ def decode_kernel_name(m: int, k: int) -> str:
         return "gemv_dot_kernel"
     if k % 256 != 0:
         return "gemv_mfma_ragged_kernel"
-    if 3 <= m <= 16 and m * (2 * k + 16) + 8 * 16 * 144 + 64 <= 160 * 1024:
+    if 3 <= m <= 16 and m * (2 * k + 16) + 8 * 3072 + 64 <= 160 * 1024:
         return "gemv_xres_kernel"
     return "gemv_panel_kernel" if k % 512 == 0 else "gemv_mfma_kernel"
 

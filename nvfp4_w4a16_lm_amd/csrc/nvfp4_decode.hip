@@ -32,6 +32,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0) alone / lgkmcnt(0) alone
 constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
 constexpr int kCachePolicyNT = 2;   // cache-policy operand of direct-to-LDS loads: nontemporal
+constexpr int kScaleGroup = 4;      // chunks of scales per direct-to-LDS scale copy
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -387,10 +389,12 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
 // gemv_xres_kernel<NW>: 2 < M <= 16 with the whole activation resident in LDS
 // (M * (2K + 16) bytes; K % 256 == 0).  NW wavefronts per workgroup; x is
 // copied into LDS once, then every wavefront streams whole 16-row weight
-// tiles over all of K with no further synchronisation.  Weights arrive 8
-// lanes per 128-byte line and are transposed through a per-wavefront LDS
-// tile into the 16x16x32 operand layout, as in gemv_mfma_kernel.  MFMA
-// columns m >= M read row M - 1 of x and are never stored.
+// tiles over all of K with no further synchronisation.  Each 256-k chunk of
+// a tile's weights (and every 4 chunks its scales) is copied by
+// direct-to-LDS loads into the wavefront's own swizzled regions, one chunk
+// ahead (across tiles too), and read in the 16x16x32 operand layout, as in
+// gemv_panel_kernel.  MFMA columns m >= M read row M - 1 of x and are never
+// stored.
 //
 // The arithmetic is f16 MFMA with fp32 accumulation:
 //  * weights: code * s is exact in f16 (at most 6 significant bits, within
@@ -414,18 +418,23 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
                                                           const uint16_t* __restrict__ bias,
                                                           uint16_t* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int xpitch = 2 * K + 16;                    // bytes per x row (the pad spreads rows over banks)
   uint8_t* const xl = lds;
-  uint8_t (*const wl)[16][kWPitch] = reinterpret_cast<uint8_t (*)[16][kWPitch]>(lds + M * xpitch);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* const wmine = lds + M * xpitch + 2048 * wave;               // 16 rows x 128 B of weights
+  uint8_t* const smine = lds + M * xpitch + 2048 * NW + 1024 * wave;   // 16 rows x 64 B of scales
+  float* const xup = reinterpret_cast<float*>(lds + M * xpitch + 3072 * NW);   // 2^p_m
   const int r = lane & 15, g = lane >> 4;
-  const int lr = lane >> 3, lq = lane & 7;          // loader: row within 8, 16-byte piece of the line
   const int nchunks = K / kChunk;
   const int64_t prow = K >> 1, srow = K >> 4;
+  // copies: weight piece (lane & 7) ^ (lane >> 3) of row 8 j + (lane >> 3); scale piece
+  // (lane & 3) ^ ((lane >> 3) & 3) of row lane >> 2 (the swizzles of gemv_panel_kernel)
+  const int wpiece = (lane & 7) ^ (lane >> 3), spiece = (lane & 3) ^ ((lane >> 3) & 3);
+  const int wrd0 = r * 128 + 16 * ((2 * g) ^ (r & 7)), wrd1 = r * 128 + 16 * ((2 * g + 1) ^ (r & 7));
+  const int srd = r * 64 + 4 * g, skey = (r >> 1) & 3;
 
   // x -> f16 rows in LDS: wavefront w handles rows w, w + NW, ...: the row's
   // largest |x| (bf16 magnitudes compare as integers), then x * 2^-p_m
-  float* const xup = reinterpret_cast<float*>(lds + M * xpitch + NW * 16 * kWPitch);   // 2^p_m
   const int xvec = K / 8;                           // 16-byte vectors per x row
   for (int m = wave; m < M; m += NW) {
     const uint16_t* xr = x + (int64_t)m * K;
@@ -458,24 +467,41 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   const uint8_t* const xrow = xl + min(r, M - 1) * xpitch + 128 * g;   // this lane's k-group, chunk 0
 
   const int ntiles = (N + 15) / 16;
-  for (int tile = blockIdx.x * NW + wave; tile < ntiles; tile += gridDim.x * NW) {
+  const int stride = gridDim.x * NW;
+  auto w_copy = [&](int tile, int c) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t row = min(16 * tile + 8 * j + (lane >> 3), N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(packed + row * prow + 128 * c + 16 * wpiece),
+                                       (lds_ptr_t)(wmine + 1024 * j), 16, 0, kCachePolicyNT);
+    }
+  };
+  auto s_copy = [&](int tile, int grp) {
+    const int64_t row = min(16 * tile + (lane >> 2), N - 1);
+    const int64_t off = min((int64_t)16 * (kScaleGroup * grp + spiece), srow - 16);   // past the row end: unused
+    __builtin_amdgcn_global_load_lds((const void*)(scales + row * srow + off), (lds_ptr_t)smine, 16, 0, 0);
+  };
+  int tile = blockIdx.x * NW + wave;
+  if (tile < ntiles) {
+    w_copy(tile, 0);
+    s_copy(tile, 0);
+  }
+  for (; tile < ntiles; tile += stride) {
     const int n_base = tile * 16;
-    const uint8_t* lp[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) lp[j] = packed + (int64_t)min(n_base + 8 * j + lr, N - 1) * prow + 16 * lq;
-    const uint8_t* const lsc = scales + (int64_t)min(n_base + r, N - 1) * srow + 4 * g;
-    auto load_w = [&](int c, WChunk<1>& wc) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) wc.w[0][j] = load_stream16(lp[j] + 128 * c);
-      wc.s[0] = *reinterpret_cast<const uint32_t*>(lsc + 16 * c);
-    };
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto chunk = [&](int c, const WChunk<1>& wc) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&wl[wave][8 * j + lr][16 * lq]) = wc.w[0][j];
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(&wl[wave][r][32 * g]);
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(&wl[wave][r][32 * g + 16]);
-      const uint32_t sw = wc.s[0];
+    for (int c = 0; c < nchunks; ++c) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this chunk's copies have landed
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wmine + wrd0);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(wmine + wrd1);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * ((c % kScaleGroup) ^ skey));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // the regions may now be overwritten
+      if (c + 1 < nchunks) {                          // next chunk, or the next tile's first one
+        w_copy(tile, c + 1);
+        if ((c + 1) % kScaleGroup == 0) s_copy(tile, (c + 1) / kScaleGroup);
+      } else if (tile + stride < ntiles) {
+        w_copy(tile + stride, 0);
+        s_copy(tile + stride, 0);
+      }
       float e2[4];
       f16x2 mu[4];
 #pragma unroll
@@ -491,15 +517,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
         const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
         acc = mfma16x16x32_f16(dequant8_f16(wd[s], e2[s >> 1], mu[s >> 1]), bx, acc);
       }
-    };
-    WChunk<1> wa, wb;
-    load_w(0, wa);
-    for (int c = 0; c < nchunks; c += 2) {
-      if (c + 1 < nchunks) load_w(c + 1, wb);
-      chunk(c, wa);
-      if (c + 1 >= nchunks) break;
-      if (c + 2 < nchunks) load_w(c + 2, wa);
-      chunk(c + 1, wb);
     }
     if (r < M) {
       acc *= up;
@@ -541,8 +558,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
 // stored; MFMA columns past M read row M - 1 of x and are never stored.
 // ---------------------------------------------------------------------------
 constexpr int kPanelXBytes = 64 * 1024;                 // x panel: M * 2 pk bytes at most
-constexpr int kScaleGroup = 4;                          // chunks per scale copy
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int MT, int NW, int kPanelR>
 __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __restrict__ x, int M, int K,
@@ -809,9 +824,9 @@ static hipError_t mfma_launch(const void* x, int M, int K, const uint8_t* packed
 // VGPRs per activation row), so it takes M = 1 up to K = 8192 and M = 2 up to
 // K = 4096; everything else goes to the MFMA kernel.
 // Dynamic LDS of gemv_xres_kernel<NW> for (M, K): x rows, NW per-wavefront
-// weight tiles, 16 row scales.
+// weight (2 KiB) and scale (1 KiB) regions, 16 row scales.
 static int64_t xres_lds_bytes(int64_t M, int64_t K, int nw) {
-  return M * (2 * K + 16) + (int64_t)nw * 16 * kWPitch + 16 * sizeof(float);
+  return M * (2 * K + 16) + (int64_t)nw * 3072 + 16 * sizeof(float);
 }
 
 template <int NW>
