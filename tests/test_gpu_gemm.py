@@ -151,10 +151,15 @@ def test_gpu_quantized_buffers_match_oracle_buffers_in_gemm():
     assert np.array_equal(y_oracle_buf, y_gpu_buf)
 
 
-def test_decode_activation_rows_of_extreme_magnitude():
+@pytest.mark.parametrize("m,k", [(8, 1024), (40, 1024), (16, 8192)])
+def test_decode_activation_rows_of_extreme_magnitude(m, k):
     """Decode rows whose magnitudes span the bf16 range: zeros, ~2^100, ~2^-100,
-    a mix of 2^20 and 2^-20 within one row, one huge element among tiny ones."""
-    n, k, m = 1027, 1024, 8
+    a mix of 2^20 and 2^-20 within one row, one huge element among tiny ones,
+    and rows whose largest elements come only in the last (or only in the
+    first) columns.  M = 8 keeps x resident in LDS (f16 products with a
+    per-row exponent); M = 40 (two 512-column panels) and M = 16 at K = 8192
+    (four 2048-column panels) take the panel kernel."""
+    n = 1027
     _, packed, scales, gs, q = setup(n, k, seed=12)
     rng = np.random.default_rng(13)
     xf = rng.standard_normal((m, k)).astype(np.float32)
@@ -164,6 +169,10 @@ def test_decode_activation_rows_of_extreme_magnitude():
     xf[3] *= np.where(rng.random(k) < 0.5, np.float32(2.0 ** 20), np.float32(2.0 ** -20))
     xf[4] *= np.float32(2.0 ** -60)
     xf[4, 17] = np.float32(3.0e4)
+    xf[5, : k - 64] *= np.float32(2.0 ** -40)
+    xf[5, k - 64:] *= np.float32(2.0 ** 40)
+    xf[6, :64] *= np.float32(2.0 ** 40)
+    xf[6, 64:] *= np.float32(2.0 ** -40)
     x = torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     y = gemm_gpu(x, q)
     assert not np.any(y[0] & 0x7FFF), "zero row must give zero logits"
