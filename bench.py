@@ -214,11 +214,37 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
 
     avg_ms = {op: float(np.mean([a.elapsed_time(b) for a, b in ev[op]])) for op in ops}
+
+    # Pre-quantized checkpoint import (not part of the step): global scale from
+    # the partition scales + one NaN scan of the block scales, timed the same way.
+    ps = Q[0][2].reshape(1).clone()
+    gsi = torch.empty((), dtype=torch.float32, device=dev)
+    flg = torch.empty((), dtype=torch.int32, device=dev)
+    for i in range(args.warmup):
+        B.nvfp4_import_checkpoint(ps, Q[i % copies][1], k, "modelopt", gsi, flg)
+    torch.cuda.synchronize()
+    imp_ev = []
+    for i in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.nvfp4_import_checkpoint(ps, Q[i % copies][1], k, "modelopt", gsi, flg)
+        b.record()
+        imp_ev.append((a, b))
+    torch.cuda.synchronize()
+    if int(flg.item()) != 0:
+        raise RuntimeError(f"checkpoint import flags {int(flg.item())} on freshly quantized scales")
+    imp_ms = float(np.mean([a.elapsed_time(b) for a, b in imp_ev]))
+    imp_bytes = n * k / 16 + 4 + 8
+
     step_bytes = quant_bytes(n, k) + sum(gemm_bytes(m, n, k) for m in ms)
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
 
     per_op = {"quantize": {"ms": avg_ms["quantize"],
                            "GB/s": quant_bytes(n, k) / (avg_ms["quantize"] * 1e-3) / 1e9}}
+    per_op["import_checkpoint"] = {"ms": imp_ms, "GB/s": imp_bytes / (imp_ms * 1e-3) / 1e9,
+                                   "kernels": "import_prepare (1 wavefront) + scale_nan_scan",
+                                   "in_step": False}
     for m in ms:
         t = avg_ms[f"gemm_m{m}"] * 1e-3
         per_op[f"gemm_m{m}"] = {"ms": avg_ms[f"gemm_m{m}"],

@@ -3,7 +3,9 @@
  *
  * Three calls: quantize a bf16 lm_head weight to NVFP4, re-quantize it in
  * place into the same buffers, and compute logits from the quantized weight
- * with bf16 activations.  Everything runs in hand-written HIP kernels.
+ * with bf16 activations.  Two more adopt a pre-quantized NVFP4 checkpoint
+ * (ModelOpt or compressed-tensors) for the same GEMM.  Everything runs in
+ * hand-written HIP kernels.
  *
  * The method is the one the vLLM API docs describe for
  * vllm.model_executor.layers.quantization.online.lm_head (function
@@ -24,7 +26,9 @@
  *    a HIP error raised while enqueueing (see nvfp4_last_hip_error()).
  *  - Device faults surface as HIP errors at the caller's next synchronisation.
  *  - Alignment: W, x and y must be 16-byte aligned; packed 16-byte aligned;
- *    scales 4-byte aligned; global_scale 4-byte aligned; bias 2-byte aligned.
+ *    scales 4-byte aligned (16-byte for the two checkpoint calls);
+ *    global_scale, flags and partition scales 4-byte aligned; bias 2-byte
+ *    aligned.
  *  - Outputs may not overlap inputs or each other (NVFP4_ERR_ALIAS).
  *  - Non-finite weights are outside the contract (results unspecified).
  */
@@ -43,7 +47,8 @@ typedef enum {
   NVFP4_ERR_SHAPE = 2,  /* N < 1, K < 16, K % 16 != 0, M < 0, or a size too large       */
   NVFP4_ERR_ALIGN = 3,  /* a pointer breaks the alignment rules above                   */
   NVFP4_ERR_ALIAS = 4,  /* an output byte range overlaps an input or another output     */
-  NVFP4_ERR_LAUNCH = 5  /* HIP reported an error while enqueueing                        */
+  NVFP4_ERR_LAUNCH = 5, /* HIP reported an error while enqueueing                        */
+  NVFP4_ERR_ARG = 6     /* an enumerated argument (e.g. a scale convention) is out of range */
 } nvfp4_status;
 
 /* Group size along K: one E4M3 scale per 16 consecutive weights of a row
@@ -117,6 +122,70 @@ nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t M, int64_t K,
                               const uint8_t* packed, const uint8_t* scales,
                               const float* global_scale, int64_t N,
                               const void* bias, void* y, void* stream);
+
+/*
+ * Pre-quantized checkpoints.
+ * (vLLM modelopt.py, class KNvfp4Static, create_weights and process; vLLM API
+ * docs, compressed_tensors.schemes, class CompressedTensorsW4A16Fp4,
+ * create_weights and process_weights_after_loading.)
+ *
+ * Both formats store the packed codes as uint8 [N, K/2] and the block scales
+ * as float8_e4m3fn [N, K/16] exactly as nvfp4_quantize writes them, so
+ * nvfp4_w4a16_gemm reads them as loaded.  They differ in the per-partition
+ * global scale (one float per fused output partition, e.g. 1 for lm_head):
+ */
+typedef enum {
+  /* weight_scale_2 = amax / 2688 (the dequantization direction); the global
+   * scale is the largest of them, used as is */
+  NVFP4_SCALE2_MODELOPT = 0,
+  /* weight_global_scale = 2688 / amax, stored inverted; the global scale is
+   * 1 / (the largest of them), one IEEE float32 division */
+  NVFP4_SCALE2_COMPRESSED_TENSORS = 1
+} nvfp4_scale2_convention;
+
+/* Bits of the flags word nvfp4_import_checkpoint writes. */
+#define NVFP4_IMPORT_SCALES_NOT_LOADED 1u   /* a block scale is an e4m3fn NaN (0x7F or 0xFF)      */
+#define NVFP4_IMPORT_PARTITIONS_DIFFER 2u   /* the partition scales are not all equal (IEEE ==),   */
+                                            /* which costs accuracy: one global scale serves all   */
+#define NVFP4_IMPORT_BAD_GLOBAL_SCALE  4u   /* the global scale is not a finite number > 0         */
+
+/*
+ * nvfp4_fill_scale_sentinel -- mark a block-scale buffer as not loaded.
+ *
+ *   scales  out  float8_e4m3fn bytes [N, K/16], 16-byte aligned; every byte is
+ *                set to 0x7F (an e4m3fn NaN), the sentinel KNvfp4Static
+ *                creates its weight_scale with
+ *   N, K    in   the weight's shape (rules of nvfp4_quantize)
+ *
+ * Call it on a freshly allocated buffer before the checkpoint loader fills
+ * it, so that nvfp4_import_checkpoint can tell which scales were never loaded.
+ */
+nvfp4_status nvfp4_fill_scale_sentinel(uint8_t* scales, int64_t N, int64_t K, void* stream);
+
+/*
+ * nvfp4_import_checkpoint -- the GEMM's global scale from a checkpoint, and a
+ * check of its block scales.
+ *
+ *   partition_scales in  float [num_partitions], 4-byte aligned: the stored
+ *                        per-partition global scales, in `convention`
+ *   num_partitions   in  1 .. 2^20
+ *   convention       in  an nvfp4_scale2_convention (else NVFP4_ERR_ARG)
+ *   scales           in  float8_e4m3fn bytes [N, K/16] as loaded, 16-byte aligned
+ *   N, K             in  the weight's shape (rules of nvfp4_quantize)
+ *   global_scale     out 1 float: what nvfp4_w4a16_gemm takes as global_scale
+ *                        (a NaN result is written as the quiet NaN 0x7FC00000)
+ *   flags            out 1 uint32: NVFP4_IMPORT_* bits
+ *
+ * The library only reports: a caller that follows KNvfp4Static rejects the
+ * tensor when NVFP4_IMPORT_SCALES_NOT_LOADED is set and warns on
+ * NVFP4_IMPORT_PARTITIONS_DIFFER.  Both outputs are valid once the stream
+ * reaches the end of the call; no output may overlap an input or the other
+ * output.  The partition scales are read once, the block scales once
+ * (N*K/16 bytes).
+ */
+nvfp4_status nvfp4_import_checkpoint(const float* partition_scales, int64_t num_partitions, int convention,
+                                     const uint8_t* scales, int64_t N, int64_t K, float* global_scale,
+                                     uint32_t* flags, void* stream);
 
 /* Host-side helpers (no device work). */
 const char* nvfp4_status_string(int status);   /* static string for a status code        */

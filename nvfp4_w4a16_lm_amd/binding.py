@@ -14,7 +14,7 @@ import os
 import torch
 
 LIB_NAME = "libnvfp4_w4a16.so"
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS_NAMES = {
     0: "NVFP4_OK",
@@ -23,10 +23,20 @@ STATUS_NAMES = {
     3: "NVFP4_ERR_ALIGN",
     4: "NVFP4_ERR_ALIAS",
     5: "NVFP4_ERR_LAUNCH",
+    6: "NVFP4_ERR_ARG",
 }
+
+#: Scale conventions of nvfp4_import_checkpoint (nvfp4_scale2_convention).
+SCALE2_CONVENTIONS = {"modelopt": 0, "compressed-tensors": 1}
+
+#: Flag bits written by nvfp4_import_checkpoint.
+IMPORT_SCALES_NOT_LOADED = 1
+IMPORT_PARTITIONS_DIFFER = 2
+IMPORT_BAD_GLOBAL_SCALE = 4
 
 #: Entry points declared in include/nvfp4_w4a16.h.
 EXPORTED = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
+            "nvfp4_fill_scale_sentinel", "nvfp4_import_checkpoint",
             "nvfp4_status_string", "nvfp4_last_hip_error", "nvfp4_abi_version")
 
 
@@ -66,6 +76,10 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.nvfp4_w4a16_gemm.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, vp, vp]
     lib.nvfp4_w4a16_gemm.restype = ctypes.c_int
+    lib.nvfp4_fill_scale_sentinel.argtypes = [vp, i64, i64, vp]
+    lib.nvfp4_fill_scale_sentinel.restype = ctypes.c_int
+    lib.nvfp4_import_checkpoint.argtypes = [vp, i64, ctypes.c_int, vp, i64, i64, vp, vp, vp]
+    lib.nvfp4_import_checkpoint.restype = ctypes.c_int
     lib.nvfp4_status_string.argtypes = [ctypes.c_int]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_last_hip_error.argtypes = []
@@ -171,3 +185,64 @@ def nvfp4_w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
            lib.nvfp4_w4a16_gemm(_ptr(x), m, k, _ptr(packed), _ptr(scales), _ptr(global_scale), n,
                                 _ptr(bias), _ptr(out), _stream_of(x, stream)))
     return out
+
+
+class NVFP4NotLoadedError(RuntimeError):
+    """Block scales still hold the NaN sentinel: the checkpoint never wrote them."""
+
+
+def nvfp4_fill_scale_sentinel(scales: torch.Tensor, k: int, stream=None) -> None:
+    """Fill a [N, K/16] block-scale buffer with the e4m3fn NaN sentinel 0x7F."""
+    if scales.dim() != 2 or scales.shape[1] * 16 != k:
+        raise ValueError(f"scales shape {tuple(scales.shape)} does not match K={k}")
+    n = scales.shape[0]
+    _check_out(scales, (n, k // 16), (torch.float8_e4m3fn, torch.uint8), scales.device, "scales")
+    lib = load_library()
+    _check("nvfp4_fill_scale_sentinel",
+           lib.nvfp4_fill_scale_sentinel(_ptr(scales), n, k, _stream_of(scales, stream)))
+
+
+def nvfp4_import_checkpoint(partition_scales: torch.Tensor, scales: torch.Tensor, k: int,
+                            convention: str, global_scale: torch.Tensor | None = None,
+                            flags: torch.Tensor | None = None, stream=None):
+    """Global scale (fp32 []) and flags (int32 [], NVFP4_IMPORT_* bits) of a
+    pre-quantized checkpoint; both are device tensors, valid in stream order."""
+    if convention not in SCALE2_CONVENTIONS:
+        raise ValueError(f"convention must be one of {sorted(SCALE2_CONVENTIONS)}, got {convention!r}")
+    if scales.dim() != 2 or scales.shape[1] * 16 != k:
+        raise ValueError(f"scales shape {tuple(scales.shape)} does not match K={k}")
+    n = scales.shape[0]
+    dev = scales.device
+    _check_out(scales, (n, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, "scales")
+    ps = partition_scales.reshape(-1)
+    if ps.dtype != torch.float32 or ps.device != dev or not ps.is_contiguous():
+        raise ValueError("partition_scales must be contiguous float32 on the scales' device")
+    if global_scale is None:
+        global_scale = torch.empty((), dtype=torch.float32, device=dev)
+    if flags is None:
+        flags = torch.empty((), dtype=torch.int32, device=dev)
+    if global_scale.numel() != 1 or global_scale.dtype != torch.float32 or global_scale.device != dev:
+        raise ValueError("global_scale must be one float32 on the scales' device")
+    if flags.numel() != 1 or flags.dtype != torch.int32 or flags.device != dev:
+        raise ValueError("flags must be one int32 on the scales' device")
+    lib = load_library()
+    _check("nvfp4_import_checkpoint",
+           lib.nvfp4_import_checkpoint(_ptr(ps), ps.numel(), SCALE2_CONVENTIONS[convention], _ptr(scales),
+                                       n, k, _ptr(global_scale), _ptr(flags), _stream_of(scales, stream)))
+    return global_scale, flags
+
+
+def check_import_flags(flags: torch.Tensor, what: str = "lm_head") -> int:
+    """Host-side reaction to the flags, as the checkpoint loaders react
+    (synchronises): raise when block scales were never loaded or the global
+    scale is unusable; warn when partitions had different global scales."""
+    f = int(flags.item())
+    if f & IMPORT_SCALES_NOT_LOADED:
+        raise NVFP4NotLoadedError(f"NVFP4 block scales of {what} were never loaded (still NaN)")
+    if f & IMPORT_BAD_GLOBAL_SCALE:
+        raise NVFP4NotLoadedError(f"NVFP4 global scale of {what} is not a finite positive number")
+    if f & IMPORT_PARTITIONS_DIFFER:
+        import warnings
+        warnings.warn(f"NVFP4 global scales differ across the fused partitions of {what}; "
+                      "one (the largest) serves all of them, which may reduce accuracy")
+    return f

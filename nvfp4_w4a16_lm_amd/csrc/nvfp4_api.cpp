@@ -15,6 +15,7 @@ thread_local char g_last_hip_error[256] = "";
 constexpr int64_t kMaxDim = (int64_t)1 << 30;        // per-dimension bound (int32 kernel indexing)
 constexpr int64_t kMaxElems = (int64_t)1 << 40;      // N*K bound (64-bit flat offsets)
 constexpr int64_t kMaxPrefillM = (int64_t)65535 * 128;  // grid.y limit of the prefill kernel
+constexpr int64_t kMaxPartitions = (int64_t)1 << 20;     // partition scales per checkpoint tensor
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -104,20 +105,51 @@ nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t M, int64_t K, const uint8_t
   return finish(nvfp4::launch_gemm_prefill(x, M, K, packed, scales, global_scale, N, bias, y, st));
 }
 
+nvfp4_status nvfp4_import_checkpoint(const float* partition_scales, int64_t num_partitions, int convention,
+                                     const uint8_t* scales, int64_t N, int64_t K, float* global_scale,
+                                     uint32_t* flags, void* stream) {
+  if (!partition_scales || !scales || !global_scale || !flags) return NVFP4_ERR_NULL;
+  if (convention != NVFP4_SCALE2_MODELOPT && convention != NVFP4_SCALE2_COMPRESSED_TENSORS) return NVFP4_ERR_ARG;
+  nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (num_partitions < 1 || num_partitions > kMaxPartitions) return NVFP4_ERR_SHAPE;
+  if (!aligned(partition_scales, 4) || !aligned(scales, 16) || !aligned(global_scale, 4) || !aligned(flags, 4))
+    return NVFP4_ERR_ALIGN;
+  const Range rp = span(partition_scales, num_partitions * 4), rs = span(scales, N * K / 16),
+              rg = span(global_scale, 4), rf = span(flags, 4);
+  if (overlap(rg, rp) || overlap(rg, rs) || overlap(rf, rp) || overlap(rf, rs) || overlap(rg, rf))
+    return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_import(partition_scales, num_partitions, convention, scales, N * K / 16,
+                                     global_scale, flags, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_fill_scale_sentinel(uint8_t* scales, int64_t N, int64_t K, void* stream) {
+  if (!scales) return NVFP4_ERR_NULL;
+  const nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (!aligned(scales, 16)) return NVFP4_ERR_ALIGN;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_fill_sentinel(scales, N * K / 16, (hipStream_t)stream));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_NULL: return "a required pointer is NULL";
     case NVFP4_ERR_SHAPE: return "invalid shape (need N >= 1, K >= 16, K % 16 == 0, M >= 0, sizes in range)";
-    case NVFP4_ERR_ALIGN: return "misaligned pointer (W, x, y, packed: 16 B; scales, global_scale: 4 B; bias: 2 B)";
+    case NVFP4_ERR_ALIGN:
+      return "misaligned pointer (W, x, y, packed: 16 B; scales: 4 B, 16 B for the import calls; "
+             "global_scale, flags, partition scales: 4 B; bias: 2 B)";
     case NVFP4_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case NVFP4_ERR_LAUNCH: return "HIP error while enqueueing (see nvfp4_last_hip_error)";
+    case NVFP4_ERR_ARG: return "an enumerated argument is out of range";
     default: return "unknown status";
   }
 }
 
 const char* nvfp4_last_hip_error(void) { return g_last_hip_error; }
 
-int nvfp4_abi_version(void) { return 1; }
+int nvfp4_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -29,4 +29,12 @@ hipError_t launch_gemm_prefill(const void* x, int64_t M, int64_t K, const uint8_
 
 constexpr int64_t kDecodeMaxM = 64;
 
+// Checkpoint import: collapse the partition scales into the global scale and
+// write the flags word, then scan the nbytes block-scale bytes for NaN.
+hipError_t launch_import(const float* partition_scales, int64_t P, int convention, const uint8_t* scales,
+                         int64_t nbytes, float* global_scale, uint32_t* flags, hipStream_t stream);
+
+// Fill nbytes block-scale bytes with the e4m3fn NaN sentinel 0x7F.
+hipError_t launch_fill_sentinel(uint8_t* scales, int64_t nbytes, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -92,7 +92,7 @@ def collapse_global_scale(partition_scales: np.ndarray, convention: str) -> np.f
     if convention == MODELOPT:
         return np.float32(m)
     if convention == COMPRESSED_TENSORS:
-        with np.errstate(divide="ignore", invalid="ignore"):
+        with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
             return np.float32(np.float32(1.0) / m)
     raise ValueError(f"unknown convention {convention!r}")
 

@@ -18,7 +18,7 @@ from nvfp4_w4a16_lm_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4_w4a16.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS = 0, 1, 2, 3, 4
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_ARG = 0, 1, 2, 3, 4, 6
 
 # Fake, well-separated, 256-byte aligned addresses: only compared, never touched.
 W, P, S, G, X, Y, B = (0x10000000 * (i + 1) for i in range(7))
@@ -37,9 +37,10 @@ def lib():
     return binding.load_library()
 
 
-def test_header_declares_the_three_calls():
+def test_header_declares_the_three_calls_and_the_checkpoint_calls():
     fns = declared_functions()
-    for name in ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm"):
+    for name in ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
+                 "nvfp4_fill_scale_sentinel", "nvfp4_import_checkpoint"):
         assert name in fns
     assert set(fns) == set(binding.EXPORTED)
 
@@ -55,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.nvfp4_abi_version() == binding.ABI_VERSION
-    for st in range(6):
+    for st in range(7):
         assert lib.nvfp4_status_string(st).decode()
     assert lib.nvfp4_status_string(99).decode() == "unknown status"
     assert lib.nvfp4_last_hip_error().decode() == ""
@@ -116,6 +117,37 @@ def test_gemm_validation(lib):
     assert gm(lib, m=0) == OK
     assert gm(lib, m=0, x=0, y=0) == OK
     assert gm(lib, m=1, x=0) == ERR_NULL
+
+
+def imp(lib, ps=P, np_=3, conv=0, s=S, n=1024, k=512, g=G, f=B):
+    return lib.nvfp4_import_checkpoint(ps, np_, conv, s, n, k, g, f, None)
+
+
+def test_import_checkpoint_validation(lib):
+    assert imp(lib, ps=0) == ERR_NULL
+    assert imp(lib, s=0) == ERR_NULL
+    assert imp(lib, g=0) == ERR_NULL
+    assert imp(lib, f=0) == ERR_NULL
+    assert imp(lib, conv=2) == ERR_ARG
+    assert imp(lib, conv=-1) == ERR_ARG
+    for np_, n, k in [(0, 1024, 512), (-1, 1024, 512), ((1 << 20) + 1, 1024, 512), (3, 0, 512), (3, 1024, 40)]:
+        assert imp(lib, np_=np_, n=n, k=k) == ERR_SHAPE, (np_, n, k)
+    assert imp(lib, ps=P + 2) == ERR_ALIGN
+    assert imp(lib, s=S + 4) == ERR_ALIGN       # the scan reads 16-byte vectors
+    assert imp(lib, g=G + 1) == ERR_ALIGN
+    assert imp(lib, f=B + 2) == ERR_ALIGN
+    assert imp(lib, g=S + 1024) == ERR_ALIAS
+    assert imp(lib, f=P + 8) == ERR_ALIAS
+    assert imp(lib, g=G, f=G) == ERR_ALIAS
+    assert lib.nvfp4_fill_scale_sentinel(0, 1024, 512, None) == ERR_NULL
+    assert lib.nvfp4_fill_scale_sentinel(S, 1024, 40, None) == ERR_SHAPE
+    assert lib.nvfp4_fill_scale_sentinel(S + 4, 1024, 512, None) == ERR_ALIGN
+
+
+def test_binding_import_rejects_unknown_convention():
+    import torch
+    with pytest.raises(ValueError):
+        binding.nvfp4_import_checkpoint(torch.ones(1), torch.zeros(4, 2, dtype=torch.uint8), 32, "gguf")
 
 
 def test_binding_maps_shape_errors_to_valueerror(lib):
