@@ -237,6 +237,39 @@ def main() -> int:
     imp_ms = float(np.mean([a.elapsed_time(b) for a, b in imp_ev]))
     imp_bytes = n * k / 16 + 4 + 8
 
+    # The FP8 copy (not part of the step): row-wise E4M3 quantization of the
+    # weight, then per M the per-token activation quantization + FP8 GEMM.
+    fq, fs = B.nvfp4_fp8_quantize_rows(W)
+    xq8 = {m: B.nvfp4_fp8_quantize_rows(xs[m]) for m in ms}
+    y8 = {m: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for m in ms}
+    fp8_ev = {"fp8_quantize_w": []} | {f"fp8_linear_m{m}": [] for m in ms}
+
+    def fp8_step(record: bool):
+        e0 = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            e0.record()
+        B.nvfp4_fp8_quantize_rows(W, fq, fs)
+        for m in ms:
+            if record:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record()
+                fp8_ev["fp8_quantize_w" if m == ms[0] else f"fp8_linear_m{prev}"].append((e0, e1))
+                e0 = e1
+            B.nvfp4_fp8_quantize_rows(xs[m], *xq8[m])
+            B.nvfp4_fp8_gemm(*xq8[m], fq, fs, out=y8[m])
+            prev = m
+        if record:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record()
+            fp8_ev[f"fp8_linear_m{prev}"].append((e0, e1))
+
+    for _ in range(args.warmup):
+        fp8_step(False)
+    for _ in range(args.steps):
+        fp8_step(True)
+    torch.cuda.synchronize()
+    fp8_ms = {op: float(np.mean([a.elapsed_time(b) for a, b in v])) for op, v in fp8_ev.items()}
+
     step_bytes = quant_bytes(n, k) + sum(gemm_bytes(m, n, k) for m in ms)
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
 
@@ -245,6 +278,16 @@ def main() -> int:
     per_op["import_checkpoint"] = {"ms": imp_ms, "GB/s": imp_bytes / (imp_ms * 1e-3) / 1e9,
                                    "kernels": "import_prepare (1 wavefront) + scale_nan_scan",
                                    "in_step": False}
+    per_op["fp8_quantize_w"] = {"ms": fp8_ms["fp8_quantize_w"],
+                                "GB/s": (n * k * 3 + 4 * n) / (fp8_ms["fp8_quantize_w"] * 1e-3) / 1e9,
+                                "kernels": "fp8_quant_rows (bf16 weight -> e4m3 + per-row scales)",
+                                "in_step": False}
+    for m in ms:
+        t8 = fp8_ms[f"fp8_linear_m{m}"] * 1e-3
+        per_op[f"fp8_linear_m{m}"] = {"ms": fp8_ms[f"fp8_linear_m{m}"],
+                                      "TB/s": (n * k + 4 * n + 3 * m * k + 4 * m + 2 * m * n) / t8 / 1e12,
+                                      "TFLOP/s": gemm_flops(m, n, k) / t8 / 1e12,
+                                      "kernels": "fp8_quant_rows (per token) + fp8_gemm", "in_step": False}
     for m in ms:
         t = avg_ms[f"gemm_m{m}"] * 1e-3
         per_op[f"gemm_m{m}"] = {"ms": avg_ms[f"gemm_m{m}"],

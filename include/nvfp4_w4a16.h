@@ -187,6 +187,46 @@ nvfp4_status nvfp4_import_checkpoint(const float* partition_scales, int64_t num_
                                      const uint8_t* scales, int64_t N, int64_t K, float* global_scale,
                                      uint32_t* flags, void* stream);
 
+/*
+ * The FP8 lm_head copy.
+ * (vLLM API docs, quantization.online.lm_head, quantized_lm_head_copy: the
+ * "fp8" copy uses per-row weight scales and per-token activation scales on
+ * an FP8 linear kernel; vLLM modelopt.py, KFp8StaticChannel and the
+ * FP8_PER_CHANNEL_PER_TOKEN recipe; vLLM API docs, compressed_tensors.schemes,
+ * the W8A8 FP8 apply_weights path.)
+ *
+ * nvfp4_fp8_quantize_rows -- row-wise E4M3 quantization of a bf16 matrix;
+ * quantizes the weight once (one scale per output row) and the activations
+ * at every call (one scale per token).
+ *
+ *   A           in   bf16 [R, K], 16-byte aligned (R >= 1, K >= 16, K % 16 == 0)
+ *   q           out  float8_e4m3fn bytes [R, K], 16-byte aligned
+ *   row_scales  out  float [R]
+ *
+ *   s[r] = max(max_k |A[r,k]| / 448, 1e-12)     (float32, one IEEE division)
+ *   q[r,k] = e4m3_rne(clamp(A[r,k] * (1 / s[r]), -448, 448)), sign kept
+ *
+ * The pages do not show the quantizer's arithmetic; this is the plainest
+ * reading (the clamp mirrors the NVFP4 global scale's).
+ */
+nvfp4_status nvfp4_fp8_quantize_rows(const void* A, int64_t R, int64_t K, uint8_t* q, float* row_scales,
+                                     void* stream);
+
+/*
+ * nvfp4_fp8_gemm -- logits from the FP8 copy.
+ *
+ *   xq, x_scales in  float8_e4m3fn [M, K] and float [M] from nvfp4_fp8_quantize_rows (M >= 0;
+ *                    M == 0 enqueues nothing, and xq, x_scales and y may then be NULL)
+ *   wq, w_scales in  float8_e4m3fn [N, K] and float [N], likewise
+ *   bias         in  bf16 [N] or NULL
+ *   y            out bf16 [M, N], 16-byte aligned
+ *
+ *   y[m, n] = bf16_rne(x_scales[m] * w_scales[n] * sum_k e4m3(xq[m,k]) * e4m3(wq[n,k]) + bias[n])
+ * with float32 accumulation of exact float32 products.
+ */
+nvfp4_status nvfp4_fp8_gemm(const uint8_t* xq, const float* x_scales, int64_t M, int64_t K, const uint8_t* wq,
+                            const float* w_scales, int64_t N, const void* bias, void* y, void* stream);
+
 /* Host-side helpers (no device work). */
 const char* nvfp4_status_string(int status);   /* static string for a status code        */
 const char* nvfp4_last_hip_error(void);        /* last HIP error text of this thread, or "" */

@@ -37,6 +37,7 @@ IMPORT_BAD_GLOBAL_SCALE = 4
 #: Entry points declared in include/nvfp4_w4a16.h.
 EXPORTED = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
             "nvfp4_fill_scale_sentinel", "nvfp4_import_checkpoint",
+            "nvfp4_fp8_quantize_rows", "nvfp4_fp8_gemm",
             "nvfp4_status_string", "nvfp4_last_hip_error", "nvfp4_abi_version")
 
 
@@ -80,6 +81,10 @@ def load_library() -> ctypes.CDLL:
     lib.nvfp4_fill_scale_sentinel.restype = ctypes.c_int
     lib.nvfp4_import_checkpoint.argtypes = [vp, i64, ctypes.c_int, vp, i64, i64, vp, vp, vp]
     lib.nvfp4_import_checkpoint.restype = ctypes.c_int
+    lib.nvfp4_fp8_quantize_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.nvfp4_fp8_quantize_rows.restype = ctypes.c_int
+    lib.nvfp4_fp8_gemm.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
+    lib.nvfp4_fp8_gemm.restype = ctypes.c_int
     lib.nvfp4_status_string.argtypes = [ctypes.c_int]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_last_hip_error.argtypes = []
@@ -246,3 +251,50 @@ def check_import_flags(flags: torch.Tensor, what: str = "lm_head") -> int:
         warnings.warn(f"NVFP4 global scales differ across the fused partitions of {what}; "
                       "one (the largest) serves all of them, which may reduce accuracy")
     return f
+
+
+def nvfp4_fp8_quantize_rows(a: torch.Tensor, q: torch.Tensor | None = None,
+                            scales: torch.Tensor | None = None, stream=None):
+    """bf16 [R, K] -> (float8_e4m3fn [R, K], float32 [R]): one E4M3 scale per
+    row (per output row of a weight, per token of an activation)."""
+    a = _as_bf16_2d(a, "a")
+    r, k = a.shape
+    dev = a.device
+    if q is None:
+        q = torch.empty((r, k), dtype=torch.float8_e4m3fn, device=dev)
+    else:
+        _check_out(q, (r, k), (torch.float8_e4m3fn, torch.uint8), dev, "q")
+    if scales is None:
+        scales = torch.empty((r,), dtype=torch.float32, device=dev)
+    else:
+        _check_out(scales, (r,), (torch.float32,), dev, "scales")
+    lib = load_library()
+    _check("nvfp4_fp8_quantize_rows",
+           lib.nvfp4_fp8_quantize_rows(_ptr(a), r, k, _ptr(q), _ptr(scales), _stream_of(a, stream)))
+    return q, scales
+
+
+def nvfp4_fp8_gemm(xq: torch.Tensor, x_scales: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor,
+                   bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """bf16 [M, N] = x_scales[m] * w_scales[n] * (xq . wq^T) (+ bias)."""
+    if xq.dim() != 2 or wq.dim() != 2 or xq.shape[1] != wq.shape[1]:
+        raise ValueError(f"xq {tuple(xq.shape)} and wq {tuple(wq.shape)} must be [M, K] and [N, K]")
+    m, k = xq.shape
+    n = wq.shape[0]
+    dev = wq.device
+    _check_out(xq, (m, k), (torch.float8_e4m3fn, torch.uint8), dev, "xq")
+    _check_out(wq, (n, k), (torch.float8_e4m3fn, torch.uint8), dev, "wq")
+    _check_out(x_scales, (m,), (torch.float32,), dev, "x_scales")
+    _check_out(w_scales, (n,), (torch.float32,), dev, "w_scales")
+    if bias is not None:
+        _check_out(bias, (n,), (torch.bfloat16,), dev, "bias")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_out(out, (m, n), (torch.bfloat16,), dev, "out")
+    lib = load_library()
+    _check("nvfp4_fp8_gemm",
+           lib.nvfp4_fp8_gemm(_ptr(xq), _ptr(x_scales), m, k, _ptr(wq), _ptr(w_scales), n, _ptr(bias),
+                              _ptr(out), _stream_of(wq, stream)))
+    return out

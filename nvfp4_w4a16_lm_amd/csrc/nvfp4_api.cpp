@@ -133,6 +133,36 @@ nvfp4_status nvfp4_fill_scale_sentinel(uint8_t* scales, int64_t N, int64_t K, vo
   return finish(nvfp4::launch_fill_sentinel(scales, N * K / 16, (hipStream_t)stream));
 }
 
+nvfp4_status nvfp4_fp8_quantize_rows(const void* A, int64_t R, int64_t K, uint8_t* q, float* row_scales,
+                                     void* stream) {
+  if (!A || !q || !row_scales) return NVFP4_ERR_NULL;
+  const nvfp4_status s = check_weight_shape(R, K);
+  if (s != NVFP4_OK) return s;
+  if (!aligned(A, 16) || !aligned(q, 16) || !aligned(row_scales, 4)) return NVFP4_ERR_ALIGN;
+  const Range ra = span(A, R * K * 2), rq = span(q, R * K), rs = span(row_scales, R * 4);
+  if (overlap(ra, rq) || overlap(ra, rs) || overlap(rq, rs)) return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_fp8_quant_rows(A, R, K, q, row_scales, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_fp8_gemm(const uint8_t* xq, const float* x_scales, int64_t M, int64_t K, const uint8_t* wq,
+                            const float* w_scales, int64_t N, const void* bias, void* y, void* stream) {
+  if (!wq || !w_scales || (M != 0 && (!xq || !x_scales || !y))) return NVFP4_ERR_NULL;
+  const nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (M < 0 || M > kMaxPrefillM || M * K > kMaxElems || M * N > kMaxElems) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(x_scales, 4) ||
+      !aligned(w_scales, 4) || (bias && !aligned(bias, 2)))
+    return NVFP4_ERR_ALIGN;
+  const Range ry = span(y, M * N * 2);
+  if (overlap(ry, span(xq, M * K)) || overlap(ry, span(x_scales, M * 4)) || overlap(ry, span(wq, N * K)) ||
+      overlap(ry, span(w_scales, N * 4)) || (bias && overlap(ry, span(bias, N * 2))))
+    return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_fp8_gemm(xq, x_scales, M, K, wq, w_scales, N, bias, y, (hipStream_t)stream));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

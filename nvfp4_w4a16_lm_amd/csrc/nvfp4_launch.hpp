@@ -37,4 +37,11 @@ hipError_t launch_import(const float* partition_scales, int64_t P, int conventio
 // Fill nbytes block-scale bytes with the e4m3fn NaN sentinel 0x7F.
 hipError_t launch_fill_sentinel(uint8_t* scales, int64_t nbytes, hipStream_t stream);
 
+// FP8 copy: row-wise E4M3 quantization of a bf16 [R, K] matrix, and the
+// scaled FP8 GEMM y = bf16(s_x[m] s_w[n] sum_k xq wq (+ bias)).
+hipError_t launch_fp8_quant_rows(const void* a, int64_t R, int64_t K, uint8_t* q, float* scales,
+                                 hipStream_t stream);
+hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
+                           const float* ws, int64_t N, const void* bias, void* y, hipStream_t stream);
+
 }  // namespace nvfp4

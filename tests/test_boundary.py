@@ -144,6 +144,23 @@ def test_import_checkpoint_validation(lib):
     assert lib.nvfp4_fill_scale_sentinel(S + 4, 1024, 512, None) == ERR_ALIGN
 
 
+def test_fp8_validation(lib):
+    q8 = lib.nvfp4_fp8_quantize_rows
+    assert q8(0, 1024, 512, P, S, None) == ERR_NULL
+    assert q8(W, 1024, 40, P, S, None) == ERR_SHAPE
+    assert q8(W + 8, 1024, 512, P, S, None) == ERR_ALIGN
+    assert q8(W, 1024, 512, P + 8, S, None) == ERR_ALIGN
+    assert q8(W, 1024, 512, W + 4096, S, None) == ERR_ALIAS
+    g8 = lib.nvfp4_fp8_gemm
+    assert g8(0, G, 4, 512, P, S, 1024, None, Y, None) == ERR_NULL
+    assert g8(0, 0, 0, 512, P, S, 1024, None, 0, None) == OK
+    assert g8(X, G, 4, 40, P, S, 1024, None, Y, None) == ERR_SHAPE
+    assert g8(X, G, -1, 512, P, S, 1024, None, Y, None) == ERR_SHAPE
+    assert g8(X + 8, G, 4, 512, P, S, 1024, None, Y, None) == ERR_ALIGN
+    assert g8(X, G, 4, 512, P, S, 1024, B + 1, Y, None) == ERR_ALIGN
+    assert g8(X, G, 4, 512, P, S, 1024, None, P + 256, None) == ERR_ALIAS
+
+
 def test_binding_import_rejects_unknown_convention():
     import torch
     with pytest.raises(ValueError):

@@ -1,0 +1,144 @@
+"""GPU parity of the FP8 lm_head copy against oracle/fp8_oracle.py.
+
+Row quantization (weights per output row, activations per token): every byte
+and every scale bit.  GEMM: every logit against the float64 reference of the
+same quantized operands, within the benchmark spec's bound and a tight bound set by
+the fp8 MFMA's accumulation precision (see check_fp8_gemm), and the argmax.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.fp8_oracle as F
+from nvfp4_w4a16_lm_amd import binding as B
+from nvfp4_w4a16_lm_amd import workloads as wl
+
+from gpu_util import DEV, dev_bf16, dev_u8, f32_bits, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def quant_gpu(bits):
+    q, s = B.nvfp4_fp8_quantize_rows(dev_bf16(bits))
+    torch.cuda.synchronize()
+    return q.view(torch.uint8).cpu().numpy(), s.cpu().numpy()
+
+
+def assert_quant_equal(bits, label):
+    q, s = quant_gpu(bits)
+    oq, os_ = F.quantize_rows(bits)
+    bad_s = np.flatnonzero(s.view(np.uint32) != os_.view(np.uint32))
+    assert bad_s.size == 0, f"{label}: {bad_s.size} scales differ, first row {bad_s[0]}: {s[bad_s[0]]!r} vs {os_[bad_s[0]]!r}"
+    bad = np.argwhere(q != oq)
+    if bad.size:
+        i, j = bad[0]
+        v = wl.bf16_bits_to_f32(bits[i, j:j + 1])[0]
+        raise AssertionError(f"{label}: {len(bad)} bytes differ; first [{i},{j}] x={v!r} scale={os_[i]!r} "
+                             f"gpu={q[i, j]:#04x} oracle={oq[i, j]:#04x}")
+    return q, s
+
+
+def check_fp8_gemm(y_bits, xq, xs, wq, ws, bias_bits=None, label="", argmax_min=0.999):
+    """Spec bound 1e-3 |x_m| |w_n| on the dequantized operands, and a
+    tight bound for the arithmetic: v_mfma_f32_16x16x32_fp8_fp8 sums its 32
+    products in reduced precision (errors up to 2^-16.7 of sum|x w| were
+    measured on single instructions, far more than float32 rounding), so the
+    bound allows 2^-14 sum|x w| s_x s_w for the instructions plus float32
+    accumulation across them and the final bf16 rounding."""
+    y = wl.bf16_bits_to_f32(y_bits).astype(np.float64)
+    y64 = F.gemm_ref(xq, xs, wq, ws, bias_bits)
+    yabs = F.gemm_abs_ref(xq, xs, wq, ws, bias_bits)
+    xn = np.linalg.norm(F.e4m3_decode_signed(xq) * np.asarray(xs, np.float64)[:, None], axis=1)
+    wn = np.linalg.norm(F.e4m3_decode_signed(wq) * np.asarray(ws, np.float64)[:, None], axis=1)
+    ns = 1e-3 * xn[:, None] * wn[None, :] + 2.0 ** -9 * np.abs(y64)
+    assert np.all(np.abs(y - y64) <= ns), f"{label}: north-star bound"
+    k = xq.shape[1]
+    acc = (2.0 ** -14 + (k + 4) * 2.0 ** -24) * yabs
+    tight = 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
+    err = np.abs(y - y64)
+    worst = np.unravel_index(np.argmax(err - tight), err.shape)
+    assert np.all(err <= tight), (f"{label}: |err| {err[worst]:.3e} > bound {tight[worst]:.3e} at {worst}: "
+                                  f"gpu {y[worst]!r} ref {y64[worst]!r}")
+    if argmax_min > 0 and y.shape[1] > 1:
+        # tie-aware: the reference winner's bf16 logit equals the row's bf16 maximum
+        win = np.argmax(y64, axis=1)
+        ok = y[np.arange(y.shape[0]), win] == y.max(axis=1)
+        assert ok.mean() >= argmax_min, f"{label}: argmax agreement {ok.mean():.4f}"
+
+
+@pytest.mark.parametrize("r,k", [(1, 16), (37, 96), (1027, 1024), (300, 4112), (5, 8192)])
+def test_quantize_rows_bit_exact(r, k):
+    bits = wl.random_weight_bits(r, k, sigma=0.05, seed=r + k)
+    assert_quant_equal(bits, f"{r}x{k}")
+
+
+def test_quantize_rows_special_rows():
+    k = 64
+    rng = np.random.default_rng(8)
+    rows = []
+    rows.append(np.zeros(k, np.float32))                                  # zero row
+    v = np.zeros(k, np.float32); v[3] = -0.0; v[5] = 1.0; rows.append(v)  # -0 and one value
+    v = rng.standard_normal(k).astype(np.float32) * 1e-3; v[0] = 3.0e4; rows.append(v)   # subnormal codes
+    v = rng.standard_normal(k).astype(np.float32) * 2.0 ** 100; rows.append(v)
+    v = rng.standard_normal(k).astype(np.float32) * 2.0 ** -100; rows.append(v)
+    v = np.full(k, -7.0, np.float32); rows.append(v)
+    # values landing exactly between two codes after scaling by 448 / 448
+    codes = np.arange(0x08, 0x7E, dtype=np.uint8)
+    mids = ((F.e4m3_decode_signed(codes[:-1]) + F.e4m3_decode_signed(codes[1:])) / 2)[:k - 1]
+    v = np.concatenate([[448.0], mids]).astype(np.float32); rows.append(v)
+    bits = torch.from_numpy(np.stack(rows)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q, s = assert_quant_equal(bits, "special rows")
+    assert not q[0].any()
+    assert q[1, 3] == 0x80 and q[1, 5] == 0x7E
+
+
+@pytest.mark.parametrize("m", [1, 4, 17, 64, 65, 130, 300])
+@pytest.mark.parametrize("n,k", [(1027, 512), (128, 48), (300, 1040)])
+def test_gemm_matches_oracle(m, n, k):
+    w = wl.random_weight_bits(n, k, sigma=0.02, seed=n + k)
+    x = wl.random_activation_bits(m, k, seed=m + 7)
+    wq, ws = F.quantize_rows(w)
+    xq, xs = F.quantize_rows(x)
+    y = B.nvfp4_fp8_gemm(dev_u8(xq), torch.from_numpy(xs).to(DEV), dev_u8(wq), torch.from_numpy(ws).to(DEV))
+    check_fp8_gemm(host_bits(y), xq, xs, wq, ws, label=f"M={m} N={n} K={k}")
+
+
+def test_gemm_with_bias_end_to_end():
+    """GPU quantization of both operands, then the GEMM with a bias."""
+    n, k, m = 515, 320, 9
+    w = wl.random_weight_bits(n, k, sigma=0.02, seed=1)
+    x = wl.random_activation_bits(m, k, seed=2)
+    bias = wl.random_weight_bits(1, n, sigma=0.5, seed=3)[0]
+    wq, ws = assert_quant_equal(w, "w")
+    xq, xs = assert_quant_equal(x, "x")
+    qw, sw = B.nvfp4_fp8_quantize_rows(dev_bf16(w))
+    qx, sx = B.nvfp4_fp8_quantize_rows(dev_bf16(x))
+    y = B.nvfp4_fp8_gemm(qx, sx, qw, sw, bias=dev_bf16(bias))
+    check_fp8_gemm(host_bits(y), xq, xs, wq, ws, bias, label="bias")
+
+
+def test_gemm_empty_batch_and_scale_bits():
+    w = wl.random_weight_bits(64, 32, seed=5)
+    qw, sw = B.nvfp4_fp8_quantize_rows(dev_bf16(w))
+    y = B.nvfp4_fp8_gemm(torch.empty((0, 32), dtype=torch.uint8, device=DEV),
+                         torch.empty((0,), dtype=torch.float32, device=DEV), qw, sw)
+    assert y.shape == (0, 64)
+    _, os_ = F.quantize_rows(w)
+    assert all(f32_bits(a) == f32_bits(b) for a, b in zip(sw.cpu().numpy(), os_))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_size_8b_shape():
+    """128256 x 4096 weight: every byte and scale; every logit at M = 64."""
+    w = wl.WORKLOADS["llama3_8b"]
+    wb = wl.weight_bits(w)
+    xb = wl.activation_bits(w)
+    q, s = quant_gpu(wb)
+    oq, os_ = F.quantize_rows(wb)
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q, oq)
+    xq, xs = F.quantize_rows(xb[:64])
+    y = B.nvfp4_fp8_gemm(dev_u8(xq), torch.from_numpy(xs).to(DEV), dev_u8(oq), torch.from_numpy(os_).to(DEV))
+    check_fp8_gemm(host_bits(y), xq, xs, oq, os_, label="8B M=64")
