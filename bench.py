@@ -270,6 +270,25 @@ def main() -> int:
     torch.cuda.synchronize()
     fp8_ms = {op: float(np.mean([a.elapsed_time(b) for a, b in v])) for op, v in fp8_ev.items()}
 
+    # NVFP4 W4A4 (not part of the step): per M, activation quantization with a
+    # static global input scale + the W4A4 GEMM on the step's quantized weight.
+    gi = torch.tensor(np.float32(2.0 ** -7), device=dev)
+    wsp = torch.empty((int(B.load_library().nvfp4_w4a4_workspace_bytes(max(ms), k)),), dtype=torch.uint8,
+                      device=dev)
+    w4_ev = {m: [] for m in ms}
+    for it in range(args.warmup + args.steps):
+        for m in ms:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            xp4, xs4 = B.nvfp4_quantize_activations(xs[m], gi)
+            B.nvfp4_w4a4_gemm(xp4, xs4, gi, *Q[0], out=Y[m], workspace=wsp)
+            b.record()
+            if it >= args.warmup:
+                w4_ev[m].append((a, b))
+    torch.cuda.synchronize()
+    w4_ms = {m: float(np.mean([a.elapsed_time(b) for a, b in v])) for m, v in w4_ev.items()}
+
     step_bytes = quant_bytes(n, k) + sum(gemm_bytes(m, n, k) for m in ms)
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
 
@@ -288,6 +307,12 @@ def main() -> int:
                                       "TB/s": (n * k + 4 * n + 3 * m * k + 4 * m + 2 * m * n) / t8 / 1e12,
                                       "TFLOP/s": gemm_flops(m, n, k) / t8 / 1e12,
                                       "kernels": "fp8_quant_rows (per token) + fp8_gemm", "in_step": False}
+    for m in ms:
+        t4 = w4_ms[m] * 1e-3
+        per_op[f"w4a4_m{m}"] = {"ms": w4_ms[m], "TB/s": gemm_bytes(m, n, k) / t4 / 1e12,
+                                "TFLOP/s": gemm_flops(m, n, k) / t4 / 1e12,
+                                "kernels": "quant_pack (activations, given scale) + w4a4_dequant_x + the W4A16 GEMM",
+                                "in_step": False}
     for m in ms:
         t = avg_ms[f"gemm_m{m}"] * 1e-3
         per_op[f"gemm_m{m}"] = {"ms": avg_ms[f"gemm_m{m}"],

@@ -227,6 +227,50 @@ nvfp4_status nvfp4_fp8_quantize_rows(const void* A, int64_t R, int64_t K, uint8_
 nvfp4_status nvfp4_fp8_gemm(const uint8_t* xq, const float* x_scales, int64_t M, int64_t K, const uint8_t* wq,
                             const float* w_scales, int64_t N, const void* bias, void* y, void* stream);
 
+/*
+ * NVFP4 W4A4: activations quantized to NVFP4 at run time with a static global
+ * input scale, and the GEMM of the two NVFP4 operands.
+ * (vLLM modelopt.py, KNvfp4Dynamic, maybe_fuse_global_scales and the NVFP4
+ * recipe: static FP4 weight, dynamic FP4 activation, alpha =
+ * input_global_scale * weight_global_scale.)
+ *
+ * nvfp4_quantize_activations -- x bf16 [M, K] (16-byte aligned) -> packed
+ * uint8 [M, K/2] and float8_e4m3fn scales [M, K/16], with the rules of
+ * nvfp4_quantize but the given input_global_scale (1 float on the device, the
+ * dequantization direction, e.g. the max of a checkpoint's input_scale; it
+ * must be a finite number > 0) in place of amax/2688.  Nothing is written to
+ * input_global_scale.
+ */
+nvfp4_status nvfp4_quantize_activations(const void* x, int64_t M, int64_t K, const float* input_global_scale,
+                                        uint8_t* packed, uint8_t* scales, void* stream);
+
+/*
+ * nvfp4_w4a4_workspace_bytes -- size of nvfp4_w4a4_gemm's workspace: 2*M*K + 16
+ * (host helper, no device work; 0 for negative sizes).
+ */
+int64_t nvfp4_w4a4_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * nvfp4_w4a4_gemm -- logits from NVFP4 activations and the NVFP4 weight.
+ *
+ *   x_packed, x_scales   in  from nvfp4_quantize_activations, [M, K/2] / [M, K/16]
+ *   input_global_scale   in  the global scale they were quantized with (1 float)
+ *   packed, scales, global_scale, N, bias   in  as for nvfp4_w4a16_gemm
+ *   workspace            tmp device buffer of nvfp4_w4a4_workspace_bytes(M, K) bytes,
+ *                            16-byte aligned, overlapping nothing else; it holds the
+ *                            activations' exact bf16 values code * block scale, then
+ *                            alpha, and may be reused once the stream is past the call
+ *   y                    out bf16 [M, N]
+ *
+ *   y[m, n] = bf16_rne( alpha * sum_k (E2M1(cx) * e4m3(sx)) * (E2M1(cw) * e4m3(sw)) + bias[n] ),
+ *   alpha = fl32(input_global_scale * global_scale), float32 accumulation of exact products.
+ * M == 0 enqueues nothing (the activation pointers, workspace and y may then be NULL).
+ */
+nvfp4_status nvfp4_w4a4_gemm(const uint8_t* x_packed, const uint8_t* x_scales, const float* input_global_scale,
+                             int64_t M, int64_t K, const uint8_t* packed, const uint8_t* scales,
+                             const float* global_scale, int64_t N, const void* bias, void* workspace, void* y,
+                             void* stream);
+
 /* Host-side helpers (no device work). */
 const char* nvfp4_status_string(int status);   /* static string for a status code        */
 const char* nvfp4_last_hip_error(void);        /* last HIP error text of this thread, or "" */

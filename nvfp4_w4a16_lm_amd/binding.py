@@ -38,6 +38,7 @@ IMPORT_BAD_GLOBAL_SCALE = 4
 EXPORTED = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
             "nvfp4_fill_scale_sentinel", "nvfp4_import_checkpoint",
             "nvfp4_fp8_quantize_rows", "nvfp4_fp8_gemm",
+            "nvfp4_quantize_activations", "nvfp4_w4a4_workspace_bytes", "nvfp4_w4a4_gemm",
             "nvfp4_status_string", "nvfp4_last_hip_error", "nvfp4_abi_version")
 
 
@@ -85,6 +86,12 @@ def load_library() -> ctypes.CDLL:
     lib.nvfp4_fp8_quantize_rows.restype = ctypes.c_int
     lib.nvfp4_fp8_gemm.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
     lib.nvfp4_fp8_gemm.restype = ctypes.c_int
+    lib.nvfp4_quantize_activations.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    lib.nvfp4_quantize_activations.restype = ctypes.c_int
+    lib.nvfp4_w4a4_workspace_bytes.argtypes = [i64, i64]
+    lib.nvfp4_w4a4_workspace_bytes.restype = i64
+    lib.nvfp4_w4a4_gemm.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.nvfp4_w4a4_gemm.restype = ctypes.c_int
     lib.nvfp4_status_string.argtypes = [ctypes.c_int]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_last_hip_error.argtypes = []
@@ -297,4 +304,58 @@ def nvfp4_fp8_gemm(xq: torch.Tensor, x_scales: torch.Tensor, wq: torch.Tensor, w
     _check("nvfp4_fp8_gemm",
            lib.nvfp4_fp8_gemm(_ptr(xq), _ptr(x_scales), m, k, _ptr(wq), _ptr(w_scales), n, _ptr(bias),
                               _ptr(out), _stream_of(wq, stream)))
+    return out
+
+
+def nvfp4_quantize_activations(x: torch.Tensor, input_global_scale: torch.Tensor, stream=None):
+    """bf16 [M, K] -> (packed uint8 [M, K/2], scales float8_e4m3fn [M, K/16]) with a
+    given global scale (fp32 [] on the device, dequantization direction)."""
+    x = _as_bf16_2d(x, "x")
+    m, k = x.shape
+    dev = x.device
+    if input_global_scale.numel() != 1 or input_global_scale.dtype != torch.float32 or \
+            input_global_scale.device != dev:
+        raise ValueError("input_global_scale must be one float32 on x's device")
+    packed = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((m, k // 16), dtype=torch.float8_e4m3fn, device=dev)
+    lib = load_library()
+    _check("nvfp4_quantize_activations",
+           lib.nvfp4_quantize_activations(_ptr(x), m, k, _ptr(input_global_scale), _ptr(packed), _ptr(scales),
+                                          _stream_of(x, stream)))
+    return packed, scales
+
+
+def nvfp4_w4a4_gemm(x_packed: torch.Tensor, x_scales: torch.Tensor, input_global_scale: torch.Tensor,
+                    packed: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
+                    bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 [M, N] = alpha * (NVFP4 x) . (NVFP4 W)^T (+ bias), alpha = gs_in * gs_w."""
+    if x_packed.dim() != 2 or packed.dim() != 2 or x_packed.shape[1] != packed.shape[1]:
+        raise ValueError(f"x_packed {tuple(x_packed.shape)} and packed {tuple(packed.shape)} do not match")
+    m, k = x_packed.shape[0], x_packed.shape[1] * 2
+    n = packed.shape[0]
+    dev = packed.device
+    _check_out(x_packed, (m, k // 2), (torch.uint8,), dev, "x_packed")
+    _check_out(x_scales, (m, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, "x_scales")
+    _check_out(packed, (n, k // 2), (torch.uint8,), dev, "packed")
+    _check_out(scales, (n, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, "scales")
+    for t, what in ((input_global_scale, "input_global_scale"), (global_scale, "global_scale")):
+        if t.numel() != 1 or t.dtype != torch.float32 or t.device != dev:
+            raise ValueError(f"{what} must be one float32 on the weight's device")
+    if bias is not None:
+        _check_out(bias, (n,), (torch.bfloat16,), dev, "bias")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_out(out, (m, n), (torch.bfloat16,), dev, "out")
+    lib = load_library()
+    need = int(lib.nvfp4_w4a4_workspace_bytes(m, k))
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+        raise ValueError(f"workspace needs {need} bytes on {dev}")
+    _check("nvfp4_w4a4_gemm",
+           lib.nvfp4_w4a4_gemm(_ptr(x_packed), _ptr(x_scales), _ptr(input_global_scale), m, k, _ptr(packed),
+                               _ptr(scales), _ptr(global_scale), n, _ptr(bias), _ptr(workspace), _ptr(out),
+                               _stream_of(packed, stream)))
     return out

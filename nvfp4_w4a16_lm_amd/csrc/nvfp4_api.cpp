@@ -163,6 +163,57 @@ nvfp4_status nvfp4_fp8_gemm(const uint8_t* xq, const float* x_scales, int64_t M,
   return finish(nvfp4::launch_fp8_gemm(xq, x_scales, M, K, wq, w_scales, N, bias, y, (hipStream_t)stream));
 }
 
+nvfp4_status nvfp4_quantize_activations(const void* x, int64_t M, int64_t K, const float* input_global_scale,
+                                        uint8_t* packed, uint8_t* scales, void* stream) {
+  if (!x || !input_global_scale || !packed || !scales) return NVFP4_ERR_NULL;
+  const nvfp4_status s = check_weight_shape(M, K);
+  if (s != NVFP4_OK) return s;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(input_global_scale, 4))
+    return NVFP4_ERR_ALIGN;
+  const Range rx = span(x, M * K * 2), rg = span(input_global_scale, 4), rp = span(packed, M * K / 2),
+              rs = span(scales, M * K / 16);
+  if (overlap(rp, rx) || overlap(rp, rg) || overlap(rs, rx) || overlap(rs, rg) || overlap(rp, rs))
+    return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_quantize_given_scale(x, M, K, input_global_scale, packed, scales,
+                                                   (hipStream_t)stream));
+}
+
+int64_t nvfp4_w4a4_workspace_bytes(int64_t M, int64_t K) { return (M < 0 || K < 0) ? 0 : 2 * M * K + 16; }
+
+nvfp4_status nvfp4_w4a4_gemm(const uint8_t* x_packed, const uint8_t* x_scales, const float* input_global_scale,
+                             int64_t M, int64_t K, const uint8_t* packed, const uint8_t* scales,
+                             const float* global_scale, int64_t N, const void* bias, void* workspace, void* y,
+                             void* stream) {
+  if (!packed || !scales || !global_scale ||
+      (M != 0 && (!x_packed || !x_scales || !input_global_scale || !workspace || !y)))
+    return NVFP4_ERR_NULL;
+  nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (M < 0 || M > kMaxPrefillM || M * K > kMaxElems || M * N > kMaxElems) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!aligned(x_packed, 16) || !aligned(x_scales, 4) || !aligned(input_global_scale, 4) || !aligned(packed, 16) ||
+      !aligned(scales, 4) || !aligned(global_scale, 4) || !aligned(workspace, 16) || !aligned(y, 16) ||
+      (bias && !aligned(bias, 2)))
+    return NVFP4_ERR_ALIGN;
+  const Range ry = span(y, M * N * 2), rw = span(workspace, nvfp4_w4a4_workspace_bytes(M, K));
+  const Range ins[] = {span(x_packed, M * K / 2), span(x_scales, M * K / 16), span(input_global_scale, 4),
+                       span(packed, N * K / 2),   span(scales, N * K / 16),   span(global_scale, 4),
+                       span(bias ? bias : y, bias ? N * 2 : 0)};
+  if (overlap(ry, rw)) return NVFP4_ERR_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(ry, r) || overlap(rw, r)) return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  const hipStream_t st = (hipStream_t)stream;
+  uint8_t* const xd = static_cast<uint8_t*>(workspace);
+  float* const alpha = reinterpret_cast<float*>(xd + 2 * M * K);
+  hipError_t e = nvfp4::launch_w4a4_dequant_x(x_packed, x_scales, M, K, input_global_scale, global_scale, xd,
+                                              alpha, st);
+  if (e != hipSuccess) return finish(e);
+  if (M <= nvfp4::kDecodeMaxM) return finish(nvfp4::launch_gemv(xd, M, K, packed, scales, alpha, N, bias, y, st));
+  return finish(nvfp4::launch_gemm_prefill(xd, M, K, packed, scales, alpha, N, bias, y, st));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

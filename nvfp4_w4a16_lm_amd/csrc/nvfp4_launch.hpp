@@ -41,6 +41,13 @@ hipError_t launch_fill_sentinel(uint8_t* scales, int64_t nbytes, hipStream_t str
 // scaled FP8 GEMM y = bf16(s_x[m] s_w[n] sum_k xq wq (+ bias)).
 hipError_t launch_fp8_quant_rows(const void* a, int64_t R, int64_t K, uint8_t* q, float* scales,
                                  hipStream_t stream);
+// W4A4: NVFP4 quantization of activations with a given global scale, and the
+// exact bf16 dequantization of them (code * block scale) plus alpha.
+hipError_t launch_quantize_given_scale(const void* X, int64_t M, int64_t K, const float* global_scale,
+                                       uint8_t* packed, uint8_t* scales, hipStream_t stream);
+hipError_t launch_w4a4_dequant_x(const uint8_t* x_packed, const uint8_t* x_scales, int64_t M, int64_t K,
+                                 const float* gs_in, const float* gs_w, void* xd, float* alpha,
+                                 hipStream_t stream);
 hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
                            const float* ws, int64_t N, const void* bias, void* y, hipStream_t stream);
 

@@ -125,8 +125,10 @@ __device__ __forceinline__ uint32_t encode_half_block(const u32x4 v, float inv, 
 
 // One kSpan-vector span per workgroup, taken from the end of the tensor
 // (workgroup 0 gets the last span).
+// gs_word: the tagged amax or the global scale itself; gs_out (may be null):
+// where workgroup 0 stores the global scale.
 __global__ __launch_bounds__(kThreads) void quant_pack_kernel(const u32x4* __restrict__ w, int64_t n16,
-                                                              float* __restrict__ gs_word,
+                                                              const float* gs_word, float* gs_out,
                                                               uint32_t* __restrict__ packed,
                                                               uint8_t* __restrict__ scales) {
   __shared__ float rlut[128];
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void quant_pack_kernel(const u32x4* __res
   } else {
     gs = __uint_as_float(word);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_word = gs;
+  if (gs_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   const float inv = 1.0f / gs;                        // fl32(1 / gs)
   if (threadIdx.x < 128) {
     // r for E4M3 byte threadIdx.x (0..126 are the finite non-negative scales)
@@ -214,9 +216,20 @@ hipError_t launch_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed,
                     reinterpret_cast<const u32x4*>(W), n16, amax_span, word);
   if (e != hipSuccess) return e;
   e = launch_kernel((const void*)quant_pack_kernel, dim3(pack_grid), dim3(kThreads), stream,
-                    reinterpret_cast<const u32x4*>(W), n16, global_scale, reinterpret_cast<uint32_t*>(packed),
-                    scales);
+                    reinterpret_cast<const u32x4*>(W), n16, (const float*)global_scale, global_scale,
+                    reinterpret_cast<uint32_t*>(packed), scales);
   return e;
+}
+
+// Activations of a W4A4 layer: the same block scales and codes with a given
+// (static) global scale; no amax pass, nothing written back to it.
+hipError_t launch_quantize_given_scale(const void* X, int64_t M, int64_t K, const float* global_scale,
+                                       uint8_t* packed, uint8_t* scales, hipStream_t stream) {
+  const int64_t n16 = M * K / 8;
+  const int pack_grid = (int)((n16 + kSpan - 1) / kSpan);
+  return launch_kernel((const void*)quant_pack_kernel, dim3(pack_grid), dim3(kThreads), stream,
+                       reinterpret_cast<const u32x4*>(X), n16, global_scale, (float*)nullptr,
+                       reinterpret_cast<uint32_t*>(packed), scales);
 }
 
 }  // namespace nvfp4

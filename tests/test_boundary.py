@@ -26,7 +26,7 @@ W, P, S, G, X, Y, B = (0x10000000 * (i + 1) for i in range(7))
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|const char\*|int)\s+(nvfp4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|const char\*|int|int64_t)\s+(nvfp4_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -159,6 +159,30 @@ def test_fp8_validation(lib):
     assert g8(X + 8, G, 4, 512, P, S, 1024, None, Y, None) == ERR_ALIGN
     assert g8(X, G, 4, 512, P, S, 1024, B + 1, Y, None) == ERR_ALIGN
     assert g8(X, G, 4, 512, P, S, 1024, None, P + 256, None) == ERR_ALIAS
+
+
+def test_w4a4_validation(lib):
+    qa = lib.nvfp4_quantize_activations
+    assert qa(0, 4, 512, G, P, S, None) == ERR_NULL
+    assert qa(X, 4, 40, G, P, S, None) == ERR_SHAPE
+    assert qa(X, 0, 512, G, P, S, None) == ERR_SHAPE
+    assert qa(X + 8, 4, 512, G, P, S, None) == ERR_ALIGN
+    assert qa(X, 4, 512, G, P, X + 64, None) == ERR_ALIAS
+    assert lib.nvfp4_w4a4_workspace_bytes(4, 512) == 2 * 4 * 512 + 16
+    g4 = lib.nvfp4_w4a4_gemm
+    args = dict(xp=X, xs=B, gi=G + 64, m=4, k=512, p=P, s=S, g=G, n=1024, b=None, ws=W, y=Y)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return g4(a["xp"], a["xs"], a["gi"], a["m"], a["k"], a["p"], a["s"], a["g"], a["n"], a["b"], a["ws"],
+                  a["y"], None)
+    assert call(ws=0) == ERR_NULL
+    assert call(m=0, xp=0, xs=0, gi=0, ws=0, y=0) == OK
+    assert call(k=40) == ERR_SHAPE
+    assert call(ws=W + 8) == ERR_ALIGN
+    assert call(ws=Y + 64) == ERR_ALIAS
+    assert call(ws=P - 1024) == ERR_ALIAS
+    assert call(y=X + 256) == ERR_ALIAS
 
 
 def test_binding_import_rejects_unknown_convention():
