@@ -14,9 +14,10 @@
 // reading of the pages: s = max(amax / 448, 1e-12) in float32, q =
 // e4m3(clamp(x * (1 / s), -448, 448)), round to nearest even, sign kept.
 //
-// fp8_quant_rows_kernel: one wavefront per row; pass 1 takes the row's
-//   largest |x| (bf16 magnitudes compare as integers), pass 2 re-reads the
-//   row (from L2) and converts 8 values per lane with v_cvt_pk_fp8_f32.
+// fp8_quant_rows_kernel<V>: one wavefront per row; the row's largest |x|
+//   (bf16 magnitudes compare as integers), a wavefront butterfly, then 8
+//   values per lane converted with v_cvt_pk_fp8_f32; rows up to 8192 values
+//   stay in registers between the two steps (read from HBM once).
 // fp8_gemm_kernel<MT>: a workgroup of 4 wavefronts owns 128 weight rows and
 //   16 MT activation rows (MT <= 8); K is walked in 64-byte slabs staged in
 //   double-buffered LDS (next slab's global loads in registers while the
@@ -39,17 +40,49 @@ namespace nvfp4 {
 constexpr float kFp8Max = 448.0f;
 constexpr float kFp8ScaleMin = 1e-12f;
 
+// Largest bf16 magnitude (as its bit pattern) of the 8 values of a vector.
+__device__ __forceinline__ uint32_t mag_max8(const u32x4 d) {
+  const uint32_t a = max(max(d.x & 0x7FFFu, (d.x >> 16) & 0x7FFFu), max(d.y & 0x7FFFu, (d.y >> 16) & 0x7FFFu));
+  const uint32_t b = max(max(d.z & 0x7FFFu, (d.z >> 16) & 0x7FFFu), max(d.w & 0x7FFFu, (d.w >> 16) & 0x7FFFu));
+  return max(a, b);
+}
+
+// 8 bf16 values times inv, clamped to +-448, as 8 e4m3 bytes (RNE).
+__device__ __forceinline__ uint2 to_e4m3x8(const u32x4 d, float inv) {
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = fminf(fmaxf(bf16_lo(d[e]) * inv, -kFp8Max), kFp8Max);
+    f[2 * e + 1] = fminf(fmaxf(bf16_hi(d[e]) * inv, -kFp8Max), kFp8Max);
+  }
+  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+  return make_uint2(lo, hi);
+}
+
+// V > 0: the lane's V vectors of the row stay in registers between the two
+// passes (K <= 512 V), so the row is read once; V == 0: any K, the row is
+// read a second time for the conversion.
+template <int V>
 __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __restrict__ a, int64_t R, int K,
                                                              uint8_t* __restrict__ q, float* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int nvec = K >> 3;                                       // 8 bf16 per 16-byte vector
   for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < R; row += (int64_t)gridDim.x * 4) {
     const u32x4* src = reinterpret_cast<const u32x4*>(a + row * K);
+    uint2* dst = reinterpret_cast<uint2*>(q + row * K);
+    u32x4 buf[V > 0 ? V : 1];
     uint32_t mx = 0;
-    for (int v = lane; v < nvec; v += 64) {
-      const u32x4 d = src[v];
-      mx = max(mx, max(max(d.x & 0x7FFFu, (d.x >> 16) & 0x7FFFu), max(d.y & 0x7FFFu, (d.y >> 16) & 0x7FFFu)));
-      mx = max(mx, max(max(d.z & 0x7FFFu, (d.z >> 16) & 0x7FFFu), max(d.w & 0x7FFFu, (d.w >> 16) & 0x7FFFu)));
+    if constexpr (V > 0) {
+      // clamped, unconditional loads; a repeated vector does not change the max
+#pragma unroll
+      for (int j = 0; j < V; ++j) buf[j] = src[min(lane + 64 * j, nvec - 1)];
+#pragma unroll
+      for (int j = 0; j < V; ++j) mx = max(mx, mag_max8(buf[j]));
+    } else {
+      for (int v = lane; v < nvec; v += 64) mx = max(mx, mag_max8(src[v]));
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
@@ -57,20 +90,12 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __r
     const float s = fmaxf(amax / kFp8Max, kFp8ScaleMin);          // IEEE division
     const float inv = 1.0f / s;
     if (lane == 0) scales[row] = s;
-    uint2* dst = reinterpret_cast<uint2*>(q + row * K);
-    for (int v = lane; v < nvec; v += 64) {
-      const u32x4 d = src[v];
-      float f[8];
+    if constexpr (V > 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[2 * e] = fminf(fmaxf(bf16_lo(d[e]) * inv, -kFp8Max), kFp8Max);
-        f[2 * e + 1] = fminf(fmaxf(bf16_hi(d[e]) * inv, -kFp8Max), kFp8Max);
-      }
-      uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-      uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-      dst[v] = make_uint2(lo, hi);
+      for (int j = 0; j < V; ++j)
+        if (lane + 64 * j < nvec) dst[lane + 64 * j] = to_e4m3x8(buf[j], inv);
+    } else {
+      for (int v = lane; v < nvec; v += 64) dst[v] = to_e4m3x8(src[v], inv);
     }
   }
 }
@@ -194,8 +219,11 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t* __restrict
 hipError_t launch_fp8_quant_rows(const void* a, int64_t R, int64_t K, uint8_t* q, float* scales,
                                  hipStream_t stream) {
   const int64_t blocks = std::min<int64_t>((R + 3) / 4, 65536);
-  return launch_kernel((const void*)fp8_quant_rows_kernel, dim3((unsigned)blocks), dim3(256), stream,
-                       (const uint16_t*)a, R, (int)K, q, scales);
+  const void* fn = K <= 2048   ? (const void*)fp8_quant_rows_kernel<4>
+                   : K <= 4096 ? (const void*)fp8_quant_rows_kernel<8>
+                   : K <= 8192 ? (const void*)fp8_quant_rows_kernel<16>
+                               : (const void*)fp8_quant_rows_kernel<0>;
+  return launch_kernel(fn, dim3((unsigned)blocks), dim3(256), stream, (const uint16_t*)a, R, (int)K, q, scales);
 }
 
 template <int MT>

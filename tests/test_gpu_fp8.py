@@ -67,7 +67,7 @@ def check_fp8_gemm(y_bits, xq, xs, wq, ws, bias_bits=None, label="", argmax_min=
         assert ok.mean() >= argmax_min, f"{label}: argmax agreement {ok.mean():.4f}"
 
 
-@pytest.mark.parametrize("r,k", [(1, 16), (37, 96), (1027, 1024), (300, 4112), (5, 8192)])
+@pytest.mark.parametrize("r,k", [(1, 16), (37, 96), (1027, 1024), (7, 3072), (300, 4112), (5, 8192), (3, 8208)])
 def test_quantize_rows_bit_exact(r, k):
     bits = wl.random_weight_bits(r, k, sigma=0.05, seed=r + k)
     assert_quant_equal(bits, f"{r}x{k}")
