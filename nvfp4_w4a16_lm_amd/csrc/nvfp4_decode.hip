@@ -433,6 +433,28 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   const int wrd0 = r * 128 + 16 * ((2 * g) ^ (r & 7)), wrd1 = r * 128 + 16 * ((2 * g + 1) ^ (r & 7));
   const int srd = r * 64 + 4 * g, skey = (r >> 1) & 3;
 
+  const int ntiles = (N + 15) / 16;
+  const int stride = gridDim.x * NW;
+  auto w_copy = [&](int tile, int c) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t row = min(16 * tile + 8 * j + (lane >> 3), N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(packed + row * prow + 128 * c + 16 * wpiece),
+                                       (lds_ptr_t)(wmine + 1024 * j), 16, 0, kCachePolicyNT);
+    }
+  };
+  auto s_copy = [&](int tile, int grp) {
+    const int64_t row = min(16 * tile + (lane >> 2), N - 1);
+    const int64_t off = min((int64_t)16 * (kScaleGroup * grp + spiece), srow - 16);   // past the row end: unused
+    __builtin_amdgcn_global_load_lds((const void*)(scales + row * srow + off), (lds_ptr_t)smine, 16, 0, 0);
+  };
+  // the first chunk's copies fly while x is converted
+  int tile = blockIdx.x * NW + wave;
+  if (tile < ntiles) {
+    w_copy(tile, 0);
+    s_copy(tile, 0);
+  }
+
   // x -> f16 rows in LDS: wavefront w handles rows w, w + NW, ...: the row's
   // largest |x| (bf16 magnitudes compare as integers), then x * 2^-p_m
   const int xvec = K / 8;                           // 16-byte vectors per x row
@@ -466,26 +488,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   const float up = xup[min(r, M - 1)];
   const uint8_t* const xrow = xl + min(r, M - 1) * xpitch + 128 * g;   // this lane's k-group, chunk 0
 
-  const int ntiles = (N + 15) / 16;
-  const int stride = gridDim.x * NW;
-  auto w_copy = [&](int tile, int c) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t row = min(16 * tile + 8 * j + (lane >> 3), N - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(packed + row * prow + 128 * c + 16 * wpiece),
-                                       (lds_ptr_t)(wmine + 1024 * j), 16, 0, kCachePolicyNT);
-    }
-  };
-  auto s_copy = [&](int tile, int grp) {
-    const int64_t row = min(16 * tile + (lane >> 2), N - 1);
-    const int64_t off = min((int64_t)16 * (kScaleGroup * grp + spiece), srow - 16);   // past the row end: unused
-    __builtin_amdgcn_global_load_lds((const void*)(scales + row * srow + off), (lds_ptr_t)smine, 16, 0, 0);
-  };
-  int tile = blockIdx.x * NW + wave;
-  if (tile < ntiles) {
-    w_copy(tile, 0);
-    s_copy(tile, 0);
-  }
   for (; tile < ntiles; tile += stride) {
     const int n_base = tile * 16;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
