@@ -22,6 +22,8 @@
 //   (double buffered), and each wavefront reuses those fragments for R tiles
 //   of 16 weight rows, with the next chunk's weights prefetched into
 //   registers while the current one computes.
+#include <atomic>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -836,16 +838,18 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
   const void* fn = (const void*)gemv_xres_kernel<NW>;
   const int lds = (int)xres_lds_bytes(M, K, NW);
-  // raise the dynamic LDS limit once per kernel (the default allows less than the hardware's 160 KiB)
-  static bool attr_set = false;
-  if (!attr_set) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  // raise the dynamic LDS limit (the default allows less than the hardware's
+  // 160 KiB) once per kernel and device; concurrent first calls both set it
+  static std::atomic<uint64_t> attr_done{0};
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit == 0 || !(attr_done.load(std::memory_order_acquire) & bit)) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kXresLdsMax);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_done.fetch_or(bit, std::memory_order_release);
   }
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
   const int ntiles = (N + 15) / 16;
