@@ -7,7 +7,9 @@ import concurrent.futures
 import numpy as np
 import torch
 
+import oracle.fp8_oracle as F
 import oracle.nvfp4_oracle as O
+import oracle.nvfp4_w4a4_oracle as A
 from nvfp4_w4a16_lm_amd import binding as B
 from nvfp4_w4a16_lm_amd import workloads as wl
 
@@ -129,3 +131,52 @@ def check_gemm(y_bits, x_bits, packed, scales, gs, bias_bits=None, label="", arg
         tie, strict = O.argmax_agreement(y, y64)
         assert tie >= argmax_min, f"{label}: tie-aware argmax agreement {tie} (strict {strict})"
     return y64
+
+
+def check_fp8_gemm(y_bits, xq, xs, wq, ws, bias_bits=None, label="", argmax_min=0.999):
+    """Spec bound 1e-3 |x_m| |w_n| on the dequantized operands, and a
+    tight bound for the arithmetic: v_mfma_f32_16x16x32_fp8_fp8 sums its 32
+    products in reduced precision (errors up to 2^-16.7 of sum|x w| were
+    measured on single instructions, far more than float32 rounding), so the
+    bound allows 2^-14 sum|x w| s_x s_w for the instructions plus float32
+    accumulation across them and the final bf16 rounding."""
+    y = wl.bf16_bits_to_f32(y_bits).astype(np.float64)
+    y64 = F.gemm_ref(xq, xs, wq, ws, bias_bits)
+    yabs = F.gemm_abs_ref(xq, xs, wq, ws, bias_bits)
+    xn = np.linalg.norm(F.e4m3_decode_signed(xq) * np.asarray(xs, np.float64)[:, None], axis=1)
+    wn = np.linalg.norm(F.e4m3_decode_signed(wq) * np.asarray(ws, np.float64)[:, None], axis=1)
+    ns = 1e-3 * xn[:, None] * wn[None, :] + 2.0 ** -9 * np.abs(y64)
+    assert np.all(np.abs(y - y64) <= ns), f"{label}: north-star bound"
+    k = xq.shape[1]
+    acc = (2.0 ** -14 + (k + 4) * 2.0 ** -24) * yabs
+    tight = 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
+    err = np.abs(y - y64)
+    worst = np.unravel_index(np.argmax(err - tight), err.shape)
+    assert np.all(err <= tight), (f"{label}: |err| {err[worst]:.3e} > bound {tight[worst]:.3e} at {worst}: "
+                                  f"gpu {y[worst]!r} ref {y64[worst]!r}")
+    if argmax_min > 0 and y.shape[1] > 1:
+        # tie-aware: the reference winner's bf16 logit equals the row's bf16 maximum
+        win = np.argmax(y64, axis=1)
+        ok = y[np.arange(y.shape[0]), win] == y.max(axis=1)
+        assert ok.mean() >= argmax_min, f"{label}: argmax agreement {ok.mean():.4f}"
+
+
+def check_w4a4(y_bits, xp, xs, wp, ws, a, bias_bits=None, label="", argmax_min=0.999):
+    y = wl.bf16_bits_to_f32(y_bits).astype(np.float64)
+    y64 = A.gemm_ref(xp, xs, wp, ws, a, bias_bits)
+    yabs = A.gemm_abs_ref(xp, xs, wp, ws, a, bias_bits)
+    xn = np.linalg.norm(A.block_values(xp, xs), axis=1)
+    wn = np.linalg.norm(A.block_values(wp, ws), axis=1)
+    ns = 1e-3 * float(a) * xn[:, None] * wn[None, :] + 2.0 ** -9 * np.abs(y64)
+    err = np.abs(y - y64)
+    assert np.all(err <= ns), f"{label}: north-star bound"
+    k = xp.shape[1] * 2
+    acc = (k + 4) * 2.0 ** -24 * yabs
+    tight = 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
+    worst = np.unravel_index(np.argmax(err - tight), err.shape)
+    assert np.all(err <= tight), (f"{label}: |err| {err[worst]:.3e} > {tight[worst]:.3e} at {worst}: "
+                                  f"gpu {y[worst]!r} ref {y64[worst]!r}")
+    if argmax_min > 0 and y.shape[1] > 1:
+        win = np.argmax(y64, axis=1)
+        ok = y[np.arange(y.shape[0]), win] == y.max(axis=1)
+        assert ok.mean() >= argmax_min, f"{label}: argmax agreement {ok.mean():.4f}"

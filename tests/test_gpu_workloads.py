@@ -5,20 +5,24 @@ Quantization: every byte of packed codes and scales and the global scale's bits
 against the oracle (quantized on a thread pool, same arithmetic).
 GEMM: every logit of each decode M against the fp64 oracle; for the prefill
 sizes (M = 4096, 8192), a sample of activation rows against all N and all rows
-against a sample of vocabulary columns.  One test per workload, so each
-weight is generated and quantized once; each step prints its case first.
+against a sample of vocabulary columns.  The same for NVFP4 W4A4 (activations
+quantized with a static global input scale) at every decode M and the Qwen
+prefill, and for the FP8 copy at the Qwen prefill.  One test per workload, so
+each weight is generated and quantized once; each step prints its case first.
 """
 
 import numpy as np
 import pytest
 import torch
 
+import oracle.fp8_oracle as F
 import oracle.nvfp4_oracle as O
+import oracle.nvfp4_w4a4_oracle as A
 from nvfp4_w4a16_lm_amd import binding as B
 from nvfp4_w4a16_lm_amd import workloads as wl
 
-from gpu_util import (DEV, assert_quant_equal, check_gemm, dev_bf16, host_bits,
-                      oracle_quantize_threaded)
+from gpu_util import (DEV, assert_quant_equal, check_fp8_gemm, check_gemm, check_w4a4, dev_bf16, dev_u8,
+                      host_bits, oracle_quantize_threaded)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 
@@ -38,12 +42,24 @@ def quantize_both(w, wb):
     return wd, (p, s, g), (op, os_, gs), got
 
 
+def input_scale(xb):
+    """A static global input scale for the activations: their amax/2688, as a
+    checkpoint's calibrated input_scale would hold."""
+    return O.global_scale(O.weight_amax(xb))
+
+
 def decode_checks(w, xb, q, oq, ms):
+    gi = input_scale(xb)
+    gi_dev = torch.tensor(gi, device=DEV)
     for m in ms:
         say(f"[{w.name}] decode GEMM M={m}")
         x = xb[:m]
         y = host_bits(B.nvfp4_w4a16_gemm(dev_bf16(x), *q))
         check_gemm(y, x, *oq, label=f"{w.name} M={m}", argmax_min=0.999)
+        say(f"[{w.name}] W4A4 GEMM M={m}")
+        xp, xs = A.quantize_activations(x, gi)
+        y4 = host_bits(B.nvfp4_w4a4_gemm(dev_u8(xp), dev_u8(xs), gi_dev, *q))
+        check_w4a4(y4, xp, xs, oq[0], oq[1], A.alpha(gi, oq[2]), label=f"{w.name} W4A4 M={m}")
 
 
 def prefill_checks(w, xb, q, oq, m):
@@ -106,13 +122,45 @@ def test_llama3_70b_with_refresh_and_graph():
     check_gemm(host_bits(out), x, op2, os2, gs2, label="70b graph after refresh")
 
 
+def sample_rows_cols(m, n, seed=7):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 126, replace=False)]))
+    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 254, replace=False)]))
+    return rows, cols
+
+
 def test_qwen_prefill():
     w = wl.WORKLOADS["qwen_prefill"]
     say(f"[{w.name}] generating {w.n}x{w.k}")
     wb, xb = wl.weight_bits(w), wl.activation_bits(w)
     say(f"[{w.name}] quantize parity")
-    _, q, oq, _ = quantize_both(w, wb)
+    wd, q, oq, _ = quantize_both(w, wb)
     prefill_checks(w, xb, q, oq, 4096)
+    m = 4096
+    rows, cols = sample_rows_cols(m, w.n)
+    rt, ct = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
+
+    say(f"[{w.name}] W4A4 prefill M={m}")
+    gi = input_scale(xb[:m])
+    xp, xs = A.quantize_activations(xb[:m], gi)
+    y4 = B.nvfp4_w4a4_gemm(dev_u8(xp), dev_u8(xs), torch.tensor(gi, device=DEV), *q)
+    torch.cuda.synchronize()
+    a = A.alpha(gi, oq[2])
+    check_w4a4(host_bits(y4[rt]), xp[rows], xs[rows], oq[0], oq[1], a, label="qwen W4A4 rows")
+    check_w4a4(host_bits(y4[:, ct]), xp, xs, oq[0][cols], oq[1][cols], a, label="qwen W4A4 cols", argmax_min=0.0)
+    del y4
+
+    say(f"[{w.name}] FP8 copy: weight quantization parity + prefill M={m}")
+    qw, sw = B.nvfp4_fp8_quantize_rows(wd)
+    torch.cuda.synchronize()
+    owq, ows = F.quantize_rows(wb)
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), ows.view(np.uint32))
+    assert np.array_equal(qw.view(torch.uint8).cpu().numpy(), owq)
+    xq, xsc = F.quantize_rows(xb[:m])
+    y8 = B.nvfp4_fp8_gemm(dev_u8(xq), torch.from_numpy(xsc).to(DEV), dev_u8(owq), torch.from_numpy(ows).to(DEV))
+    torch.cuda.synchronize()
+    check_fp8_gemm(host_bits(y8[rt]), xq[rows], xsc[rows], owq, ows, label="qwen FP8 rows")
+    check_fp8_gemm(host_bits(y8[:, ct]), xq, xsc, owq[cols], ows[cols], label="qwen FP8 cols", argmax_min=0.0)
 
 
 def test_heavy_tail():
