@@ -30,6 +30,18 @@
 //   p ^ ((r >> 2) & 3), so 8 consecutive lanes read 8 different bank groups.
 //   Pieces past K are zero in both operands.  Epilogue: acc * s_x[m] *
 //   s_w[n] (+ bias[n]) in float32, one rounding to bf16.
+// fp8_prefill_kernel (M > 64, K >= 64, K % 64 == 0): a 256 x 256 output tile per
+//   workgroup of 4 wavefronts (2 x 2, 128 x 128 each, v_mfma_f32_32x32x16_fp8_fp8
+//   with the accumulators of 4 x 4 MFMA tiles in registers).  K is walked in
+//   64-byte steps; both operand tiles (256 rows x 64 bytes each) arrive by
+//   direct-to-LDS copies two steps ahead into a ring of three buffers, so
+//   each step waits only for its own copies, and one barrier per step both
+//   publishes the next tile and frees the buffer the copy after it refills.
+//   Rows are 64 bytes, 16-byte piece p of row r at slot p ^ ((r >> 2) & 3).
+//   Lane (r, h) = (l % 32, l / 32) reads pieces h and h + 2 of its row of
+//   each operand; MFMA step (c, j) uses bytes 8 j .. 8 j + 7 of piece
+//   h + 2 c (the same k order for both operands).  The output tile goes
+//   through LDS for row-contiguous 16-byte stores.
 #include <algorithm>
 
 #include "nvfp4_device.hpp"
@@ -216,6 +228,167 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t* __restrict
   }
 }
 
+typedef float fp8_f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* fp8_lds_ptr_t;
+constexpr int kFp8WaitVm0 = 0x0F70;                    // s_waitcnt vmcnt(0) alone
+constexpr int kFp8PT = 256;                            // prefill tile (rows of each operand)
+constexpr int kFp8PStep = kFp8PT * 64;                 // bytes per operand per 64-k step
+constexpr int kFp8PBuf = 2 * kFp8PStep;                // one ring buffer: weights, then activations
+constexpr int kFp8OP = kFp8PT + 8;                     // bf16 per row of the output staging tile
+constexpr int kFp8PLds = (3 * kFp8PBuf > kFp8PT * kFp8OP * 2) ? 3 * kFp8PBuf : kFp8PT * kFp8OP * 2;
+constexpr int kFp8WaitVm8 = 0x0F78;                    // s_waitcnt vmcnt(8) alone
+
+// Workgroup barrier for the copy ring.  __syncthreads() would also wait for
+// every outstanding copy (vmcnt(0)), including the prefetch that must stay in
+// flight; here the caller has already waited for the copies that matter, and
+// every LDS read before the barrier has been consumed by an MFMA (so its
+// lgkmcnt is drained).  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __restrict__ xq,
+                                                             const float* __restrict__ xs, int M, int K,
+                                                             const uint8_t* __restrict__ wq,
+                                                             const float* __restrict__ ws, int N,
+                                                             const uint16_t* __restrict__ bias,
+                                                             uint16_t* __restrict__ y, int m_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFp8PLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int mt = blockIdx.x % m_tiles, nt = blockIdx.x / m_tiles;
+  const int n0 = nt * kFp8PT, m0 = mt * kFp8PT;
+  const int nsteps = K / 64;
+
+  // copies: instruction i of wavefront w fills rows 16 (4 i + w) .. + 15 of an
+  // operand tile; lane l fills slot l & 3 of row 16 (4 i + w) + (l >> 2), i.e.
+  // piece (l & 3) ^ ((l >> 4) & 3)
+  const int cpiece = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint8_t* wsrc[4];
+  const uint8_t* xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * (4 * i + wave) + (lane >> 2);
+    wsrc[i] = wq + (int64_t)min(n0 + row, N - 1) * K + 16 * cpiece;
+    xsrc[i] = xq + (int64_t)min(m0 + row, M - 1) * K + 16 * cpiece;
+  }
+  auto copy_step = [&](int st) __attribute__((always_inline)) {
+    uint8_t* const buf = lds + (st % 3) * kFp8PBuf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + 64 * st), (fp8_lds_ptr_t)(buf + 1024 * (4 * i + wave)),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + 64 * st),
+                                       (fp8_lds_ptr_t)(buf + kFp8PStep + 1024 * (4 * i + wave)), 16, 0, 0);
+    }
+  };
+  // fragment reads: row 128 wn + 32 i + r of the weight tile, 128 wm + 32 j + r of the activation tile
+  const int r = lane & 31, h = lane >> 5;
+  auto slot = [&](int row, int p) { return row * 64 + 16 * (p ^ ((row >> 2) & 3)); };
+
+  fp8_f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const uint8_t* const wb = lds + (st % 3) * kFp8PBuf;
+    const uint8_t* const xb = wb + kFp8PStep;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4*>(wb + slot(128 * wn + 32 * i + r, h + 2 * c));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(xb + slot(128 * wm + 32 * j + r, h + 2 * c));
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const long a8 = (long)(((uint64_t)af[i][2 * jj + 1] << 32) | af[i][2 * jj]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const long b8 = (long)(((uint64_t)bf[j][2 * jj + 1] << 32) | bf[j][2 * jj]);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a8, b8, acc[i][j], 0, 0, 0);
+          }
+        }
+    }
+  };
+
+  // The waits sit on straight-line paths (no join before a barrier), so each
+  // barrier keeps the one step still in flight outstanding.
+  copy_step(0);
+  if (nsteps > 1) {
+    copy_step(1);
+    __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);         // step 0 has landed (step 1 may fly)
+    ring_barrier();
+  } else {
+    __builtin_amdgcn_s_waitcnt(kFp8WaitVm0);
+    ring_barrier();
+  }
+  int st = 0;
+  for (; st + 2 < nsteps; ++st) {
+    copy_step(st + 2);                                // into the buffer step st - 1 used
+    compute(st);
+    __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);         // step st + 1 has landed
+    ring_barrier();                                   // ... for every wavefront; step st is no longer read
+  }
+  if (st + 1 < nsteps) {
+    compute(st);
+    __builtin_amdgcn_s_waitcnt(kFp8WaitVm0);
+    ring_barrier();
+    ++st;
+  }
+  compute(st);
+  __syncthreads();                                    // the ring is free for the output tile
+
+  // epilogue: y[m][n] = bf16(acc * s_x[m] * s_w[n] + bias[n]) through an LDS tile [m][n]
+  uint16_t (*out)[kFp8OP] = reinterpret_cast<uint16_t (*)[kFp8OP]>(lds);
+  float sx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sx[j] = xs[min(m0 + 128 * wm + 32 * j + r, M - 1)];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // accumulators 4q..4q+3 of MFMA row-tile i: 4 consecutive n, shared by the 4 column tiles
+      const int nl = 128 * wn + 32 * i + 8 * q + 4 * h;
+      float sw[4], bv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int nn = min(n0 + nl + v, N - 1);
+        sw[v] = ws[nn];
+        bv[v] = bias != nullptr ? __uint_as_float((uint32_t)bias[nn] << 16) : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ml = 128 * wm + 32 * j + r;
+        uint32_t hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) hv[v] = f32_to_bf16_rne(acc[i][j][4 * q + v] * sx[j] * sw[v] + bv[v]);
+        *reinterpret_cast<uint2*>(&out[ml][nl]) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      }
+    }
+  __syncthreads();
+#pragma unroll 4
+  for (int it = 0; it < kFp8PT * kFp8PT / 8 / 256; ++it) {
+    const int lin = it * 256 + tid;
+    const int ml = lin >> 5, c = lin & 31;
+    const int m = m0 + ml, n = n0 + 8 * c;
+    if (m >= M || n >= N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&out[ml][8 * c]);
+    uint16_t* dst = y + (int64_t)m * N + n;
+    if ((N & 7) == 0 && n + 8 <= N) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      const uint16_t* hvv = reinterpret_cast<const uint16_t*>(&out[ml][8 * c]);
+      for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = hvv[e];
+    }
+  }
+}
+
 hipError_t launch_fp8_quant_rows(const void* a, int64_t R, int64_t K, uint8_t* q, float* scales,
                                  hipStream_t stream) {
   const int64_t blocks = std::min<int64_t>((R + 3) / 4, 65536);
@@ -237,6 +410,11 @@ static hipError_t fp8_gemm_launch(const uint8_t* xq, const float* xs, int M, int
 hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
                            const float* ws, int64_t N, const void* bias, void* y, hipStream_t stream) {
   const int m = (int)M, k = (int)K, n = (int)N;
+  if (M > 64 && K >= 64 && K % 64 == 0) {
+    const int m_tiles = (int)((M + kFp8PT - 1) / kFp8PT), n_tiles = (int)((N + kFp8PT - 1) / kFp8PT);
+    return launch_kernel((const void*)fp8_prefill_kernel, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), stream,
+                         xq, xs, m, k, wq, ws, n, (const uint16_t*)bias, (uint16_t*)y, m_tiles);
+  }
   switch (std::min<int64_t>((M + 15) / 16, 8)) {
     case 1: return fp8_gemm_launch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     case 2: return fp8_gemm_launch<2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
