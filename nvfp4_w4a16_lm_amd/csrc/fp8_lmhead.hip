@@ -230,12 +230,15 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t* __restrict
 
 typedef float fp8_f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* fp8_lds_ptr_t;
+typedef int fp8_i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kFp8UnitScales = 0x7F7F7F7F;           // E8M0 block scales of 1 (2^0) in every byte
 constexpr int kFp8WaitVm0 = 0x0F70;                    // s_waitcnt vmcnt(0) alone
 constexpr int kFp8PT = 256;                            // prefill tile (rows of each operand)
 constexpr int kFp8PStep = kFp8PT * 64;                 // bytes per operand per 64-k step
 constexpr int kFp8PBuf = 2 * kFp8PStep;                // one ring buffer: weights, then activations
 constexpr int kFp8OP = kFp8PT + 8;                     // bf16 per row of the output staging tile
-constexpr int kFp8PLds = (3 * kFp8PBuf > kFp8PT * kFp8OP * 2) ? 3 * kFp8PBuf : kFp8PT * kFp8OP * 2;
+constexpr int kFp8PRing = 4;                          // ring buffers (copies run 3 steps ahead)
+constexpr int kFp8PLds = (kFp8PRing * kFp8PBuf > kFp8PT * kFp8OP * 2) ? kFp8PRing * kFp8PBuf : kFp8PT * kFp8OP * 2;
 constexpr int kFp8WaitVm8 = 0x0F78;                    // s_waitcnt vmcnt(8) alone
 
 // Workgroup barrier for the copy ring.  __syncthreads() would also wait for
@@ -271,19 +274,28 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
     wsrc[i] = wq + (int64_t)min(n0 + row, N - 1) * K + 16 * cpiece;
     xsrc[i] = xq + (int64_t)min(m0 + row, M - 1) * K + 16 * cpiece;
   }
-  auto copy_step = [&](int st) __attribute__((always_inline)) {
-    uint8_t* const buf = lds + (st % 3) * kFp8PBuf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + 64 * st), (fp8_lds_ptr_t)(buf + 1024 * (4 * i + wave)),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + 64 * st),
+  // copy instruction c (0..7) of step st: c < 4 weight rows, c >= 4 activation
+  // rows; steps past the last re-read the last step (never used)
+  auto copy_one = [&](int st, int c) __attribute__((always_inline)) {
+    uint8_t* const buf = lds + (st % kFp8PRing) * kFp8PBuf;
+    const int64_t off = 64 * (int64_t)min(st, nsteps - 1);
+    const int i = c & 3;
+    if (c < 4)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + off), (fp8_lds_ptr_t)(buf + 1024 * (4 * i + wave)), 16,
+                                       0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + off),
                                        (fp8_lds_ptr_t)(buf + kFp8PStep + 1024 * (4 * i + wave)), 16, 0, 0);
-    }
   };
   // fragment reads: row 128 wn + 32 i + r of the weight tile, 128 wm + 32 j + r of the activation tile
   const int r = lane & 31, h = lane >> 5;
   auto slot = [&](int row, int p) { return row * 64 + 16 * (p ^ ((row >> 2) & 3)); };
+  // the 32 bytes (pieces 2 h, 2 h + 1) of one row that lane half h feeds to a 32x32x64 MFMA
+  auto frag32 = [&](const uint8_t* base, int row) __attribute__((always_inline)) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + slot(row, 2 * h));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + slot(row, 2 * h + 1));
+    return fp8_i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
 
   fp8_f32x16 acc[4][4];
 #pragma unroll
@@ -293,55 +305,49 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto compute = [&](int st) __attribute__((always_inline)) {
-    const uint8_t* const wb = lds + (st % 3) * kFp8PBuf;
-    const uint8_t* const xb = wb + kFp8PStep;
+  typedef fp8_i32x8 Frag[4];
+  auto read_frags = [&](int st, int f, Frag& a, Frag& b) __attribute__((always_inline)) {
+    const uint8_t* const wb = lds + (st % kFp8PRing) * kFp8PBuf;
+    if (f < 4)
+      a[f] = frag32(wb, 128 * wn + 32 * f + r);
+    else
+      b[f - 4] = frag32(wb + kFp8PStep, 128 * wm + 32 * (f - 4) + r);
+  };
+  // One k step st: 16 MFMAs on the fragments (ca, cb) of step st.  Between
+  // them, the fragments of step st + 1 are read into (na, nb) and the copies
+  // of step st + 3 are issued into the buffer step st - 1 used.  Then the
+  // copies of step st + 2 are waited for (the 8 of step st + 3 stay in
+  // flight) and the barrier publishes them.
+  auto kstep = [&](int st, const Frag& ca, const Frag& cb, Frag& na, Frag& nb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      u32x4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4*>(wb + slot(128 * wn + 32 * i + r, h + 2 * c));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(xb + slot(128 * wm + 32 * j + r, h + 2 * c));
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long a8 = (long)(((uint64_t)af[i][2 * jj + 1] << 32) | af[i][2 * jj]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const long b8 = (long)(((uint64_t)bf[j][2 * jj + 1] << 32) | bf[j][2 * jj]);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a8, b8, acc[i][j], 0, 0, 0);
-          }
-        }
+    for (int q = 0; q < 16; ++q) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ca[q >> 2], cb[q & 3], acc[q >> 2][q & 3], 0,
+                                                                           0, 0, kFp8UnitScales, 0, kFp8UnitScales);
+      if (q < 8)
+        read_frags(st + 1, q, na, nb);
+      else
+        copy_one(st + 3, q - 8);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);
+    ring_barrier();
   };
 
-  // The waits sit on straight-line paths (no join before a barrier), so each
-  // barrier keeps the one step still in flight outstanding.
-  copy_step(0);
-  if (nsteps > 1) {
-    copy_step(1);
-    __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);         // step 0 has landed (step 1 may fly)
-    ring_barrier();
-  } else {
-    __builtin_amdgcn_s_waitcnt(kFp8WaitVm0);
-    ring_barrier();
-  }
+  // prologue: steps 0..2 in flight, then steps 0 and 1 landed and step 0's fragments read
+#pragma unroll
+  for (int c = 0; c < 24; ++c) copy_one(c >> 3, c & 7);
+  __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);
+  ring_barrier();
+  Frag fa, fb, ga, gb;
+#pragma unroll
+  for (int f = 0; f < 8; ++f) read_frags(0, f, fa, fb);
   int st = 0;
-  for (; st + 2 < nsteps; ++st) {
-    copy_step(st + 2);                                // into the buffer step st - 1 used
-    compute(st);
-    __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);         // step st + 1 has landed
-    ring_barrier();                                   // ... for every wavefront; step st is no longer read
+  for (; st + 2 <= nsteps; st += 2) {
+    kstep(st, fa, fb, ga, gb);
+    kstep(st + 1, ga, gb, fa, fb);
   }
-  if (st + 1 < nsteps) {
-    compute(st);
-    __builtin_amdgcn_s_waitcnt(kFp8WaitVm0);
-    ring_barrier();
-    ++st;
-  }
-  compute(st);
+  if (st < nsteps) kstep(st, fa, fb, ga, gb);
+  __builtin_amdgcn_s_waitcnt(kFp8WaitVm0);           // the last (unused) copies land before LDS is reused
   __syncthreads();                                    // the ring is free for the output tile
 
   // epilogue: y[m][n] = bf16(acc * s_x[m] * s_w[n] + bias[n]) through an LDS tile [m][n]
