@@ -90,6 +90,21 @@ def test_gemm_with_bias_end_to_end():
     check_fp8_gemm(host_bits(y), xq, xs, wq, ws, bias, label="bias")
 
 
+@pytest.mark.parametrize("m,n,k", [(65, 300, 64), (300, 515, 192), (257, 1027, 320), (513, 260, 128), (300, 100, 256)])
+def test_prefill_tiles_odd_step_counts_with_bias(m, n, k):
+    """M > 64 with K % 64 == 0 (the 256 x 256 tile kernel): 1, 2, 3, 4 and 5
+    64-byte k steps (odd counts end on the loop's tail step), ragged M and N,
+    N below one tile, several M tiles, and a bias."""
+    w = wl.random_weight_bits(n, k, sigma=0.02, seed=n * 3 + k)
+    x = wl.random_activation_bits(m, k, seed=m * 5 + k)
+    bias = wl.random_weight_bits(1, n, sigma=0.5, seed=n + 1)[0]
+    wq, ws = F.quantize_rows(w)
+    xq, xs = F.quantize_rows(x)
+    y = B.nvfp4_fp8_gemm(dev_u8(xq), torch.from_numpy(xs).to(DEV), dev_u8(wq), torch.from_numpy(ws).to(DEV),
+                         bias=dev_bf16(bias))
+    check_fp8_gemm(host_bits(y), xq, xs, wq, ws, bias, label=f"prefill M={m} N={n} K={k}")
+
+
 def test_gemm_empty_batch_and_scale_bits():
     w = wl.random_weight_bits(64, 32, seed=5)
     qw, sw = B.nvfp4_fp8_quantize_rows(dev_bf16(w))

@@ -40,7 +40,7 @@ def test_tiny_workload_end_to_end():
 # K = 128 (a single weight superblock) exercise both prefill kernels
 @pytest.mark.parametrize("m", [1, 2, 4, 15, 16, 17, 33, 48, 64, 65, 100, 128, 129, 300])
 @pytest.mark.parametrize("n,k", [(1024, 512), (1027, 272), (77, 4096), (200, 48), (5, 16),
-                                 (300, 7168), (64, 8448), (515, 320), (300, 128)])
+                                 (300, 7168), (64, 8448), (515, 320), (300, 128), (260, 64), (100, 192)])
 def test_shapes(m, n, k):
     w, packed, scales, gs, q = setup(n, k, seed=m)
     x = wl.random_activation_bits(m, k, seed=n)
