@@ -145,7 +145,7 @@ def check_fp8_gemm(y_bits, xq, xs, wq, ws, bias_bits=None, label="", argmax_min=
     yabs = F.gemm_abs_ref(xq, xs, wq, ws, bias_bits)
     xn = np.linalg.norm(F.e4m3_decode_signed(xq) * np.asarray(xs, np.float64)[:, None], axis=1)
     wn = np.linalg.norm(F.e4m3_decode_signed(wq) * np.asarray(ws, np.float64)[:, None], axis=1)
-    ns = 1e-3 * xn[:, None] * wn[None, :] + 2.0 ** -9 * np.abs(y64)
+    ns = 1e-3 * xn[:, None] * wn[None, :] + 2.0 ** -8 * np.abs(y64)
     assert np.all(np.abs(y - y64) <= ns), f"{label}: north-star bound"
     k = xq.shape[1]
     acc = (2.0 ** -14 + (k + 4) * 2.0 ** -24) * yabs
@@ -167,7 +167,7 @@ def check_w4a4(y_bits, xp, xs, wp, ws, a, bias_bits=None, label="", argmax_min=0
     yabs = A.gemm_abs_ref(xp, xs, wp, ws, a, bias_bits)
     xn = np.linalg.norm(A.block_values(xp, xs), axis=1)
     wn = np.linalg.norm(A.block_values(wp, ws), axis=1)
-    ns = 1e-3 * float(a) * xn[:, None] * wn[None, :] + 2.0 ** -9 * np.abs(y64)
+    ns = 1e-3 * float(a) * xn[:, None] * wn[None, :] + 2.0 ** -8 * np.abs(y64)
     err = np.abs(y - y64)
     assert np.all(err <= ns), f"{label}: north-star bound"
     k = xp.shape[1] * 2
