@@ -118,13 +118,126 @@ def cpu_baseline(wl, w, w_bits, x_bits, ms, budget_s: float):
     }
 
 
+def moe_active_bytes(ids, E: int, H: int, I: int):
+    """NVFP4 bytes of the experts that receive at least one pair: (w13, w2)."""
+    import numpy as np
+
+    active = int(np.unique(ids).size)
+    return active * 2 * I * H * (0.5 + 0.0625), active * H * I * (0.5 + 0.0625)
+
+
+def bench_moe(args, mw, dev) -> int:
+    """The W4A16 expert layer (routing, grouped GEMM with w13, SiLU-and-mul,
+    grouped GEMM with w2, weighted combine) at each token count of the
+    workload.  value = algorithmic HBM bytes of the layer over its time: the
+    NVFP4 bytes of the experts that receive a pair, x, the bf16 intermediates
+    written and read once, and the output."""
+    import numpy as np
+    import torch
+
+    from nvfp4_w4a16_lm_amd import binding as B
+    from nvfp4_w4a16_lm_amd import workloads as wl
+
+    E, H, I, topk = mw.experts, mw.hidden, mw.inter, mw.topk
+    t0 = time.perf_counter()
+    w13_bits = wl.moe_expert_bits(2 * I, H, E, mw.sigma, mw.cfg, 10)
+    w2_bits = wl.moe_expert_bits(H, I, E, mw.sigma, mw.cfg, 1000)
+    tmax = max(mw.tokens)
+    x_bits = wl.normal_bits(tmax, H, 1.0, (mw.cfg, 2))
+    print(f"# MoE inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def quant_experts(bits, rows, k):
+        packed = torch.empty((E, rows, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((E, rows, k // 16), dtype=torch.uint8, device=dev)
+        gs = torch.empty((E,), dtype=torch.float32, device=dev)
+        for e in range(E):
+            we = to_dev(bits[e])
+            B.nvfp4_refresh_inplace(we, packed[e], scales[e], gs[e])
+            del we
+        return packed, scales, gs
+
+    w13 = quant_experts(w13_bits, 2 * I, H)
+    w2 = quant_experts(w2_bits, H, I)
+    del w13_bits, w2_bits
+    X = to_dev(x_bits)
+    torch.cuda.synchronize()
+    per_t = {}
+    for T in mw.tokens:
+        ids_np, tw_np = wl.moe_routing(T, E, topk, mw.cfg)
+        ids = torch.from_numpy(ids_np).to(dev)
+        tw = torch.from_numpy(tw_np).to(dev)
+        x = X[:T]
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((int(B.load_library().nvfp4_moe_workspace_bytes(T, topk, E, H, I)),), dtype=torch.uint8,
+                         device=dev)
+        h = torch.empty((T * topk, 2 * I), dtype=torch.bfloat16, device=dev)
+        gws = torch.empty((int(B.load_library().nvfp4_moe_gemm_workspace_bytes(T * topk, E)) + 16,),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            B.nvfp4_moe_w4a16_forward(x, ids, tw, w13, w2, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        evf, evg = [], []
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            c = torch.cuda.Event(enable_timing=True)
+            a.record()
+            B.nvfp4_moe_w4a16_forward(x, ids, tw, w13, w2, out=out, workspace=ws)
+            b.record()
+            B.nvfp4_moe_w4a16_gemm(x, ids, topk, *w13, out=h, workspace=gws)
+            c.record()
+            evf.append((a, b))
+            evg.append((b, c))
+        torch.cuda.synchronize()
+        tf = float(np.mean([a.elapsed_time(b) for a, b in evf]))
+        tg = float(np.mean([a.elapsed_time(b) for a, b in evg]))
+        b13, b2 = moe_active_bytes(ids_np, E, H, I)
+        P = T * topk
+        layer_bytes = b13 + b2 + 2 * T * H + 2 * P * (2 * I) * 2 + 2 * P * I * 2 + 2 * P * H * 2 + 2 * T * H
+        g1_bytes = b13 + 2 * T * H + 2 * P * 2 * I
+        per_t[T] = {"ms": tf, "TB/s": layer_bytes / (tf * 1e-3) / 1e12, "bytes": layer_bytes,
+                    "experts_active": int(np.unique(ids_np).size),
+                    "grouped_gemm_w13_ms": tg, "grouped_gemm_w13_TB/s": g1_bytes / (tg * 1e-3) / 1e12,
+                    "grouped_gemm_w13_bytes": g1_bytes}
+    total_bytes = sum(v["bytes"] for v in per_t.values())
+    total_ms = sum(v["ms"] for v in per_t.values())
+    tdom = max(per_t, key=lambda t: per_t[t]["grouped_gemm_w13_ms"])
+    ach = per_t[tdom]["grouped_gemm_w13_bytes"] / (per_t[tdom]["grouped_gemm_w13_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": total_bytes / (total_ms * 1e-3) / 1e12,
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x nvfp4 (fp32 accumulate)",
+        "data": "synthetic (seeded; no trained weights)",
+        "config": {"workload": mw.name, "description": mw.description, "E": E, "H": H, "I": I, "topk": topk,
+                   "T": list(mw.tokens), "step": "nvfp4_moe_w4a16_forward at each T"},
+        "per_op": {f"moe_forward_t{t}": v for t, v in per_t.items()},
+        "roofline": {"op": f"nvfp4_moe_w4a16_gemm (w13) T={tdom}", "kernels": "moe_route + moe_gemm",
+                     "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBPS, "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b",
-                    help="llama3_8b (default), llama3_70b, qwen_prefill, heavy_tail, tiny")
+                    help="llama3_8b (default), llama3_70b, qwen_prefill, heavy_tail, tiny; "
+                         "moe_8x4096 / moe_small time the W4A16 expert layer instead")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=3, help="rotating quantized-weight copies")
@@ -158,6 +271,8 @@ def main() -> int:
         return 0
     B.load_library()
     dev = torch.device("cuda:0")
+    if args.workload in wl.MOE_WORKLOADS:
+        return bench_moe(args, wl.MOE_WORKLOADS[args.workload], dev)
     w = wl.WORKLOADS[args.workload]
     n, k, ms = w.n, w.k, w.ms
     t0 = time.perf_counter()

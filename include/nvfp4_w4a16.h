@@ -271,6 +271,78 @@ nvfp4_status nvfp4_w4a4_gemm(const uint8_t* x_packed, const uint8_t* x_scales, c
                              const float* global_scale, int64_t N, const void* bias, void* workspace, void* y,
                              void* stream);
 
+/*
+ * Mixture of experts, W4A16 NVFP4 (vLLM modelopt.py, ModelOptNvFp4FusedMoE with
+ * use_a16: per-expert NVFP4 weights w13 [E, 2I, H/2] / scales [E, 2I, H/16] and
+ * w2 [E, H, I/2] / scales [E, H, I/16], one float32 global scale per expert and
+ * matrix -- for w13 the w1 column of w13_weight_scale_2 -- and routing by
+ * topk_ids / topk_weights as apply() receives them).
+ *
+ * Pair p = t * topk + j is token t's j-th routed expert topk_ids[t * topk + j].
+ * A pair whose id lies outside [0, E) is outside the contract: it is counted
+ * into *invalid_pairs (when non-NULL) and its GEMM output row is zero.
+ *
+ * nvfp4_moe_gemm_workspace_bytes -- workspace of nvfp4_moe_w4a16_gemm: the
+ * routing table, 4 * (round_up(E + 2, 4) + round_up(P, 4)) bytes (host helper;
+ * 0 for P < 0 or E < 1).
+ */
+int64_t nvfp4_moe_gemm_workspace_bytes(int64_t P, int64_t E);
+
+/*
+ * nvfp4_moe_w4a16_gemm -- the grouped expert GEMM:
+ *   y[p, n] = bf16_rne( gs[e] * sum_k x[p / row_div, k] * E2M1(code_e[n, k]) * e4m3(scale_e[n, k/16]) ),
+ *   e = topk_ids[p], float32 accumulation of exact products.
+ *
+ *   x              in  bf16 [x_rows, K]; row_div = topk reads token rows (the first
+ *                      GEMM), row_div = 1 reads one row per pair (the second);
+ *                      x_rows >= ceil(P / row_div)
+ *   topk_ids       in  int32 [P]
+ *   packed, scales in  [E, N, K/2] uint8 / [E, N, K/16] e4m3fn, the per-expert layout
+ *                      of the pages (packed 16-byte aligned)
+ *   global_scales  in  float32 [E]
+ *   workspace      tmp nvfp4_moe_gemm_workspace_bytes(P, E) bytes, 16-byte aligned
+ *   y              out bf16 [P, N]
+ *   invalid_pairs  out optional uint32 (NULL = not reported)
+ * An expert with no pair reads none of its weights.  P == 0 enqueues nothing.
+ */
+nvfp4_status nvfp4_moe_w4a16_gemm(const void* x, int64_t x_rows, int64_t K, const int32_t* topk_ids, int64_t P,
+                                  int64_t row_div, const uint8_t* packed, const uint8_t* scales,
+                                  const float* global_scales, int64_t E, int64_t N, void* workspace, void* y,
+                                  uint32_t* invalid_pairs, void* stream);
+
+/*
+ * nvfp4_moe_silu_and_mul -- a[p, i] = bf16_rne( silu(h[p, i]) * h[p, I + i] ),
+ * silu(g) = g / (1 + exp(-g)) in float32: the act-and-mul layout [w1; w3] of
+ * w13.  h bf16 [P, 2I], a bf16 [P, I], I % 8 == 0, both 16-byte aligned.
+ */
+nvfp4_status nvfp4_moe_silu_and_mul(const void* h, int64_t P, int64_t I, void* a, void* stream);
+
+/*
+ * nvfp4_moe_combine -- out[t, n] = bf16_rne( sum_j topk_weights[t, j] * o[t * topk + j, n] ),
+ * float32 in slot order j = 0, 1, ...  o bf16 [T * topk, H], topk_weights float32
+ * [T, topk], out bf16 [T, H], H % 8 == 0, o and out 16-byte aligned.
+ */
+nvfp4_status nvfp4_moe_combine(const void* o, const float* topk_weights, int64_t T, int64_t topk, int64_t H,
+                               void* out, void* stream);
+
+/*
+ * nvfp4_moe_workspace_bytes -- workspace of nvfp4_moe_w4a16_forward: the routing
+ * table, then h [P, 2I], a [P, I] and o [P, H] in bf16, each rounded up to 256 bytes
+ * (host helper; 0 for invalid sizes).
+ *
+ * nvfp4_moe_w4a16_forward -- the whole W4A16 expert layer on bf16 x [T, H]:
+ * routing, h = grouped GEMM with w13, a = silu_and_mul(h), o = grouped GEMM
+ * with w2, out = combine(o, topk_weights); each stage as the calls above, h, a
+ * and o rounded to bf16.  out bf16 [T, H].  T == 0 enqueues nothing.
+ */
+int64_t nvfp4_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I);
+nvfp4_status nvfp4_moe_w4a16_forward(const void* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                     const float* topk_weights, int64_t topk, const uint8_t* w13_packed,
+                                     const uint8_t* w13_scales, const float* w13_global_scales,
+                                     const uint8_t* w2_packed, const uint8_t* w2_scales,
+                                     const float* w2_global_scales, int64_t E, int64_t I, void* workspace,
+                                     void* out, uint32_t* invalid_pairs, void* stream);
+
 /* Host-side helpers (no device work). */
 const char* nvfp4_status_string(int status);   /* static string for a status code        */
 const char* nvfp4_last_hip_error(void);        /* last HIP error text of this thread, or "" */

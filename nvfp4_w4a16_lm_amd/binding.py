@@ -14,7 +14,7 @@ import os
 import torch
 
 LIB_NAME = "libnvfp4_w4a16.so"
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS_NAMES = {
     0: "NVFP4_OK",
@@ -39,6 +39,8 @@ EXPORTED = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
             "nvfp4_fill_scale_sentinel", "nvfp4_import_checkpoint",
             "nvfp4_fp8_quantize_rows", "nvfp4_fp8_gemm",
             "nvfp4_quantize_activations", "nvfp4_w4a4_workspace_bytes", "nvfp4_w4a4_gemm",
+            "nvfp4_moe_gemm_workspace_bytes", "nvfp4_moe_w4a16_gemm", "nvfp4_moe_silu_and_mul",
+            "nvfp4_moe_combine", "nvfp4_moe_workspace_bytes", "nvfp4_moe_w4a16_forward",
             "nvfp4_status_string", "nvfp4_last_hip_error", "nvfp4_abi_version")
 
 
@@ -92,6 +94,19 @@ def load_library() -> ctypes.CDLL:
     lib.nvfp4_w4a4_workspace_bytes.restype = i64
     lib.nvfp4_w4a4_gemm.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, vp, vp]
     lib.nvfp4_w4a4_gemm.restype = ctypes.c_int
+    lib.nvfp4_moe_gemm_workspace_bytes.argtypes = [i64, i64]
+    lib.nvfp4_moe_gemm_workspace_bytes.restype = i64
+    lib.nvfp4_moe_w4a16_gemm.argtypes = [vp, i64, i64, vp, i64, i64, vp, vp, vp, i64, i64, vp, vp, vp, vp]
+    lib.nvfp4_moe_w4a16_gemm.restype = ctypes.c_int
+    lib.nvfp4_moe_silu_and_mul.argtypes = [vp, i64, i64, vp, vp]
+    lib.nvfp4_moe_silu_and_mul.restype = ctypes.c_int
+    lib.nvfp4_moe_combine.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    lib.nvfp4_moe_combine.restype = ctypes.c_int
+    lib.nvfp4_moe_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.nvfp4_moe_workspace_bytes.restype = i64
+    lib.nvfp4_moe_w4a16_forward.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp,
+                                            vp, vp]
+    lib.nvfp4_moe_w4a16_forward.restype = ctypes.c_int
     lib.nvfp4_status_string.argtypes = [ctypes.c_int]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_last_hip_error.argtypes = []
@@ -358,4 +373,148 @@ def nvfp4_w4a4_gemm(x_packed: torch.Tensor, x_scales: torch.Tensor, input_global
            lib.nvfp4_w4a4_gemm(_ptr(x_packed), _ptr(x_scales), _ptr(input_global_scale), m, k, _ptr(packed),
                                _ptr(scales), _ptr(global_scale), n, _ptr(bias), _ptr(workspace), _ptr(out),
                                _stream_of(packed, stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Mixture of experts (W4A16)
+# ---------------------------------------------------------------------------
+
+def _check_experts(packed: torch.Tensor, scales: torch.Tensor, global_scales: torch.Tensor, k: int, dev,
+                   what: str):
+    if packed.dim() != 3 or packed.shape[2] * 2 != k:
+        raise ValueError(f"{what} packed shape {tuple(packed.shape)} does not match K={k}")
+    e, n = packed.shape[0], packed.shape[1]
+    _check_out(packed, (e, n, k // 2), (torch.uint8,), dev, f"{what} packed")
+    _check_out(scales, (e, n, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, f"{what} scales")
+    _check_out(global_scales, (e,), (torch.float32,), dev, f"{what} global_scales")
+    return e, n
+
+
+def _check_ids(topk_ids: torch.Tensor, dev) -> torch.Tensor:
+    if topk_ids.dtype != torch.int32 or topk_ids.device != dev:
+        raise ValueError("topk_ids must be int32 on the weights' device")
+    return topk_ids.contiguous()
+
+
+def moe_collapse_w13_scale2(w13_weight_scale_2: torch.Tensor) -> torch.Tensor:
+    """The per-expert global scale of w13 from its [E, 2] checkpoint tensor: the w1
+    column, with a warning when the w3 column differs (the pages keep one scale
+    for the fused w1/w3 matrix).  A slice and a comparison, no arithmetic."""
+    s = w13_weight_scale_2.reshape(w13_weight_scale_2.shape[0], -1)
+    if s.shape[1] > 1 and not torch.equal(s[:, 0], s[:, 1]):
+        import warnings
+        warnings.warn("w1_weight_scale_2 differs from w3_weight_scale_2; the w1 value serves both, "
+                      "which may reduce accuracy")
+    return s[:, 0].contiguous()
+
+
+def nvfp4_moe_w4a16_gemm(x: torch.Tensor, topk_ids: torch.Tensor, row_div: int, packed: torch.Tensor,
+                         scales: torch.Tensor, global_scales: torch.Tensor, out: torch.Tensor | None = None,
+                         invalid_pairs: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """Grouped expert GEMM: bf16 [P, N], row p = x[p // row_div] . deq(W[topk_ids[p]])^T."""
+    x = _as_bf16_2d(x, "x")
+    rows, k = x.shape
+    dev = x.device
+    e, n = _check_experts(packed, scales, global_scales, k, dev, "expert")
+    ids = _check_ids(topk_ids, dev).reshape(-1)
+    p = ids.numel()
+    if out is None:
+        out = torch.empty((p, n), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_out(out, (p, n), (torch.bfloat16,), dev, "out")
+    if invalid_pairs is not None and (invalid_pairs.numel() != 1 or invalid_pairs.dtype != torch.int32
+                                      or invalid_pairs.device != dev):
+        raise ValueError("invalid_pairs must be one int32 on the device")
+    lib = load_library()
+    need = int(lib.nvfp4_moe_gemm_workspace_bytes(p, e))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+        raise ValueError(f"workspace needs {need} bytes on {dev}")
+    _check("nvfp4_moe_w4a16_gemm",
+           lib.nvfp4_moe_w4a16_gemm(_ptr(x), rows, k, _ptr(ids), p, int(row_div), _ptr(packed), _ptr(scales),
+                                    _ptr(global_scales), e, n, _ptr(workspace), _ptr(out), _ptr(invalid_pairs),
+                                    _stream_of(x, stream)))
+    return out
+
+
+def nvfp4_moe_silu_and_mul(h: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 [P, 2I] -> bf16 [P, I]: silu(h[:, :I]) * h[:, I:]."""
+    h = _as_bf16_2d(h, "h")
+    p, i2 = h.shape
+    if out is None:
+        out = torch.empty((p, i2 // 2), dtype=torch.bfloat16, device=h.device)
+    else:
+        _check_out(out, (p, i2 // 2), (torch.bfloat16,), h.device, "out")
+    lib = load_library()
+    _check("nvfp4_moe_silu_and_mul",
+           lib.nvfp4_moe_silu_and_mul(_ptr(h), p, i2 // 2, _ptr(out), _stream_of(h, stream)))
+    return out
+
+
+def nvfp4_moe_combine(o: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """bf16 [T*topk, H] with float32 weights [T, topk] -> bf16 [T, H]."""
+    o = _as_bf16_2d(o, "o")
+    if topk_weights.dim() != 2 or topk_weights.dtype != torch.float32 or topk_weights.device != o.device:
+        raise ValueError("topk_weights must be float32 [T, topk] on o's device")
+    w = topk_weights.contiguous()
+    t, k = w.shape
+    hdim = o.shape[1]
+    if o.shape[0] != t * k:
+        raise ValueError(f"o has {o.shape[0]} rows, expected T*topk = {t * k}")
+    if out is None:
+        out = torch.empty((t, hdim), dtype=torch.bfloat16, device=o.device)
+    else:
+        _check_out(out, (t, hdim), (torch.bfloat16,), o.device, "out")
+    lib = load_library()
+    _check("nvfp4_moe_combine",
+           lib.nvfp4_moe_combine(_ptr(o), _ptr(w), t, k, hdim, _ptr(out), _stream_of(o, stream)))
+    return out
+
+
+def nvfp4_moe_w4a16_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                            w13: tuple, w2: tuple, out: torch.Tensor | None = None,
+                            invalid_pairs: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """The W4A16 expert layer: bf16 x [T, H] -> bf16 [T, H].  ``w13`` / ``w2`` =
+    (packed, scales, global_scales) with shapes [E, 2I, H/2], [E, 2I, H/16], [E]
+    and [E, H, I/2], [E, H, I/16], [E]."""
+    x = _as_bf16_2d(x, "x")
+    t, hdim = x.shape
+    dev = x.device
+    e, n13 = _check_experts(*w13, hdim, dev, "w13")
+    if w2[0].dim() != 3:
+        raise ValueError("w2 packed must be [E, H, I/2]")
+    i = w2[0].shape[2] * 2
+    e2, n2 = _check_experts(*w2, i, dev, "w2")
+    if n13 != 2 * i or e2 != e or n2 != hdim:
+        raise ValueError(f"w13 [E, {n13}, .] and w2 [{e2}, {n2}, {i // 2}] do not fit H={hdim}")
+    ids = _check_ids(topk_ids, dev)
+    if ids.dim() != 2 or ids.shape[0] != t:
+        raise ValueError("topk_ids must be int32 [T, topk]")
+    topk = ids.shape[1]
+    if tuple(topk_weights.shape) != (t, topk) or topk_weights.dtype != torch.float32 or \
+            topk_weights.device != dev:
+        raise ValueError("topk_weights must be float32 [T, topk] on the device")
+    w = topk_weights.contiguous()
+    if out is None:
+        out = torch.empty((t, hdim), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_out(out, (t, hdim), (torch.bfloat16,), dev, "out")
+    if invalid_pairs is not None and (invalid_pairs.numel() != 1 or invalid_pairs.dtype != torch.int32
+                                      or invalid_pairs.device != dev):
+        raise ValueError("invalid_pairs must be one int32 on the device")
+    lib = load_library()
+    need = int(lib.nvfp4_moe_workspace_bytes(t, topk, e, hdim, i))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+        raise ValueError(f"workspace needs {need} bytes on {dev}")
+    _check("nvfp4_moe_w4a16_forward",
+           lib.nvfp4_moe_w4a16_forward(_ptr(x), t, hdim, _ptr(ids), _ptr(w), topk, _ptr(w13[0]), _ptr(w13[1]),
+                                       _ptr(w13[2]), _ptr(w2[0]), _ptr(w2[1]), _ptr(w2[2]), e, i,
+                                       _ptr(workspace), _ptr(out), _ptr(invalid_pairs), _stream_of(x, stream)))
     return out

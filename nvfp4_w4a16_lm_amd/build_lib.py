@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libnvfp4_w4a16.so"
 ARCH = "gfx950"
 
-SOURCES = ["nvfp4_quant.hip", "nvfp4_decode.hip", "nvfp4_prefill.hip", "nvfp4_import.hip", "fp8_lmhead.hip", "nvfp4_w4a4.hip",
+SOURCES = ["nvfp4_quant.hip", "nvfp4_decode.hip", "nvfp4_prefill.hip", "nvfp4_import.hip", "fp8_lmhead.hip", "nvfp4_w4a4.hip", "nvfp4_moe.hip",
            "nvfp4_api.cpp"]
 
 # Packed-fp32 VALU forms are disabled for all device code.

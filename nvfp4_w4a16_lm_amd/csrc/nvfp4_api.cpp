@@ -214,6 +214,151 @@ nvfp4_status nvfp4_w4a4_gemm(const uint8_t* x_packed, const uint8_t* x_scales, c
   return finish(nvfp4::launch_gemm_prefill(xd, M, K, packed, scales, alpha, N, bias, y, st));
 }
 
+// ---------------------------------------------------------------------------
+// Mixture of experts (W4A16)
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMaxExperts = 65534;               // grid.y of the grouped GEMM is E + 1
+constexpr int64_t kMaxPairs = (int64_t)1 << 28;
+
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+nvfp4_status check_experts(int64_t E, int64_t N, int64_t K) {
+  if (E < 1 || E > kMaxExperts) return NVFP4_ERR_SHAPE;
+  const nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (E * N > kMaxDim || E * N * K > kMaxElems) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nvfp4_moe_gemm_workspace_bytes(int64_t P, int64_t E) {
+  return (P < 0 || E < 1) ? 0 : nvfp4::moe_route_bytes(P, E);
+}
+
+int64_t nvfp4_moe_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I) {
+  if (T < 0 || topk < 1 || E < 1 || H < 0 || I < 0) return 0;
+  const int64_t P = T * topk;
+  return round256(nvfp4::moe_route_bytes(P, E)) + round256(P * 2 * I * 2) + round256(P * I * 2) +
+         round256(P * H * 2);
+}
+
+nvfp4_status nvfp4_moe_w4a16_gemm(const void* x, int64_t x_rows, int64_t K, const int32_t* topk_ids, int64_t P,
+                                  int64_t row_div, const uint8_t* packed, const uint8_t* scales,
+                                  const float* global_scales, int64_t E, int64_t N, void* workspace, void* y,
+                                  uint32_t* invalid_pairs, void* stream) {
+  if (!packed || !scales || !global_scales || (P != 0 && (!x || !topk_ids || !workspace || !y)))
+    return NVFP4_ERR_NULL;
+  nvfp4_status s = check_experts(E, N, K);
+  if (s != NVFP4_OK) return s;
+  if (P < 0 || P > kMaxPairs || row_div < 1 || x_rows < 0 || x_rows > kMaxDim || x_rows * K > kMaxElems ||
+      P * N > kMaxElems || (P + row_div - 1) / row_div > x_rows)
+    return NVFP4_ERR_SHAPE;
+  if (P == 0) return NVFP4_OK;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(packed, 16) || !aligned(global_scales, 4) ||
+      !aligned(topk_ids, 4) || !aligned(workspace, 16) || (invalid_pairs && !aligned(invalid_pairs, 4)))
+    return NVFP4_ERR_ALIGN;
+  const Range ry = span(y, P * N * 2), rw = span(workspace, nvfp4_moe_gemm_workspace_bytes(P, E)),
+              ri = span(invalid_pairs, invalid_pairs ? 4 : 0);
+  const Range ins[] = {span(x, x_rows * K * 2), span(topk_ids, P * 4), span(packed, E * N * K / 2),
+                       span(scales, E * N * K / 16), span(global_scales, E * 4)};
+  if (overlap(ry, rw) || overlap(ry, ri) || overlap(rw, ri)) return NVFP4_ERR_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(ry, r) || overlap(rw, r) || overlap(ri, r)) return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  const hipStream_t st = (hipStream_t)stream;
+  int32_t* const route = static_cast<int32_t*>(workspace);
+  hipError_t e = nvfp4::launch_moe_route(topk_ids, P, E, route, invalid_pairs, st);
+  if (e != hipSuccess) return finish(e);
+  return finish(nvfp4::launch_moe_gemm(x, row_div, K, route, packed, scales, global_scales, E, N, y, st));
+}
+
+nvfp4_status nvfp4_moe_silu_and_mul(const void* h, int64_t P, int64_t I, void* a, void* stream) {
+  if (P != 0 && (!h || !a)) return NVFP4_ERR_NULL;
+  if (P < 0 || P > kMaxPairs || I < 8 || I % 8 != 0 || I > kMaxDim || P * 2 * I > kMaxElems)
+    return NVFP4_ERR_SHAPE;
+  if (P == 0) return NVFP4_OK;
+  if (!aligned(h, 16) || !aligned(a, 16)) return NVFP4_ERR_ALIGN;
+  if (overlap(span(h, P * 2 * I * 2), span(a, P * I * 2))) return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_moe_silu_mul(h, P, I, a, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_moe_combine(const void* o, const float* topk_weights, int64_t T, int64_t topk, int64_t H,
+                               void* out, void* stream) {
+  if (T != 0 && (!o || !topk_weights || !out)) return NVFP4_ERR_NULL;
+  if (T < 0 || topk < 1 || T * topk > kMaxPairs || H < 8 || H % 8 != 0 || H > kMaxDim ||
+      T * topk * H > kMaxElems)
+    return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!aligned(o, 16) || !aligned(out, 16) || !aligned(topk_weights, 4)) return NVFP4_ERR_ALIGN;
+  const Range rout = span(out, T * H * 2);
+  if (overlap(rout, span(o, T * topk * H * 2)) || overlap(rout, span(topk_weights, T * topk * 4)))
+    return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  return finish(nvfp4::launch_moe_combine(o, topk_weights, T, topk, H, out, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_moe_w4a16_forward(const void* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                     const float* topk_weights, int64_t topk, const uint8_t* w13_packed,
+                                     const uint8_t* w13_scales, const float* w13_global_scales,
+                                     const uint8_t* w2_packed, const uint8_t* w2_scales,
+                                     const float* w2_global_scales, int64_t E, int64_t I, void* workspace,
+                                     void* out, uint32_t* invalid_pairs, void* stream) {
+  if (!w13_packed || !w13_scales || !w13_global_scales || !w2_packed || !w2_scales || !w2_global_scales ||
+      (T != 0 && (!x || !topk_ids || !topk_weights || !workspace || !out)))
+    return NVFP4_ERR_NULL;
+  if (T < 0 || topk < 1 || T > kMaxDim || T * topk > kMaxPairs) return NVFP4_ERR_SHAPE;
+  nvfp4_status s = check_experts(E, 2 * I, H);
+  if (s != NVFP4_OK) return s;
+  s = check_experts(E, H, I);
+  if (s != NVFP4_OK) return s;
+  const int64_t P = T * topk;
+  if (P * 2 * I > kMaxElems || P * H > kMaxElems) return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_packed, 16) || !aligned(w2_packed, 16) ||
+      !aligned(w13_global_scales, 4) || !aligned(w2_global_scales, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_weights, 4) || !aligned(workspace, 16) || (invalid_pairs && !aligned(invalid_pairs, 4)))
+    return NVFP4_ERR_ALIGN;
+  const int64_t ws_bytes = nvfp4_moe_workspace_bytes(T, topk, E, H, I);
+  const Range rout = span(out, T * H * 2), rw = span(workspace, ws_bytes),
+              ri = span(invalid_pairs, invalid_pairs ? 4 : 0);
+  const Range ins[] = {span(x, T * H * 2),
+                       span(topk_ids, P * 4),
+                       span(topk_weights, P * 4),
+                       span(w13_packed, E * 2 * I * H / 2),
+                       span(w13_scales, E * 2 * I * H / 16),
+                       span(w13_global_scales, E * 4),
+                       span(w2_packed, E * H * I / 2),
+                       span(w2_scales, E * H * I / 16),
+                       span(w2_global_scales, E * 4)};
+  if (overlap(rout, rw) || overlap(rout, ri) || overlap(rw, ri)) return NVFP4_ERR_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(rout, r) || overlap(rw, r) || overlap(ri, r)) return NVFP4_ERR_ALIAS;
+  g_last_hip_error[0] = '\0';
+  const hipStream_t st = (hipStream_t)stream;
+  uint8_t* const base = static_cast<uint8_t*>(workspace);
+  int32_t* const route = reinterpret_cast<int32_t*>(base);
+  uint8_t* const h = base + round256(nvfp4::moe_route_bytes(P, E));
+  uint8_t* const a = h + round256(P * 2 * I * 2);
+  uint8_t* const o = a + round256(P * I * 2);
+  hipError_t e = nvfp4::launch_moe_route(topk_ids, P, E, route, invalid_pairs, st);
+  if (e == hipSuccess)
+    e = nvfp4::launch_moe_gemm(x, topk, H, route, w13_packed, w13_scales, w13_global_scales, E, 2 * I, h, st);
+  if (e == hipSuccess) e = nvfp4::launch_moe_silu_mul(h, P, I, a, st);
+  if (e == hipSuccess)
+    e = nvfp4::launch_moe_gemm(a, 1, I, route, w2_packed, w2_scales, w2_global_scales, E, H, o, st);
+  if (e == hipSuccess) e = nvfp4::launch_moe_combine(o, topk_weights, T, topk, H, out, st);
+  return finish(e);
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";
@@ -231,6 +376,6 @@ const char* nvfp4_status_string(int status) {
 
 const char* nvfp4_last_hip_error(void) { return g_last_hip_error; }
 
-int nvfp4_abi_version(void) { return 2; }
+int nvfp4_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -51,4 +51,18 @@ hipError_t launch_w4a4_dequant_x(const uint8_t* x_packed, const uint8_t* x_scale
 hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
                            const float* ws, int64_t N, const void* bias, void* y, hipStream_t stream);
 
+// Mixture of experts (W4A16).  Routing workspace: int32 offsets of E + 1
+// groups (the last one holds pairs with an id outside [0, E)) padded to a
+// multiple of 4 words, then the P pair indices grouped by expert.
+inline int64_t moe_route_offsets_words(int64_t E) { return (E + 2 + 3) / 4 * 4; }
+inline int64_t moe_route_bytes(int64_t P, int64_t E) { return 4 * (moe_route_offsets_words(E) + (P + 3) / 4 * 4); }
+hipError_t launch_moe_route(const int32_t* ids, int64_t P, int64_t E, int32_t* route_ws, uint32_t* invalid,
+                            hipStream_t stream);
+hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int32_t* route_ws,
+                           const uint8_t* packed, const uint8_t* scales, const float* gs, int64_t E, int64_t N,
+                           void* y, hipStream_t stream);
+hipError_t launch_moe_silu_mul(const void* h, int64_t P, int64_t I, void* a, hipStream_t stream);
+hipError_t launch_moe_combine(const void* o, const float* w, int64_t T, int64_t topk, int64_t H, void* out,
+                              hipStream_t stream);
+
 }  // namespace nvfp4

@@ -184,3 +184,49 @@ def random_weight_bits(n: int, k: int, sigma: float = 0.02, seed: int = 0) -> np
 
 def random_activation_bits(m: int, k: int, seed: int = 0) -> np.ndarray:
     return normal_bits(m, k, 1.0, (101, seed, m, k))
+
+
+# ---------------------------------------------------------------------------
+# Mixture-of-experts inputs.  Expert e's weights are stream (cfg, 10 + e) for
+# w13 and (cfg, 1000 + e) for w2, N(0, sigma); activations stream (cfg, 2);
+# routing stream (cfg, 5): each token picks ``topk`` distinct experts
+# uniformly (``choice(E, topk, replace=False)``) with weights drawn from
+# U(0.1, 1) and divided by their float32 sum.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class MoeWorkload:
+    name: str
+    cfg: int
+    experts: int        # E
+    hidden: int         # H
+    inter: int          # I (w13 has 2I output rows)
+    topk: int
+    sigma: float
+    tokens: tuple       # T values measured
+    description: str = ""
+
+
+MOE_WORKLOADS = {
+    "moe_small": MoeWorkload("moe_small", 20, 8, 512, 256, 2, 0.02, (5,),
+                             description="8 experts, H 512, I 256, top-2"),
+    "moe_8x4096": MoeWorkload("moe_8x4096", 21, 8, 4096, 14336, 2, 0.02, (1, 16, 64),
+                              description="8 experts, H 4096, I 14336, top-2; decode T in {1,16,64}"),
+}
+
+
+def moe_expert_bits(rows: int, k: int, experts: int, sigma: float, cfg: int, stream0: int) -> np.ndarray:
+    """bf16 bits [E, rows, k]: expert e drawn from stream (cfg, stream0 + e)."""
+    out = np.empty((experts, rows, k), dtype=np.uint16)
+    for e in range(experts):
+        out[e] = normal_bits(rows, k, sigma, (cfg, stream0 + e))
+    return out
+
+
+def moe_routing(tokens: int, experts: int, topk: int, cfg: int) -> tuple[np.ndarray, np.ndarray]:
+    """(topk_ids int32 [T, topk], topk_weights float32 [T, topk])."""
+    rng = np.random.default_rng([cfg, 5, tokens])
+    ids = np.stack([rng.choice(experts, size=topk, replace=False) for _ in range(tokens)]).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, size=(tokens, topk)).astype(np.float32)
+    w = (w / w.sum(axis=1, keepdims=True, dtype=np.float32)).astype(np.float32)
+    return ids.reshape(tokens, topk), w.reshape(tokens, topk)

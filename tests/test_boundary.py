@@ -205,3 +205,39 @@ def test_product_path_has_no_oracle_or_fallback():
         if fname.endswith(".py"):
             text = open(os.path.join(pkg, fname)).read()
             assert "oracle" not in text.replace("the oracle", ""), fname
+
+
+def test_moe_validation(lib):
+    """Mixture-of-experts calls reject bad arguments before any HIP call."""
+    assert lib.nvfp4_moe_gemm_workspace_bytes(10, 8) == 4 * (12 + 12)
+    assert lib.nvfp4_moe_gemm_workspace_bytes(-1, 8) == 0
+    T, k, E, H, I = 5, 2, 8, 512, 256
+    npairs = T * k
+    assert lib.nvfp4_moe_workspace_bytes(T, k, E, H, I) == 256 + 256 * ((npairs * 4 * I + 255) // 256) + \
+        256 * ((npairs * 2 * I + 255) // 256) + 256 * ((npairs * 2 * H + 255) // 256)
+    g = lib.nvfp4_moe_w4a16_gemm
+    base = dict(x=X, rows=T, K=H, ids=B, P=npairs, div=k, p=P, s=S, g=G, E=E, N=2 * I, ws=W, y=Y, inv=None)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return g(a["x"], a["rows"], a["K"], a["ids"], a["P"], a["div"], a["p"], a["s"], a["g"], a["E"], a["N"],
+                 a["ws"], a["y"], a["inv"], None)
+    assert call(ids=0) == ERR_NULL
+    assert call(ws=0) == ERR_NULL
+    assert call(P=0, x=0, ids=0, ws=0, y=0) == OK
+    assert call(K=40) == ERR_SHAPE
+    assert call(E=0) == ERR_SHAPE
+    assert call(div=0) == ERR_SHAPE
+    assert call(rows=T - 1) == ERR_SHAPE                     # x_rows < ceil(P / row_div)
+    assert call(x=X + 8) == ERR_ALIGN
+    assert call(ids=B + 2) == ERR_ALIGN
+    assert call(y=X + 256) == ERR_ALIAS
+    assert call(ws=Y + 64) == ERR_ALIAS
+    assert lib.nvfp4_moe_silu_and_mul(X, 4, 12, Y, None) == ERR_SHAPE
+    assert lib.nvfp4_moe_silu_and_mul(X, 4, 16, X + 64, None) == ERR_ALIAS
+    assert lib.nvfp4_moe_silu_and_mul(X + 2, 4, 16, Y, None) == ERR_ALIGN
+    assert lib.nvfp4_moe_combine(X, G, 3, 0, 64, Y, None) == ERR_SHAPE
+    assert lib.nvfp4_moe_combine(X, G, 3, 2, 64, X + 128, None) == ERR_ALIAS
+    f = lib.nvfp4_moe_w4a16_forward
+    assert f(X, T, H, B, G + 4096, k, P, S, G, W + 4096, S + 4096, G + 8192, E, 40, W, Y, None, None) == ERR_SHAPE
+    assert f(X, T, H, B, G + 4096, k, P, S, G, W + 4096, S + 4096, G + 8192, E, I, 0, Y, None, None) == ERR_NULL

@@ -1,0 +1,159 @@
+"""GPU parity of the W4A16 mixture-of-experts calls against
+oracle/nvfp4_moe_oracle.py.
+
+Grouped GEMM: every output of every pair against the fp64 reference on the
+oracle's quantized experts, within the float32-accumulation bound plus one
+bf16 rounding, and the benchmark spec's bound; routing edge cases (experts with no
+pair, more than one 64-pair block, ids outside [0, E), ragged K and N).
+SiLU-and-mul and combine: every element on seeded inputs.  The whole layer:
+every output within the oracle's propagated bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.nvfp4_oracle as O
+import oracle.nvfp4_moe_oracle as MO
+from nvfp4_w4a16_lm_amd import binding as B
+from nvfp4_w4a16_lm_amd import workloads as wl
+
+from gpu_util import DEV, dev_bf16, dev_u8, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def experts(E, N, K, seed, sigma=0.02):
+    bits = wl.moe_expert_bits(N, K, E, sigma, 70 + seed, 0)
+    qs = [O.quantize(bits[e]) for e in range(E)]
+    return (np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]),
+            np.array([q[2] for q in qs], dtype=np.float32))
+
+
+def upload(w):
+    return dev_u8(w[0]), dev_u8(w[1]), torch.from_numpy(w[2]).to(DEV)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return wl.bf16_bits_to_f32(host_bits(t)).astype(np.float64)
+
+
+def check_grouped(x_bits, row_div, ids, w, got, valid=None, label=""):
+    E = w[0].shape[0]
+    y64, wn, sa = MO.grouped_gemm_ref(x_bits, row_div, np.where((ids < 0) | (ids >= E), 0, ids), *w)
+    K = x_bits.shape[1]
+    loose, tight = MO.gemm_bound(x_bits, row_div, y64, wn, sa, K)
+    g = f64(got)
+    if valid is not None:
+        assert np.all(g[~valid] == 0), f"{label}: rows of invalid pairs are not zero"
+        g, y64, loose, tight = g[valid], y64[valid], loose[valid], tight[valid]
+    err = np.abs(g - y64)
+    assert np.all(err <= tight), f"{label}: tight bound, worst {np.max(err - tight):.3e}"
+    assert np.all(err <= loose), f"{label}: north-star bound"
+
+
+@pytest.mark.parametrize("E,H,N,T,topk", [
+    (8, 512, 512, 5, 2),        # decode-sized: 10 pairs over 8 experts (some empty)
+    (4, 1024, 320, 40, 4),      # ~40 pairs per expert: several 16-row tiles, ragged N
+    (2, 256, 272, 100, 2),      # 100 pairs per expert: two 64-pair blocks
+    (3, 272, 48, 7, 3),         # K % 32 == 16 (8-byte code loads), partial chunk, N < 64
+    (5, 48, 300, 9, 1),         # K = 48: one partial chunk
+])
+def test_grouped_gemm_first_layer(E, H, N, T, topk):
+    w = experts(E, N, H, E * 100 + N)
+    x = wl.random_activation_bits(T, H, seed=T)
+    ids, _ = wl.moe_routing(T, E, topk, E + T)
+    inv = torch.zeros((), dtype=torch.int32, device=DEV)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), topk, *upload(w), invalid_pairs=inv)
+    torch.cuda.synchronize()
+    assert int(inv.item()) == 0
+    check_grouped(x, topk, ids.reshape(-1), w, y, label=f"E{E} H{H} N{N} T{T} k{topk}")
+
+
+def test_grouped_gemm_second_layer_reads_one_row_per_pair():
+    E, I, H, P = 6, 256, 520, 37
+    w = experts(E, H, I, 11)
+    a = wl.random_activation_bits(P, I, seed=12)
+    ids = np.random.default_rng(13).integers(0, E, size=P).astype(np.int32)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(a), torch.from_numpy(ids).to(DEV), 1, *upload(w))
+    torch.cuda.synchronize()
+    check_grouped(a, 1, ids, w, y, label="second layer")
+
+
+def test_invalid_ids_give_zero_rows_and_are_counted():
+    E, K, N, T, topk = 4, 256, 260, 6, 2
+    w = experts(E, N, K, 21)
+    x = wl.random_activation_bits(T, K, seed=22)
+    ids, _ = wl.moe_routing(T, E, topk, 23)
+    ids = ids.reshape(-1).copy()
+    ids[3], ids[8] = E, -1
+    inv = torch.zeros((), dtype=torch.int32, device=DEV)
+    out = torch.full((T * topk, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), topk, *upload(w), out=out,
+                           invalid_pairs=inv)
+    torch.cuda.synchronize()
+    assert int(inv.item()) == 2
+    valid = (ids >= 0) & (ids < E)
+    check_grouped(x, topk, ids, w, out, valid=valid, label="invalid ids")
+
+
+def test_all_pairs_on_one_expert_many_blocks():
+    E, K, N, T, topk = 3, 512, 256, 150, 1
+    w = experts(E, N, K, 31)
+    x = wl.random_activation_bits(T, K, seed=32)
+    ids = np.full((T, topk), 1, np.int32)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), topk, *upload(w))
+    torch.cuda.synchronize()
+    check_grouped(x, topk, ids.reshape(-1), w, y, label="one expert")
+
+
+@pytest.mark.parametrize("P,I", [(1, 8), (13, 256), (64, 1000)])
+def test_silu_and_mul(P, I):
+    rng = np.random.default_rng(P + I)
+    h = wl.f32_to_bf16_bits((rng.standard_normal((P, 2 * I)) * 3).astype(np.float32))
+    h[0, :4] = wl.f32_to_bf16_bits(np.array([0.0, -0.0, 100.0, -100.0], np.float32))
+    a = B.nvfp4_moe_silu_and_mul(dev_bf16(h))
+    torch.cuda.synchronize()
+    ref = MO.silu_and_mul_ref(h)
+    err = np.abs(f64(a) - ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -133)
+
+
+@pytest.mark.parametrize("T,topk,H", [(1, 1, 8), (7, 2, 264), (33, 8, 1024)])
+def test_combine(T, topk, H):
+    rng = np.random.default_rng(T * topk + H)
+    o = wl.f32_to_bf16_bits(rng.standard_normal((T * topk, H)).astype(np.float32))
+    _, w = wl.moe_routing(T, 16, topk, H)
+    out = B.nvfp4_moe_combine(dev_bf16(o), torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    ref = MO.combine_ref(o, w)
+    sabs = MO.combine_ref(np.bitwise_and(o, 0x7FFF), np.abs(w))
+    err = np.abs(f64(out) - ref)
+    assert np.all(err <= (topk + 2) * 2.0 ** -24 * sabs + 2.0 ** -8 * np.abs(ref))
+
+
+@pytest.mark.parametrize("E,H,I,T,topk", [(8, 512, 256, 5, 2), (4, 256, 384, 30, 3), (3, 272, 48, 4, 2)])
+def test_forward_whole_layer(E, H, I, T, topk):
+    w13 = experts(E, 2 * I, H, 41 + E)
+    w2 = experts(E, H, I, 51 + E)
+    x = wl.random_activation_bits(T, H, seed=61 + T)
+    ids, tw = wl.moe_routing(T, E, topk, 71 + T)
+    inv = torch.zeros((), dtype=torch.int32, device=DEV)
+    out = B.nvfp4_moe_w4a16_forward(dev_bf16(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(tw).to(DEV),
+                                    upload(w13), upload(w2), invalid_pairs=inv)
+    torch.cuda.synchronize()
+    assert int(inv.item()) == 0
+    ref = MO.moe_ref(x, ids, tw, w13, w2)
+    tol = MO.moe_tolerance(ref, tw, H)
+    err = np.abs(f64(out) - ref["out"])
+    assert np.all(err <= tol), f"worst excess {np.max(err - tol):.3e}"
+
+
+def test_forward_empty_batch_enqueues_nothing():
+    E, H, I = 2, 64, 32
+    w13 = upload(experts(E, 2 * I, H, 81))
+    w2 = upload(experts(E, H, I, 82))
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    out = B.nvfp4_moe_w4a16_forward(x, torch.empty((0, 2), dtype=torch.int32, device=DEV),
+                                    torch.empty((0, 2), dtype=torch.float32, device=DEV), w13, w2)
+    assert out.shape == (0, H)
