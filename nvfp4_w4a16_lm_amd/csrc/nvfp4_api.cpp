@@ -277,7 +277,7 @@ nvfp4_status nvfp4_moe_w4a16_gemm(const void* x, int64_t x_rows, int64_t K, cons
   int32_t* const route = static_cast<int32_t*>(workspace);
   hipError_t e = nvfp4::launch_moe_route(topk_ids, P, E, route, invalid_pairs, st);
   if (e != hipSuccess) return finish(e);
-  return finish(nvfp4::launch_moe_gemm(x, row_div, K, route, packed, scales, global_scales, E, N, y, st));
+  return finish(nvfp4::launch_moe_gemm(x, row_div, K, route, P, packed, scales, global_scales, E, N, y, st));
 }
 
 nvfp4_status nvfp4_moe_silu_and_mul(const void* h, int64_t P, int64_t I, void* a, void* stream) {
@@ -351,10 +351,10 @@ nvfp4_status nvfp4_moe_w4a16_forward(const void* x, int64_t T, int64_t H, const 
   uint8_t* const o = a + round256(P * I * 2);
   hipError_t e = nvfp4::launch_moe_route(topk_ids, P, E, route, invalid_pairs, st);
   if (e == hipSuccess)
-    e = nvfp4::launch_moe_gemm(x, topk, H, route, w13_packed, w13_scales, w13_global_scales, E, 2 * I, h, st);
+    e = nvfp4::launch_moe_gemm(x, topk, H, route, P, w13_packed, w13_scales, w13_global_scales, E, 2 * I, h, st);
   if (e == hipSuccess) e = nvfp4::launch_moe_silu_mul(h, P, I, a, st);
   if (e == hipSuccess)
-    e = nvfp4::launch_moe_gemm(a, 1, I, route, w2_packed, w2_scales, w2_global_scales, E, H, o, st);
+    e = nvfp4::launch_moe_gemm(a, 1, I, route, P, w2_packed, w2_scales, w2_global_scales, E, H, o, st);
   if (e == hipSuccess) e = nvfp4::launch_moe_combine(o, topk_weights, T, topk, H, out, st);
   return finish(e);
 }

@@ -58,7 +58,7 @@ inline int64_t moe_route_offsets_words(int64_t E) { return (E + 2 + 3) / 4 * 4; 
 inline int64_t moe_route_bytes(int64_t P, int64_t E) { return 4 * (moe_route_offsets_words(E) + (P + 3) / 4 * 4); }
 hipError_t launch_moe_route(const int32_t* ids, int64_t P, int64_t E, int32_t* route_ws, uint32_t* invalid,
                             hipStream_t stream);
-hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int32_t* route_ws,
+hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int32_t* route_ws, int64_t P,
                            const uint8_t* packed, const uint8_t* scales, const float* gs, int64_t E, int64_t N,
                            void* y, hipStream_t stream);
 hipError_t launch_moe_silu_mul(const void* h, int64_t P, int64_t I, void* a, hipStream_t stream);

@@ -14,16 +14,21 @@
 //   pair order inside each expert (a stable counting sort: threads own
 //   (expert, segment) cells, count, prefix-sum the cells in order, then
 //   scatter).  Pairs whose id is outside [0, E) form an extra group E.
-// moe_gemm_kernel: grid (256-row blocks of the expert's N output rows,
-//   E + 1).  A workgroup of 4 wavefronts streams its 256 weight rows of
-//   expert e once per block of up to 64 of the expert's pairs (decode-sized
-//   routing has one block); each wavefront owns 4 tiles of 16 rows, loads its
-//   weights straight into registers one 256-k chunk ahead, dequantizes them
-//   exactly (code * scale is a bf16 value) and runs bf16 MFMA
-//   (v_mfma_f32_16x16x32_bf16) against the gathered activation rows staged
-//   in LDS.  The k order inside a chunk is permuted identically on both
-//   operands so that a lane's codes are two 16-byte loads.  Group E writes
-//   zero rows.
+// moe_gemv_kernel (experts with at most 48 pairs, the decode case): a
+//   workgroup of 4 wavefronts owns 32 to 128 weight rows of one expert and
+//   splits K between 1, 2 or 4 of its wavefronts; each streams its weights, scales and activation
+//   fragments straight into registers one 256-k chunk ahead with no barrier,
+//   dequantizes exactly (code * scale is a bf16 value) and runs bf16 MFMA
+//   (v_mfma_f32_16x16x32_bf16, 16 pairs per column tile); the partial tiles
+//   are summed through LDS in wavefront order.  It also writes the zero rows
+//   of pairs whose id is outside [0, E).
+// moe_gemm_kernel (experts with more pairs): a workgroup of 4 wavefronts
+//   streams 256 weight rows of one expert once per block of 64 pairs; each
+//   wavefront owns 4 tiles of 16 rows, loads its weights straight into
+//   registers one chunk ahead and runs the same MFMA against the gathered
+//   activation rows staged in LDS.
+// In both, the k order inside a chunk is permuted identically on both
+// operands so that a lane's codes are two 16-byte loads.
 // moe_silu_mul_kernel: a = silu(h[:, :I]) * h[:, I:] in float32, one bf16
 //   rounding.
 // moe_combine_kernel: out[t] = sum_j w[t, j] * o[t * topk + j] in float32 in
@@ -42,6 +47,9 @@ constexpr int kMoeRows = 256;        // weight rows per workgroup (4 wavefronts 
 constexpr int kMoeMBlock = 64;       // pairs per block (4 MFMA column tiles)
 constexpr int kMoeChunk = 256;       // k per chunk
 constexpr int kRouteThreads = 1024;
+constexpr int kMoeSmallMax = 48;     // experts with at most this many pairs take moe_gemv_kernel
+constexpr int kGemvWaves = 4;        // moe_gemv_kernel: wavefronts splitting K
+constexpr int kGemvTiles = 2;        // moe_gemv_kernel: 16-row tiles per workgroup
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -69,27 +77,41 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
     return (v < 0 || v >= E) ? E : v;
   };
   if (groups <= kRouteThreads) {
+    __shared__ int32_t wave_sum[kRouteThreads / 64];
     const int g = tid / S, s = tid - g * S;
+    const int lane = tid & 63, wave = tid >> 6;
     int c = 0;
     const int p0 = s * seg, p1 = min(P, p0 + seg);
     if (g < groups)
       for (int p = p0; p < p1; ++p) c += group_of(p) == g;
-    cell[tid] = g < groups ? c : 0;
+    // exclusive prefix of the cells in (group, segment) order = thread order:
+    // wavefront scans, then a scan of the 16 wavefront totals
+    int v = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    if (lane == 63) wave_sum[wave] = v;
     __syncthreads();
-    if (tid == 0) {                                   // exclusive prefix in (group, segment) order
-      int run = 0;
-      for (int i = 0; i < groups * S; ++i) {
-        const int v = cell[i];
-        cell[i] = run;
-        if (i % S == 0) offsets[i / S] = run;
-        run += v;
+    if (wave == 0) {
+      int w = lane < kRouteThreads / 64 ? wave_sum[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < kRouteThreads / 64; off <<= 1) {
+        const int t = __shfl_up(w, off, 64);
+        if (lane >= off) w += t;
       }
-      offsets[groups] = run;
-      if (invalid_out) *invalid_out = (uint32_t)(run - cell[E * S]);
+      if (lane < kRouteThreads / 64) wave_sum[lane] = w;
     }
     __syncthreads();
+    const int incl = v + (wave > 0 ? wave_sum[wave - 1] : 0);
+    const int excl = incl - c;
+    const int total = wave_sum[kRouteThreads / 64 - 1];
+    if (g < groups && s == 0) offsets[g] = excl;
+    if (tid == 0) offsets[groups] = total;
+    if (g == E && s == 0 && invalid_out) *invalid_out = (uint32_t)(total - excl);
     if (g < groups) {
-      int at = cell[tid];
+      int at = excl;
       for (int p = p0; p < p1; ++p)
         if (group_of(p) == g) order[at++] = p;
     }
@@ -147,23 +169,15 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint16_t* _
                                                                const int32_t* __restrict__ order,
                                                                const uint8_t* __restrict__ packed,
                                                                const uint8_t* __restrict__ scales,
-                                                               const float* __restrict__ gs_arr, int E, int N,
+                                                               const float* __restrict__ gs_arr, int N,
                                                                uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kMoeMBlock * kMoeChunk * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int e = blockIdx.y;
   const int first = offsets[e], cnt = offsets[e + 1] - first;
-  if (cnt == 0) return;                               // uniform over the workgroup
+  if (cnt <= kMoeSmallMax) return;                    // moe_gemv_kernel's (uniform over the workgroup)
   const int nb = blockIdx.x * kMoeRows;
-  if (e == E) {                                       // invalid ids: zero rows, this block's columns
-    const int cols = min(kMoeRows, N - nb);
-    for (int i = tid; i < cnt * cols; i += kMoeThreads) {
-      const int q = i / cols, c = i - q * cols;
-      y[(int64_t)order[first + q] * N + nb + c] = 0;
-    }
-    return;
-  }
   const int64_t prow = K >> 1, srow = K >> 4;
   const uint8_t* const wbase = packed + (int64_t)e * N * prow;
   const uint8_t* const sbase = scales + (int64_t)e * N * srow;
@@ -313,6 +327,152 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------
+// Grouped GEMM for experts with at most kMoeSmallMax pairs (decode-sized
+// routing).  A workgroup of 4 wavefronts owns 16 R rows of one expert per
+// row group; K is split over `splitk` wavefronts of a group (wavefront w takes
+// chunks w % splitk, + splitk, ...; splitk = 1, 2 or 4 so that each streams at
+// least 8 chunks when K allows), each loading
+// its weights and scales straight into registers one chunk ahead and the
+// chunk's activation fragments (small, L2-resident) as it starts it, with no
+// barrier until the end, where the partial tiles of a row group are
+// summed through LDS in wavefront order.  Pairs are taken 16 at a time (one
+// MFMA column tile); the activation fragments use the chunk layout of
+// moe_gemm_kernel.  Group E (ids outside [0, E)) writes zero rows here.
+// ---------------------------------------------------------------------------
+template <int R>
+__global__ __launch_bounds__(64 * kGemvWaves) void moe_gemv_kernel(const uint16_t* __restrict__ x, int row_div,
+                                                                   int K, const int32_t* __restrict__ offsets,
+                                                                   const int32_t* __restrict__ order,
+                                                                   const uint8_t* __restrict__ packed,
+                                                                   const uint8_t* __restrict__ scales,
+                                                                   const float* __restrict__ gs_arr, int E, int N,
+                                                                   uint16_t* __restrict__ y, int splitk) {
+  __shared__ float red[kGemvWaves][4 * R][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int e = blockIdx.y;
+  const int first = offsets[e], cnt = offsets[e + 1] - first;
+  if (cnt == 0) return;                               // uniform over the workgroup
+  // wavefront w: row group w / splitk (16 R rows), chunks w % splitk + j * splitk
+  const int wg_rows = 16 * R * (kGemvWaves / splitk);
+  const int nb = blockIdx.x * wg_rows;
+  const int rg = wave / splitk, ph = wave - rg * splitk;
+  if (e == E) {                                       // invalid ids: zero rows, this block's columns
+    const int cols = min(wg_rows, N - nb);
+    for (int i = tid; i < cnt * cols; i += 64 * kGemvWaves) {
+      const int q = i / cols, c = i - q * cols;
+      y[(int64_t)order[first + q] * N + nb + c] = 0;
+    }
+    return;
+  }
+  if (cnt > kMoeSmallMax) return;                     // moe_gemm_kernel's
+  const int64_t prow = K >> 1, srow = K >> 4;
+  const uint8_t* const wbase = packed + (int64_t)e * N * prow;
+  const uint8_t* const sbase = scales + (int64_t)e * N * srow;
+  const float gs = gs_arr[e];
+  const int nchunks = (K + kMoeChunk - 1) / kMoeChunk;
+  const uint8_t* wrowp[R];
+  const uint8_t* srowp[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    const int64_t row = min(nb + 16 * R * rg + 16 * t + r, N - 1);
+    wrowp[t] = wbase + row * prow;
+    srowp[t] = sbase + row * srow;
+  }
+
+  struct Chunk {
+    u32x4 w[R][2];
+    uint32_t sc[R];
+  };
+  auto load = [&](int c, Chunk& ch) {
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int k0 = kMoeChunk * c + 128 * j + 32 * g;
+        if (k0 + 32 <= K) {
+          if ((K & 31) == 0) {
+            ch.w[t][j] = load_stream16(wrowp[t] + (k0 >> 1));
+          } else {
+            const uint2 h0 = *reinterpret_cast<const uint2*>(wrowp[t] + (k0 >> 1));
+            const uint2 h1 = *reinterpret_cast<const uint2*>(wrowp[t] + (k0 >> 1) + 8);
+            ch.w[t][j] = u32x4{h0.x, h0.y, h1.x, h1.y};
+          }
+        } else if (k0 < K) {
+          const uint2 h = *reinterpret_cast<const uint2*>(wrowp[t] + (k0 >> 1));
+          ch.w[t][j] = u32x4{h.x, h.y, 0u, 0u};
+        } else {
+          ch.w[t][j] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      uint32_t sv = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int b = 16 * c + 8 * j + 2 * g + h;
+          if (b < (K >> 4)) sv |= (uint32_t)srowp[t][b] << (8 * (2 * j + h));
+        }
+      ch.sc[t] = sv;
+    }
+  };
+
+  for (int mb = 0; mb < cnt; mb += 16) {
+    const int mrows = min(16, cnt - mb);
+    const uint16_t* const xr = x + (int64_t)(order[first + mb + min(r, mrows - 1)] / row_div) * K;
+    f32x4 acc[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // chunk c of this wavefront: its activation fragments are loaded first
+    // (L2-resident), then the weights of the wavefront's next chunk are issued
+    // into the other buffer, then chunk c computes; the two weight buffers
+    // alternate without register copies (a copy would wait for the loads), so
+    // the prefetch stays in flight while the MFMAs run
+    auto step = [&](int c, const Chunk& ch, Chunk& refill) {
+      u32x4 xv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int k0 = kMoeChunk * c + 128 * (s >> 2) + 32 * g + 8 * (s & 3);
+        xv[s] = k0 < K ? *reinterpret_cast<const u32x4*>(xr + k0) : u32x4{0u, 0u, 0u, 0u};
+      }
+      if (c + splitk < nchunks) load(c + splitk, refill);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 bx = __builtin_bit_cast(bf16x8, xv[s]);
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          const uint32_t sb = (ch.sc[t] >> (8 * (2 * (s >> 2) + ((s & 3) >> 1)))) & 0xFFu;
+          acc[t] = mfma_bf16(dequant8(ch.w[t][s >> 2][s & 3], NVFP4_E4M3_TO_F32(sb, 0)), bx, acc[t]);
+        }
+      }
+    };
+    Chunk ca, cb;
+    if (ph < nchunks) load(ph, ca);
+    for (int c = ph; c < nchunks; c += 2 * splitk) {
+      step(c, ca, cb);
+      if (c + splitk >= nchunks) break;
+      step(c + splitk, cb, ca);
+    }
+    // partial tiles -> LDS; lane (r, g) of tile t holds rows 16 t + 4 g + v, pair r
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][4 * t + v][lane] = acc[t][v];
+    __syncthreads();
+    for (int i = tid; i < 16 * wg_rows; i += 64 * kGemvWaves) {
+      const int m = i / wg_rows, nl = i - m * wg_rows;
+      const int g_of = nl / (16 * R), nl2 = nl - g_of * (16 * R);
+      const int t = nl2 >> 4, gg = (nl2 >> 2) & 3, v = nl2 & 3;
+      const int n = nb + nl;
+      float sum = 0.f;
+      for (int q = 0; q < splitk; ++q) sum += red[g_of * splitk + q][4 * t + v][16 * gg + m];
+      if (m < mrows && n < N) y[(int64_t)order[first + mb + m] * N + n] = (uint16_t)f32_to_bf16_rne(sum * gs);
+    }
+    __syncthreads();                                  // red is reused by the next 16 pairs
+  }
+}
+
+// ---------------------------------------------------------------------------
 // a[p, i] = bf16(silu(h[p, i]) * h[p, I + i]); 8 outputs per thread.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void moe_silu_mul_kernel(const uint16_t* __restrict__ h, int64_t P, int I,
@@ -372,15 +532,24 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t P, int64_t E, int32_t* r
                        offsets, order, invalid);
 }
 
-hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int32_t* route_ws,
+hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int32_t* route_ws, int64_t P,
                            const uint8_t* packed, const uint8_t* scales, const float* gs, int64_t E, int64_t N,
                            void* y, hipStream_t stream) {
   const int32_t* offsets = route_ws;
   const int32_t* order = route_ws + moe_route_offsets_words(E);
-  const dim3 grid((unsigned)((N + kMoeRows - 1) / kMoeRows), (unsigned)(E + 1));
+  // K split over 1, 2 or 4 wavefronts so that each streams at least 8 chunks
+  const int64_t nchunks = (K + kMoeChunk - 1) / kMoeChunk;
+  const int splitk = nchunks >= 32 ? 4 : nchunks >= 16 ? 2 : 1;
+  const int64_t wg_rows = 16 * kGemvTiles * (kGemvWaves / splitk);
+  const dim3 grid_small((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)(E + 1));
+  hipError_t err = launch_kernel((const void*)moe_gemv_kernel<kGemvTiles>, grid_small, dim3(64 * kGemvWaves),
+                                 stream, reinterpret_cast<const uint16_t*>(x), (int)row_div, (int)K, offsets, order,
+                                 packed, scales, gs, (int)E, (int)N, reinterpret_cast<uint16_t*>(y), splitk);
+  if (err != hipSuccess || P <= kMoeSmallMax) return err;   // no expert can have more pairs
+  const dim3 grid((unsigned)((N + kMoeRows - 1) / kMoeRows), (unsigned)E);
   return launch_kernel((const void*)moe_gemm_kernel, grid, dim3(kMoeThreads), stream,
                        reinterpret_cast<const uint16_t*>(x), (int)row_div, (int)K, offsets, order, packed, scales,
-                       gs, (int)E, (int)N, reinterpret_cast<uint16_t*>(y));
+                       gs, (int)N, reinterpret_cast<uint16_t*>(y));
 }
 
 hipError_t launch_moe_silu_mul(const void* h, int64_t P, int64_t I, void* a, hipStream_t stream) {
