@@ -412,14 +412,37 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int kXresLdsMax = 160 * 1024;
 
-template <int NW>
+// Expert-layer use of gemv_xres_kernel (kMoe): workgroup row blockIdx.y is
+// expert e; its activation rows are the expert's pairs order[offsets[e] ..
+// offsets[e + 1]) (row p reads x[p / row_div], writes y[p]); experts with
+// fewer than mmin (at least 1) or more than mcap pairs are left to the other
+// expert kernels.  gemv_panel_kernel takes the same rows.
+struct MoeRows {
+  const int32_t* offsets;
+  const int32_t* order;
+  int row_div;
+  int mcap;
+  int mmin;
+};
+
+template <int NW, bool kMoe = false>
 __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                           const uint8_t* __restrict__ packed,
                                                           const uint8_t* __restrict__ scales,
                                                           const float* __restrict__ gs_ptr, int N,
                                                           const uint16_t* __restrict__ bias,
-                                                          uint16_t* __restrict__ y) {
+                                                          uint16_t* __restrict__ y, MoeRows moe) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  int64_t first = 0;
+  if constexpr (kMoe) {                               // uniform over the workgroup, before any barrier
+    const int e = blockIdx.y;
+    first = moe.offsets[e];
+    M = moe.offsets[e + 1] - (int)first;
+    if (M < max(1, moe.mmin) || M > moe.mcap) return;
+    packed += (int64_t)e * N * (K >> 1);
+    scales += (int64_t)e * N * (K >> 4);
+    gs_ptr += e;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int xpitch = 2 * K + 16;                    // bytes per x row (the pad spreads rows over banks)
   uint8_t* const xl = lds;
@@ -461,7 +484,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   // largest |x| (bf16 magnitudes compare as integers), then x * 2^-p_m
   const int xvec = K / 8;                           // 16-byte vectors per x row
   for (int m = wave; m < M; m += NW) {
-    const uint16_t* xr = x + (int64_t)m * K;
+    const uint16_t* xr = x + (kMoe ? (int64_t)(moe.order[first + m] / moe.row_div) : (int64_t)m) * K;
     uint32_t mx = 0;
     for (int kv = lane; kv < xvec; kv += 64) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * kv);
@@ -525,7 +548,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     if (r < M) {
       acc *= up;
       const int n0 = n_base + 4 * g;
-      uint16_t* yrow = y + (int64_t)r * N;
+      uint16_t* yrow = y + (kMoe ? (int64_t)moe.order[first + r] : (int64_t)r) * N;
       if ((N & 3) == 0 && n0 + 3 < N) {
         const uint32_t lo = out_bf16(acc[0], gs, bias, n0) | (out_bf16(acc[1], gs, bias, n0 + 1) << 16);
         const uint32_t hi = out_bf16(acc[2], gs, bias, n0 + 2) | (out_bf16(acc[3], gs, bias, n0 + 3) << 16);
@@ -563,13 +586,23 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
 // ---------------------------------------------------------------------------
 constexpr int kPanelXBytes = 64 * 1024;                 // x panel: M * 2 pk bytes at most
 
-template <int MT, int NW, int kPanelR>
+template <int MT, int NW, int kPanelR, bool kMoe = false>
 __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                          const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ scales,
                                                          const float* __restrict__ gs_ptr, int N,
                                                          const uint16_t* __restrict__ bias,
-                                                         uint16_t* __restrict__ y, int pk) {
+                                                         uint16_t* __restrict__ y, int pk, MoeRows moe) {
+  int64_t first = 0;
+  if constexpr (kMoe) {                               // uniform over the workgroup, before any barrier
+    const int e = blockIdx.y;
+    first = moe.offsets[e];
+    M = moe.offsets[e + 1] - (int)first;
+    if (M < max(1, moe.mmin) || M > moe.mcap) return;
+    packed += (int64_t)e * N * (K >> 1);
+    scales += (int64_t)e * N * (K >> 4);
+    gs_ptr += e;
+  }
   constexpr int kRows = 16 * kPanelR;                   // weight rows per wavefront
   __shared__ __attribute__((aligned(16))) uint8_t xp[kPanelXBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wl[NW][kRows * 128];
@@ -616,7 +649,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
       for (int i = wave; i < M * per_row; i += NW) {
         const int m = i / per_row, h = i - m * per_row;
         const int piece = 64 * h + (lane ^ (m & 7));
-        __builtin_amdgcn_global_load_lds((const void*)(x + (int64_t)m * K + p * pk + 8 * piece),
+        const int64_t xm = kMoe ? (int64_t)(moe.order[first + m] / moe.row_div) : (int64_t)m;
+        __builtin_amdgcn_global_load_lds((const void*)(x + xm * K + p * pk + 8 * piece),
                                          (lds_ptr_t)(xp + m * xpitch + 1024 * h), 16, 0, 0);
       }
     };
@@ -688,7 +722,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
       for (int mt = 0; mt < MT; ++mt) {
         const int m = 16 * mt + r;
         if (m >= M) continue;
-        uint16_t* yrow = y + (int64_t)m * N;
+        uint16_t* yrow = y + (kMoe ? (int64_t)moe.order[first + m] : (int64_t)m) * N;
         if ((N & 3) == 0 && n0 + 3 < N) {
           const uint32_t lo = out_bf16(acc[t][mt][0], gs, bias, n0) | (out_bf16(acc[t][mt][1], gs, bias, n0 + 1) << 16);
           const uint32_t hi = out_bf16(acc[t][mt][2], gs, bias, n0 + 2) | (out_bf16(acc[t][mt][3], gs, bias, n0 + 3) << 16);
@@ -855,8 +889,65 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
   const int ntiles = (N + 15) / 16;
   const int grid = std::max(1, std::min((ntiles + NW - 1) / NW, cus * per_cu));
   hipLaunchKernelGGL((gemv_xres_kernel<NW>), dim3(grid), dim3(64 * NW), lds, stream, (const uint16_t*)x, M, K,
-                     packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y);
+                     packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y, MoeRows{});
   return hipGetLastError();
+}
+
+// Expert layer: gemv_xres_kernel<NW, true> over a (G, E) grid for experts
+// with 1..mcap pairs; mcap is the largest row count (<= 16, <= P) whose
+// activation rows fit in LDS, 0 when none does or K % 256 != 0.
+static int moe_xres_waves(int mcap, int64_t K) {
+  if (mcap < 1 || K % kChunk != 0) return 0;
+  if (xres_lds_bytes(mcap, K, 16) <= kXresLdsMax) return 16;
+  if (xres_lds_bytes(mcap, K, 8) <= kXresLdsMax) return 8;
+  return 0;
+}
+
+int moe_xres_cap(int64_t P, int64_t K) {
+  for (int m = (int)std::min<int64_t>(16, P); m >= 1; --m)
+    if (moe_xres_waves(m, K)) return m;
+  return 0;
+}
+
+template <int NW>
+static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32_t* offsets, const int32_t* order,
+                                  int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales, const float* gs,
+                                  int E, int N, void* y, hipStream_t stream) {
+  const void* fn = (const void*)gemv_xres_kernel<NW, true>;
+  const int lds = (int)xres_lds_bytes(mcap, K, NW);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  static std::atomic<uint64_t> attr_done{0};
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit == 0 || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kXresLdsMax);
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit, std::memory_order_release);
+  }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+  // at most min(E, P) experts have pairs: give each enough workgroups to fill the GPU
+  const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
+  const int ntiles = (N + 15) / 16;
+  const int64_t g = std::min<int64_t>((ntiles + NW - 1) / NW, (cus * per_cu + active - 1) / active);
+  const MoeRows moe{offsets, order, row_div, mcap, 1};
+  hipLaunchKernelGGL((gemv_xres_kernel<NW, true>), dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E),
+                     dim3(64 * NW), lds, stream, (const uint16_t*)x, 0, K, packed, scales, gs, N,
+                     (const uint16_t*)nullptr, (uint16_t*)y, moe);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
+                           int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales, const float* gs,
+                           int64_t E, int64_t N, void* y, hipStream_t stream) {
+  switch (moe_xres_waves(mcap, K)) {
+    case 16: return moe_xres_launch<16>(x, (int)row_div, (int)K, offsets, order, mcap, P, packed, scales, gs,
+                                        (int)E, (int)N, y, stream);
+    case 8: return moe_xres_launch<8>(x, (int)row_div, (int)K, offsets, order, mcap, P, packed, scales, gs,
+                                      (int)E, (int)N, y, stream);
+    default: return hipSuccess;
+  }
 }
 
 // Panel width for gemv_panel_kernel: the widest multiple of 512 columns whose
@@ -878,7 +969,47 @@ static hipError_t panel_launch(const void* x, int M, int K, const uint8_t* packe
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
   const dim3 grid(std::min(nblocks, cus * per_cu));
   return launch_kernel(fn, grid, dim3(64 * NW), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
-                       (const uint16_t*)bias, (uint16_t*)y, panel_columns(M, K));
+                       (const uint16_t*)bias, (uint16_t*)y, panel_columns(M, K), MoeRows{});
+}
+
+// Expert layer: gemv_panel_kernel<MT, 8, R, true> over a (G, E) grid for the
+// experts with mmin..mcap pairs (mcap <= 16 MT); K % 512 == 0.
+template <int MT, int R>
+static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int32_t* offsets, const int32_t* order,
+                                   int mmin, int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales,
+                                   const float* gs, int E, int N, void* y, hipStream_t stream) {
+  const void* fn = (const void*)gemv_panel_kernel<MT, 8, R, true>;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * 8, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  // at most P / mmin experts fall in the class: give each enough workgroups to fill the GPU
+  const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P / std::max(1, mmin)));
+  const int nblocks = (N + 16 * 8 * R - 1) / (16 * 8 * R);
+  const int64_t g = std::min<int64_t>(nblocks, (cus * per_cu + active - 1) / active);
+  const MoeRows moe{offsets, order, row_div, mcap, mmin};
+  return launch_kernel(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E), dim3(64 * 8), stream,
+                       (const uint16_t*)x, 0, K, packed, scales, gs, N, (const uint16_t*)nullptr, (uint16_t*)y,
+                       panel_columns(mcap, K), moe);
+}
+
+hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
+                            int mmin, int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales,
+                            const float* gs, int64_t E, int64_t N, void* y, hipStream_t stream) {
+  if (mmin > mcap || K % 512 != 0) return hipSuccess;
+  // 512 rows per workgroup (4 tiles per wavefront) when the expert has enough
+  // rows to fill the GPU with such blocks, else 128 (one tile per wavefront)
+  const bool wide = N >= 16384;
+#define NVFP4_MOE_PANEL(MT_, CAP_)                                                                              \
+  (wide ? moe_panel_launch<MT_, 4>(x, (int)row_div, (int)K, offsets, order, mmin, CAP_, P, packed, scales, gs,   \
+                                   (int)E, (int)N, y, stream)                                                   \
+        : moe_panel_launch<MT_, 1>(x, (int)row_div, (int)K, offsets, order, mmin, CAP_, P, packed, scales, gs,   \
+                                   (int)E, (int)N, y, stream))
+  if (mcap <= 16) return NVFP4_MOE_PANEL(1, mcap);
+  if (mcap <= 32) return NVFP4_MOE_PANEL(2, mcap);
+  return NVFP4_MOE_PANEL(4, std::min(mcap, 64));
+#undef NVFP4_MOE_PANEL
 }
 
 // 0 = the activation does not fit in LDS; else the wavefronts per workgroup

@@ -14,7 +14,13 @@
 //   pair order inside each expert (a stable counting sort: threads own
 //   (expert, segment) cells, count, prefix-sum the cells in order, then
 //   scatter).  Pairs whose id is outside [0, E) form an extra group E.
-// moe_gemv_kernel (experts with at most 48 pairs, the decode case): a
+// Experts with 1..mcap pairs (mcap <= 16: as many activation rows as fit in
+//   LDS) run the lm_head path's x-resident decode kernel (gemv_xres_kernel in
+//   nvfp4_decode.hip, over a (workgroups, E) grid with the expert's gathered
+//   rows converted to f16 in LDS and weights copied straight to LDS).
+// With K % 512 == 0, experts with more pairs, up to 64, run the lm_head
+//   path's panel decode kernel (gemv_panel_kernel, same row gathering).
+// moe_gemv_kernel (otherwise, the other experts with at most 48 pairs): a
 //   workgroup of 4 wavefronts owns 32 to 128 weight rows of one expert and
 //   splits K between 1, 2 or 4 of its wavefronts; each streams its weights, scales and activation
 //   fragments straight into registers one 256-k chunk ahead with no barrier,
@@ -22,7 +28,7 @@
 //   (v_mfma_f32_16x16x32_bf16, 16 pairs per column tile); the partial tiles
 //   are summed through LDS in wavefront order.  It also writes the zero rows
 //   of pairs whose id is outside [0, E).
-// moe_gemm_kernel (experts with more pairs): a workgroup of 4 wavefronts
+// moe_gemm_kernel (experts with more than 64, or 48, pairs): a workgroup of 4 wavefronts
 //   streams 256 weight rows of one expert once per block of 64 pairs; each
 //   wavefront owns 4 tiles of 16 rows, loads its weights straight into
 //   registers one chunk ahead and runs the same MFMA against the gathered
@@ -170,13 +176,13 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint16_t* _
                                                                const uint8_t* __restrict__ packed,
                                                                const uint8_t* __restrict__ scales,
                                                                const float* __restrict__ gs_arr, int N,
-                                                               uint16_t* __restrict__ y) {
+                                                               uint16_t* __restrict__ y, int large_min) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kMoeMBlock * kMoeChunk * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int e = blockIdx.y;
   const int first = offsets[e], cnt = offsets[e + 1] - first;
-  if (cnt <= kMoeSmallMax) return;                    // moe_gemv_kernel's (uniform over the workgroup)
+  if (cnt <= large_min) return;                       // another kernel's (uniform over the workgroup)
   const int nb = blockIdx.x * kMoeRows;
   const int64_t prow = K >> 1, srow = K >> 4;
   const uint8_t* const wbase = packed + (int64_t)e * N * prow;
@@ -346,7 +352,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void moe_gemv_kernel(const uint16_
                                                                    const uint8_t* __restrict__ packed,
                                                                    const uint8_t* __restrict__ scales,
                                                                    const float* __restrict__ gs_arr, int E, int N,
-                                                                   uint16_t* __restrict__ y, int splitk) {
+                                                                   uint16_t* __restrict__ y, int splitk,
+                                                                   int small_min) {
   __shared__ float red[kGemvWaves][4 * R][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void moe_gemv_kernel(const uint16_
     }
     return;
   }
-  if (cnt > kMoeSmallMax) return;                     // moe_gemm_kernel's
+  if (cnt <= small_min || cnt > kMoeSmallMax) return; // the x-resident kernel's or moe_gemm_kernel's
   const int64_t prow = K >> 1, srow = K >> 4;
   const uint8_t* const wbase = packed + (int64_t)e * N * prow;
   const uint8_t* const sbase = scales + (int64_t)e * N * srow;
@@ -537,19 +544,36 @@ hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int3
                            void* y, hipStream_t stream) {
   const int32_t* offsets = route_ws;
   const int32_t* order = route_ws + moe_route_offsets_words(E);
+  // experts with 1..mcap pairs: the x-resident decode kernel; with K % 512 == 0
+  // the panel decode kernel takes the rest up to 64 pairs, else the split-K
+  // kernel up to 48; moe_gemm_kernel takes larger experts
+  const int mcap = moe_xres_cap(P, K);
+  hipError_t err = launch_moe_xres(x, row_div, K, offsets, order, mcap, P, packed, scales, gs, E, N, y, stream);
+  if (err != hipSuccess) return err;
+  int small_min = mcap, large_min = kMoeSmallMax;
+  if (K % 512 == 0) {
+    if (P > mcap) err = launch_moe_panel(x, row_div, K, offsets, order, mcap + 1, 32, P, packed, scales, gs, E, N, y,
+                                         stream);
+    if (err == hipSuccess && P > 32)
+      err = launch_moe_panel(x, row_div, K, offsets, order, std::max(mcap + 1, 33), 64, P, packed, scales, gs, E, N,
+                             y, stream);
+    if (err != hipSuccess) return err;
+    small_min = kMoeSmallMax;                         // the split-K kernel only writes the zero rows
+    large_min = 64;
+  }
   // K split over 1, 2 or 4 wavefronts so that each streams at least 8 chunks
   const int64_t nchunks = (K + kMoeChunk - 1) / kMoeChunk;
   const int splitk = nchunks >= 32 ? 4 : nchunks >= 16 ? 2 : 1;
   const int64_t wg_rows = 16 * kGemvTiles * (kGemvWaves / splitk);
   const dim3 grid_small((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)(E + 1));
-  hipError_t err = launch_kernel((const void*)moe_gemv_kernel<kGemvTiles>, grid_small, dim3(64 * kGemvWaves),
-                                 stream, reinterpret_cast<const uint16_t*>(x), (int)row_div, (int)K, offsets, order,
-                                 packed, scales, gs, (int)E, (int)N, reinterpret_cast<uint16_t*>(y), splitk);
-  if (err != hipSuccess || P <= kMoeSmallMax) return err;   // no expert can have more pairs
+  err = launch_kernel((const void*)moe_gemv_kernel<kGemvTiles>, grid_small, dim3(64 * kGemvWaves), stream,
+                      reinterpret_cast<const uint16_t*>(x), (int)row_div, (int)K, offsets, order, packed, scales, gs,
+                      (int)E, (int)N, reinterpret_cast<uint16_t*>(y), splitk, small_min);
+  if (err != hipSuccess || P <= large_min) return err;   // no expert can have more pairs
   const dim3 grid((unsigned)((N + kMoeRows - 1) / kMoeRows), (unsigned)E);
   return launch_kernel((const void*)moe_gemm_kernel, grid, dim3(kMoeThreads), stream,
                        reinterpret_cast<const uint16_t*>(x), (int)row_div, (int)K, offsets, order, packed, scales,
-                       gs, (int)N, reinterpret_cast<uint16_t*>(y));
+                       gs, (int)N, reinterpret_cast<uint16_t*>(y), large_min);
 }
 
 hipError_t launch_moe_silu_mul(const void* h, int64_t P, int64_t I, void* a, hipStream_t stream) {

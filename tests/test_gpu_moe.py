@@ -43,6 +43,12 @@ def check_grouped(x_bits, row_div, ids, w, got, valid=None, label=""):
     y64, wn, sa = MO.grouped_gemm_ref(x_bits, row_div, np.where((ids < 0) | (ids >= E), 0, ids), *w)
     K = x_bits.shape[1]
     loose, tight = MO.gemm_bound(x_bits, row_div, y64, wn, sa, K)
+    # experts with few pairs run the x-resident decode kernel, which stores each
+    # activation row as f16 scaled by a power of two: values below 2^-28 of the
+    # row's largest move by at most 2^-39 of it (or 2^-151)
+    xf = np.abs(wl.bf16_bits_to_f32(x_bits).astype(np.float64))
+    xmax = xf.max(axis=1)[np.arange(y64.shape[0]) // row_div]
+    tight = tight + (2.0 ** -39 * xmax[:, None] + 2.0 ** -151) * np.sqrt(K) * wn
     g = f64(got)
     if valid is not None:
         assert np.all(g[~valid] == 0), f"{label}: rows of invalid pairs are not zero"
@@ -58,6 +64,7 @@ def check_grouped(x_bits, row_div, ids, w, got, valid=None, label=""):
     (2, 256, 272, 100, 2),      # 100 pairs per expert: two 64-pair blocks
     (3, 272, 48, 7, 3),         # K % 32 == 16 (8-byte code loads), partial chunk, N < 64
     (5, 48, 300, 9, 1),         # K = 48: one partial chunk
+    (2, 768, 256, 30, 2),       # K % 512 != 0: experts with 17..48 pairs take the split-K kernel
 ])
 def test_grouped_gemm_first_layer(E, H, N, T, topk):
     w = experts(E, N, H, E * 100 + N)
@@ -105,6 +112,43 @@ def test_all_pairs_on_one_expert_many_blocks():
     y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), topk, *upload(w))
     torch.cuda.synchronize()
     check_grouped(x, topk, ids.reshape(-1), w, y, label="one expert")
+
+
+def test_expert_classes_in_one_call():
+    """One call mixes experts with few pairs (x-resident kernel), up to 48
+    (split-K kernel), more (the blocked kernel) and none."""
+    E, K, N = 4, 512, 300
+    w = experts(E, N, K, 91)
+    counts = {0: 3, 1: 20, 2: 60, 3: 0}
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in counts.items()])
+    ids = ids[np.random.default_rng(92).permutation(ids.size)]
+    x = wl.random_activation_bits(ids.size, K, seed=93)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), 1, *upload(w))
+    torch.cuda.synchronize()
+    check_grouped(x, 1, ids, w, y, label="mixed classes")
+
+
+def test_wide_experts_take_the_512_row_panel_blocks():
+    """N >= 16384: experts with 17..64 pairs run the panel kernel with 512-row blocks."""
+    E, K, N = 2, 512, 16400
+    w = experts(E, N, K, 96)
+    ids = np.array([0] * 20 + [1] * 40, np.int32)
+    x = wl.random_activation_bits(ids.size, K, seed=97)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), 1, *upload(w))
+    torch.cuda.synchronize()
+    check_grouped(x, 1, ids, w, y, label="wide experts")
+
+
+def test_long_rows_cap_the_resident_rows():
+    """K = 8192: at most 8 activation rows fit in LDS, so an expert with 12
+    pairs takes the split-K kernel while one with 5 stays x-resident."""
+    E, K, N = 2, 8192, 80
+    w = experts(E, N, K, 94)
+    ids = np.array([0] * 5 + [1] * 12, np.int32)
+    x = wl.random_activation_bits(ids.size, K, seed=95)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), 1, *upload(w))
+    torch.cuda.synchronize()
+    check_grouped(x, 1, ids, w, y, label="K 8192")
 
 
 @pytest.mark.parametrize("P,I", [(1, 8), (13, 256), (64, 1000)])
