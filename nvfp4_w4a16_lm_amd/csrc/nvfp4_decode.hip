@@ -425,7 +425,7 @@ struct MoeRows {
   int mmin;
 };
 
-template <int NW, bool kMoe = false>
+template <int NW, bool kMoe = false, int KS = 1>
 __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                           const uint8_t* __restrict__ packed,
                                                           const uint8_t* __restrict__ scales,
@@ -473,11 +473,15 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     const int64_t off = min((int64_t)16 * (kScaleGroup * grp + spiece), srow - 16);   // past the row end: unused
     __builtin_amdgcn_global_load_lds((const void*)(scales + row * srow + off), (lds_ptr_t)smine, 16, 0, 0);
   };
+  // KS > 1 (expert layer, few tiles): wavefront w works on tile slot w / KS
+  // and chunks w % KS, + KS, ... of it; the KS partial tiles are summed
+  // through LDS in phase order after each tile round
+  const int slots = NW / KS, slot = wave / KS, ph = wave - slot * KS;
   // the first chunk's copies fly while x is converted
-  int tile = blockIdx.x * NW + wave;
-  if (tile < ntiles) {
-    w_copy(tile, 0);
-    s_copy(tile, 0);
+  int tile = blockIdx.x * slots + slot;
+  if (tile < ntiles && ph < nchunks) {
+    w_copy(tile, ph);
+    s_copy(tile, ph / kScaleGroup);
   }
 
   // x -> f16 rows in LDS: wavefront w handles rows w, w + NW, ...: the row's
@@ -512,6 +516,68 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   const float gs = *gs_ptr;
   const float up = xup[min(r, M - 1)];
   const uint8_t* const xrow = xl + min(r, M - 1) * xpitch + 128 * g;   // this lane's k-group, chunk 0
+
+  if constexpr (KS > 1) {
+    f32x4* const red = reinterpret_cast<f32x4*>(lds + M * xpitch + 3072 * NW + 64);   // [NW][64]
+    const int kstride = gridDim.x * slots;
+    for (int t0 = blockIdx.x * slots; t0 < ntiles; t0 += kstride) {
+      tile = t0 + slot;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (tile < ntiles) {
+        for (int c = ph; c < nchunks; c += KS) {
+          __builtin_amdgcn_s_waitcnt(kWaitVm0);      // this chunk's copies have landed
+          const u32x4 w0 = *reinterpret_cast<const u32x4*>(wmine + wrd0);
+          const u32x4 w1 = *reinterpret_cast<const u32x4*>(wmine + wrd1);
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * ((c % kScaleGroup) ^ skey));
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);    // the regions may now be overwritten
+          const int cn = c + KS;
+          if (cn < nchunks) {                         // next chunk, or the next tile's first one
+            w_copy(tile, cn);
+            if (cn / kScaleGroup != c / kScaleGroup) s_copy(tile, cn / kScaleGroup);
+          } else if (tile + kstride < ntiles) {
+            w_copy(tile + kstride, ph);
+            s_copy(tile + kstride, ph / kScaleGroup);
+          }
+          float e2[4];
+          f16x2 mu[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const float sb = b == 0 ? NVFP4_E4M3_TO_F32(sw, 0) : b == 1 ? NVFP4_E4M3_TO_F32(sw, 1)
+                           : b == 2 ? NVFP4_E4M3_TO_F32(sw, 2) : NVFP4_E4M3_TO_F32(sw, 3);
+            split_scale(sb, &e2[b], &mu[b]);
+          }
+          const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          const uint8_t* const xc = xrow + 2 * kChunk * c;
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
+            acc = mfma16x16x32_f16(dequant8_f16(wd[s], e2[s >> 1], mu[s >> 1]), bx, acc);
+          }
+        }
+      }
+      red[wave * 64 + lane] = acc;
+      __syncthreads();                                // every phase of the round is in LDS
+      if (ph == 0 && tile < ntiles && r < M) {
+        f32x4 tot = red[(slot * KS) * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < KS; ++q) tot += red[(slot * KS + q) * 64 + lane];
+        tot *= up;
+        const int n0 = tile * 16 + 4 * g;
+        uint16_t* yrow = y + (kMoe ? (int64_t)moe.order[first + r] : (int64_t)r) * N;
+        if ((N & 3) == 0 && n0 + 3 < N) {
+          const uint32_t lo = out_bf16(tot[0], gs, bias, n0) | (out_bf16(tot[1], gs, bias, n0 + 1) << 16);
+          const uint32_t hi = out_bf16(tot[2], gs, bias, n0 + 2) | (out_bf16(tot[3], gs, bias, n0 + 3) << 16);
+          *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(tot[v], gs, bias, n0 + v);
+        }
+      }
+      __syncthreads();                                // the partials are read before the next round
+    }
+    return;
+  }
 
   for (; tile < ntiles; tile += stride) {
     const int n_base = tile * 16;
@@ -893,28 +959,44 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
   return hipGetLastError();
 }
 
-// Expert layer: gemv_xres_kernel<NW, true> over a (G, E) grid for experts
-// with 1..mcap pairs; mcap is the largest row count (<= 16, <= P) whose
-// activation rows fit in LDS, 0 when none does or K % 256 != 0.
-static int moe_xres_waves(int mcap, int64_t K) {
-  if (mcap < 1 || K % kChunk != 0) return 0;
-  if (xres_lds_bytes(mcap, K, 16) <= kXresLdsMax) return 16;
-  if (xres_lds_bytes(mcap, K, 8) <= kXresLdsMax) return 8;
-  return 0;
+// Expert layer: gemv_xres_kernel<NW, true, KS> over a (G, E) grid for the
+// experts with 1..mcap pairs.  The plan picks, for 16 and for 8 wavefronts,
+// the K split KS (1, 2 or 4, each wavefront keeping at least 4 chunks) that
+// gives every wavefront slot of the GPU a tile when at most min(E, P)
+// experts hold pairs, and the largest mcap (<= 16, <= P) whose activation
+// rows fit in LDS next to the weight regions (and, for KS > 1, the partial
+// tiles); the wider mcap wins, 16 wavefronts on a tie.  mcap = 0: none fits
+// or K % 256 != 0.
+static int64_t moe_xres_lds(int64_t m, int64_t K, int nw, int ks) {
+  return m * (2 * K + 16) + (int64_t)nw * 3072 + 64 + (ks > 1 ? (int64_t)nw * 1024 : 0);
 }
 
-int moe_xres_cap(int64_t P, int64_t K) {
-  for (int m = (int)std::min<int64_t>(16, P); m >= 1; --m)
-    if (moe_xres_waves(m, K)) return m;
-  return 0;
+MoeXresPlan moe_xres_plan(int64_t P, int64_t E, int64_t K, int64_t N) {
+  MoeXresPlan best{0, 0, 1};
+  if (K % kChunk != 0 || P < 1) return best;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
+  const int64_t tiles = (N + 15) / 16 * active;
+  const int64_t nchunks = K / kChunk;
+  for (int nw : {16, 8}) {
+    int ks = 1;
+    while (ks < 4 && tiles * ks < (int64_t)cus * nw && nchunks >= 8 * ks) ks *= 2;
+    int m = (int)std::min<int64_t>(16, P);
+    while (m >= 1 && moe_xres_lds(m, K, nw, ks) > kXresLdsMax) --m;
+    if (m > best.mcap) best = MoeXresPlan{m, nw, ks};
+  }
+  return best;
 }
 
-template <int NW>
+template <int NW, int KS>
 static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32_t* offsets, const int32_t* order,
                                   int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales, const float* gs,
                                   int E, int N, void* y, hipStream_t stream) {
-  const void* fn = (const void*)gemv_xres_kernel<NW, true>;
-  const int lds = (int)xres_lds_bytes(mcap, K, NW);
+  const void* fn = (const void*)gemv_xres_kernel<NW, true, KS>;
+  const int lds = (int)moe_xres_lds(mcap, K, NW, KS);
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   static std::atomic<uint64_t> attr_done{0};
@@ -929,25 +1011,31 @@ static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
   // at most min(E, P) experts have pairs: give each enough workgroups to fill the GPU
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
-  const int ntiles = (N + 15) / 16;
-  const int64_t g = std::min<int64_t>((ntiles + NW - 1) / NW, (cus * per_cu + active - 1) / active);
+  const int ntiles = (N + 15) / 16, slots = NW / KS;
+  const int64_t g = std::min<int64_t>((ntiles + slots - 1) / slots, (cus * per_cu + active - 1) / active);
   const MoeRows moe{offsets, order, row_div, mcap, 1};
-  hipLaunchKernelGGL((gemv_xres_kernel<NW, true>), dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E),
+  hipLaunchKernelGGL((gemv_xres_kernel<NW, true, KS>), dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E),
                      dim3(64 * NW), lds, stream, (const uint16_t*)x, 0, K, packed, scales, gs, N,
                      (const uint16_t*)nullptr, (uint16_t*)y, moe);
   return hipGetLastError();
 }
 
 hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
-                           int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales, const float* gs,
-                           int64_t E, int64_t N, void* y, hipStream_t stream) {
-  switch (moe_xres_waves(mcap, K)) {
-    case 16: return moe_xres_launch<16>(x, (int)row_div, (int)K, offsets, order, mcap, P, packed, scales, gs,
-                                        (int)E, (int)N, y, stream);
-    case 8: return moe_xres_launch<8>(x, (int)row_div, (int)K, offsets, order, mcap, P, packed, scales, gs,
-                                      (int)E, (int)N, y, stream);
-    default: return hipSuccess;
+                           const MoeXresPlan& plan, int64_t P, const uint8_t* packed, const uint8_t* scales,
+                           const float* gs, int64_t E, int64_t N, void* y, hipStream_t stream) {
+  if (plan.mcap < 1) return hipSuccess;
+#define NVFP4_MOE_XRES(NW_, KS_)                                                                              \
+  return moe_xres_launch<NW_, KS_>(x, (int)row_div, (int)K, offsets, order, plan.mcap, P, packed, scales, gs, \
+                                   (int)E, (int)N, y, stream)
+  if (plan.nw == 16) {
+    if (plan.ks == 4) NVFP4_MOE_XRES(16, 4);
+    if (plan.ks == 2) NVFP4_MOE_XRES(16, 2);
+    NVFP4_MOE_XRES(16, 1);
   }
+  if (plan.ks == 4) NVFP4_MOE_XRES(8, 4);
+  if (plan.ks == 2) NVFP4_MOE_XRES(8, 2);
+  NVFP4_MOE_XRES(8, 1);
+#undef NVFP4_MOE_XRES
 }
 
 // Panel width for gemv_panel_kernel: the widest multiple of 512 columns whose

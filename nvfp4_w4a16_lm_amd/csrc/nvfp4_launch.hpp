@@ -61,12 +61,18 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t P, int64_t E, int32_t* r
 hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int32_t* route_ws, int64_t P,
                            const uint8_t* packed, const uint8_t* scales, const float* gs, int64_t E, int64_t N,
                            void* y, hipStream_t stream);
-// The x-resident decode kernel over the experts with 1..mcap pairs (mcap from
-// moe_xres_cap; 0 = none), on the routing table's offsets and order.
-int moe_xres_cap(int64_t P, int64_t K);
+// The x-resident decode kernel over the experts with 1..mcap pairs, on the
+// routing table's offsets and order: its plan (mcap = 0: not used), then the
+// launch.
+struct MoeXresPlan {
+  int mcap;   // largest pair count it takes
+  int nw;     // wavefronts per workgroup
+  int ks;     // wavefronts sharing one tile's K
+};
+MoeXresPlan moe_xres_plan(int64_t P, int64_t E, int64_t K, int64_t N);
 hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
-                           int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales, const float* gs,
-                           int64_t E, int64_t N, void* y, hipStream_t stream);
+                           const MoeXresPlan& plan, int64_t P, const uint8_t* packed, const uint8_t* scales,
+                           const float* gs, int64_t E, int64_t N, void* y, hipStream_t stream);
 // The panel decode kernel over the experts with mmin..mcap pairs (mcap <= 64,
 // K % 512 == 0; otherwise nothing is launched).
 hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,

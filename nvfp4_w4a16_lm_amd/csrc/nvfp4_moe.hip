@@ -547,8 +547,9 @@ hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int3
   // experts with 1..mcap pairs: the x-resident decode kernel; with K % 512 == 0
   // the panel decode kernel takes the rest up to 64 pairs, else the split-K
   // kernel up to 48; moe_gemm_kernel takes larger experts
-  const int mcap = moe_xres_cap(P, K);
-  hipError_t err = launch_moe_xres(x, row_div, K, offsets, order, mcap, P, packed, scales, gs, E, N, y, stream);
+  const MoeXresPlan plan = moe_xres_plan(P, E, K, N);
+  const int mcap = plan.mcap;
+  hipError_t err = launch_moe_xres(x, row_div, K, offsets, order, plan, P, packed, scales, gs, E, N, y, stream);
   if (err != hipSuccess) return err;
   int small_min = mcap, large_min = kMoeSmallMax;
   if (K % 512 == 0) {

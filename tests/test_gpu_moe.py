@@ -139,9 +139,22 @@ def test_wide_experts_take_the_512_row_panel_blocks():
     check_grouped(x, 1, ids, w, y, label="wide experts")
 
 
+@pytest.mark.parametrize("K,N,E", [(2048, 100, 3), (4096, 300, 2), (8192, 40, 2)])
+def test_few_tiles_split_k_between_wavefronts(K, N, E):
+    """Experts with few rows (few 16-row tiles) and few pairs: the x-resident
+    kernel splits each tile's K between 2 or 4 wavefronts and sums their
+    partial tiles; tile rounds include slots past the last tile."""
+    w = experts(E, N, K, 98 + K)
+    ids = (np.arange(3 * E) % E).astype(np.int32)
+    x = wl.random_activation_bits(ids.size, K, seed=99)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), 1, *upload(w))
+    torch.cuda.synchronize()
+    check_grouped(x, 1, ids, w, y, label=f"split K {K}")
+
+
 def test_long_rows_cap_the_resident_rows():
-    """K = 8192: at most 8 activation rows fit in LDS, so an expert with 12
-    pairs takes the split-K kernel while one with 5 stays x-resident."""
+    """K = 8192: fewer than 12 activation rows fit in LDS, so an expert with
+    12 pairs takes the panel kernel while one with 5 stays x-resident."""
     E, K, N = 2, 8192, 80
     w = experts(E, N, K, 94)
     ids = np.array([0] * 5 + [1] * 12, np.int32)
