@@ -222,7 +222,8 @@ def bench_moe(args, mw, dev) -> int:
         "config": {"workload": mw.name, "description": mw.description, "E": E, "H": H, "I": I, "topk": topk,
                    "T": list(mw.tokens), "step": "nvfp4_moe_w4a16_forward at each T"},
         "per_op": {f"moe_forward_t{t}": v for t, v in per_t.items()},
-        "roofline": {"op": f"nvfp4_moe_w4a16_gemm (w13) T={tdom}", "kernels": "moe_route + moe_gemm",
+        "roofline": {"op": f"nvfp4_moe_w4a16_gemm (w13) T={tdom}",
+                     "kernels": "moe_route + the expert kernels of each pair-count class",
                      "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBPS, "traffic": None},
     }

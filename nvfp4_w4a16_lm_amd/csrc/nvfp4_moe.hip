@@ -17,23 +17,26 @@
 // Experts with 1..mcap pairs (mcap <= 16: as many activation rows as fit in
 //   LDS) run the lm_head path's x-resident decode kernel (gemv_xres_kernel in
 //   nvfp4_decode.hip, over a (workgroups, E) grid with the expert's gathered
-//   rows converted to f16 in LDS and weights copied straight to LDS).
+//   rows converted to f16 in LDS and weights copied straight to LDS; when the
+//   active experts have few 16-row tiles it splits each tile's K over 2 or 4
+//   wavefronts).
 // With K % 512 == 0, experts with more pairs, up to 64, run the lm_head
 //   path's panel decode kernel (gemv_panel_kernel, same row gathering).
 // moe_gemv_kernel (otherwise, the other experts with at most 48 pairs): a
 //   workgroup of 4 wavefronts owns 32 to 128 weight rows of one expert and
-//   splits K between 1, 2 or 4 of its wavefronts; each streams its weights, scales and activation
-//   fragments straight into registers one 256-k chunk ahead with no barrier,
+//   splits K between 1, 2 or 4 of its wavefronts; each streams its weights
+//   and scales straight into registers one 256-k chunk ahead (two alternating
+//   buffers) and its activation fragments per chunk, with no barrier,
 //   dequantizes exactly (code * scale is a bf16 value) and runs bf16 MFMA
 //   (v_mfma_f32_16x16x32_bf16, 16 pairs per column tile); the partial tiles
 //   are summed through LDS in wavefront order.  It also writes the zero rows
 //   of pairs whose id is outside [0, E).
-// moe_gemm_kernel (experts with more than 64, or 48, pairs): a workgroup of 4 wavefronts
-//   streams 256 weight rows of one expert once per block of 64 pairs; each
-//   wavefront owns 4 tiles of 16 rows, loads its weights straight into
-//   registers one chunk ahead and runs the same MFMA against the gathered
-//   activation rows staged in LDS.
-// In both, the k order inside a chunk is permuted identically on both
+// moe_gemm_kernel (experts with more than 64 pairs, or 48 when K % 512 !=
+//   0): a workgroup of 4 wavefronts streams 256 weight rows of one expert
+//   once per block of 64 pairs; each wavefront owns 4 tiles of 16 rows, loads
+//   its weights straight into registers one chunk ahead and runs the same
+//   MFMA against the gathered activation rows staged in LDS.
+// In the last two, the k order inside a chunk is permuted identically on both
 // operands so that a lane's codes are two 16-byte loads.
 // moe_silu_mul_kernel: a = silu(h[:, :I]) * h[:, I:] in float32, one bf16
 //   rounding.

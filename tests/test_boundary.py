@@ -227,6 +227,7 @@ def test_moe_validation(lib):
     assert call(P=0, x=0, ids=0, ws=0, y=0) == OK
     assert call(K=40) == ERR_SHAPE
     assert call(E=0) == ERR_SHAPE
+    assert call(E=65535) == ERR_SHAPE                       # the grid holds E + 1 expert rows
     assert call(div=0) == ERR_SHAPE
     assert call(rows=T - 1) == ERR_SHAPE                     # x_rows < ceil(P / row_div)
     assert call(x=X + 8) == ERR_ALIGN

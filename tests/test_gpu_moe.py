@@ -164,6 +164,24 @@ def test_long_rows_cap_the_resident_rows():
     check_grouped(x, 1, ids, w, y, label="K 8192")
 
 
+def test_more_experts_than_routing_threads():
+    """E = 1500 > 1024: the routing kernel walks the groups 1024 at a time."""
+    E, K, N, P = 1500, 256, 32, 300
+    bits = wl.moe_expert_bits(N, K, E, 0.02, 60, 0)
+    qs = [O.quantize(bits[e]) for e in range(E)]
+    w = (np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]), np.array([q[2] for q in qs], np.float32))
+    ids = np.random.default_rng(61).integers(0, E, size=P).astype(np.int32)
+    ids[:40] = 7                                           # one expert with many pairs
+    ids[40] = E + 3                                        # one id outside [0, E)
+    x = wl.random_activation_bits(P, K, seed=62)
+    inv = torch.zeros((), dtype=torch.int32, device=DEV)
+    out = torch.full((P, N), 5.0, dtype=torch.bfloat16, device=DEV)
+    B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), 1, *upload(w), out=out, invalid_pairs=inv)
+    torch.cuda.synchronize()
+    assert int(inv.item()) == 1
+    check_grouped(x, 1, ids, w, out, valid=(ids >= 0) & (ids < E), label="E 1500")
+
+
 @pytest.mark.parametrize("P,I", [(1, 8), (13, 256), (64, 1000)])
 def test_silu_and_mul(P, I):
     rng = np.random.default_rng(P + I)
