@@ -1009,10 +1009,14 @@ static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
-  // at most min(E, P) experts have pairs: give each enough workgroups to fill the GPU
+  // at most min(E, P) experts have pairs: give each the workgroups that would
+  // fill the GPU if all of them fell in this kernel's class, twice that when
+  // the pairs average more than mcap / 2 per expert (then many experts have
+  // more than mcap and belong to another kernel)
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
+  const int64_t fill = (2 * P > (int64_t)mcap * active ? 2 : 1) * (int64_t)cus * per_cu;
   const int ntiles = (N + 15) / 16, slots = NW / KS;
-  const int64_t g = std::min<int64_t>((ntiles + slots - 1) / slots, (cus * per_cu + active - 1) / active);
+  const int64_t g = std::min<int64_t>((ntiles + slots - 1) / slots, (fill + active - 1) / active);
   const MoeRows moe{offsets, order, row_div, mcap, 1};
   hipLaunchKernelGGL((gemv_xres_kernel<NW, true, KS>), dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E),
                      dim3(64 * NW), lds, stream, (const uint16_t*)x, 0, K, packed, scales, gs, N,
@@ -1072,10 +1076,11 @@ static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int3
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * 8, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
-  // at most P / mmin experts fall in the class: give each enough workgroups to fill the GPU
+  // at most P / mmin experts fall in the class: give each twice the workgroups
+  // that would fill the GPU if all of them did
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P / std::max(1, mmin)));
   const int nblocks = (N + 16 * 8 * R - 1) / (16 * 8 * R);
-  const int64_t g = std::min<int64_t>(nblocks, (cus * per_cu + active - 1) / active);
+  const int64_t g = std::min<int64_t>(nblocks, (2 * cus * per_cu + active - 1) / active);
   const MoeRows moe{offsets, order, row_div, mcap, mmin};
   return launch_kernel(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E), dim3(64 * 8), stream,
                        (const uint16_t*)x, 0, K, packed, scales, gs, N, (const uint16_t*)nullptr, (uint16_t*)y,
