@@ -99,9 +99,9 @@ def grouped_gemm_ref(x_bits: np.ndarray, row_div: int, topk_ids: np.ndarray, pac
 
 def gemm_bound(x_bits: np.ndarray, row_div: int, y64: np.ndarray, w_norm: np.ndarray,
                abs_sum: np.ndarray, K: int) -> tuple[np.ndarray, np.ndarray]:
-    """Per-element bounds of one expert GEMM's bf16 output: (north-star, tight).
+    """Per-element bounds of one expert GEMM's bf16 output: (norm bound, tight bound).
 
-    North star: ``1e-3 * ||x_row||_2 * ||w_deq_n||_2`` plus half a bf16 ulp of
+    Norm bound: ``1e-3 * ||x_row||_2 * ||w_deq_n||_2`` plus half a bf16 ulp of
     the exact result.  Tight: float32 accumulation of exact products,
     ``(K + 2) * 2^-24 * sum|x w|``, plus one bf16 rounding, ``2^-8 |y|``.
     """
@@ -144,8 +144,9 @@ def moe_ref(x_bits, topk_ids, topk_weights, w13, w2):
     """The whole layer in fp64 with no intermediate rounding, plus what its
     error bound needs.  ``w13`` / ``w2`` = (packed, scales, gs) per E2.
 
-    Returns a dict: ``out`` [T, H], ``h`` [P, 2I], ``a`` [P, I], ``o`` [P, H]
-    and the magnitudes ``h_abs`` / ``o_abs`` (``sum |x w|`` of each GEMM).
+    Returns a dict: ``out`` [T, H], ``h`` [P, 2I], ``a`` [P, I], ``o`` [P, H],
+    ``h_abs`` (``sum |x w|`` of the first GEMM), the dequantized w2 of each
+    expert with pairs (``w2deq``) and the pairs of each expert (``groups``).
     """
     ids = np.asarray(topk_ids, dtype=np.int64)
     T, k = ids.shape

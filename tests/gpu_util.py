@@ -90,9 +90,9 @@ def half_ulp_bf16(v):
 
 def check_gemm(y_bits, x_bits, packed, scales, gs, bias_bits=None, label="", argmax_min=0.999,
                pure_bound=None):
-    """Spec bound, tight fp32/bf16 bound and tie-aware argmax against the oracle.
+    """Norm bound, tight fp32/bf16 bound and tie-aware argmax against the oracle.
 
-    The benchmark spec's bound 1e-3 * ||x_m|| * ||w_n|| is applied to the bf16 output,
+    The norm bound 1e-3 * ||x_m|| * ||w_n|| is applied to the bf16 output,
     so half a bf16 ulp of the exact logit (the rounding any bf16 result carries)
     is added to it.  With ``pure_bound`` (default: K >= 512, where |cos(x_m, w_n)|
     stays far below 0.25 for these inputs) the bound must also hold without it.
@@ -101,18 +101,18 @@ def check_gemm(y_bits, x_bits, packed, scales, gs, bias_bits=None, label="", arg
     y64, wn, s_abs = O.gemm_ref_with_norms(x_bits, packed, scales, gs, bias_bits)
     xn = np.linalg.norm(wl.bf16_bits_to_f32(x_bits).astype(np.float64), axis=1)
     bias_abs = 0.0 if bias_bits is None else np.abs(wl.bf16_bits_to_f32(bias_bits).astype(np.float64))[None, :]
-    # spec bound: 1e-3 * ||x_m|| * ||w_n|| (+ bf16 rounding of a bias term)
+    # norm bound: 1e-3 * ||x_m|| * ||w_n|| (+ bf16 rounding of a bias term)
     tol = 1e-3 * xn[:, None] * wn[None, :] + 2.0 ** -8 * bias_abs
     err = np.abs(y - y64)
     if pure_bound is None:
         pure_bound = x_bits.shape[1] >= 512
     if pure_bound:
         worst = np.unravel_index(np.argmax(err - tol), err.shape)
-        assert np.all(err <= tol), (f"{label}: north-star bound (no output-rounding term) broken at "
+        assert np.all(err <= tol), (f"{label}: norm bound (no output-rounding term) broken at "
                                     f"{worst}: y={y[worst]} y64={y64[worst]} tol={tol[worst]}")
     tol = tol + half_ulp_bf16(y64)
     worst = np.unravel_index(np.argmax(err - tol), err.shape)
-    assert np.all(err <= tol), (f"{label}: north-star bound broken at {worst}: y={y[worst]} "
+    assert np.all(err <= tol), (f"{label}: norm bound broken at {worst}: y={y[worst]} "
                                 f"y64={y64[worst]} tol={tol[worst]}")
     # tight bound: fp32 accumulation of K exact products in any order, the scale and
     # bias operations, then one round-to-nearest to bf16.  The f16 decode route
@@ -134,7 +134,7 @@ def check_gemm(y_bits, x_bits, packed, scales, gs, bias_bits=None, label="", arg
 
 
 def check_fp8_gemm(y_bits, xq, xs, wq, ws, bias_bits=None, label="", argmax_min=0.999):
-    """Spec bound 1e-3 |x_m| |w_n| on the dequantized operands, and a
+    """Norm bound 1e-3 |x_m| |w_n| on the dequantized operands, and a
     tight bound for the arithmetic: v_mfma_f32_16x16x32_fp8_fp8 sums its 32
     products in reduced precision (errors up to 2^-16.7 of sum|x w| were
     measured on single instructions, far more than float32 rounding), so the
@@ -146,7 +146,7 @@ def check_fp8_gemm(y_bits, xq, xs, wq, ws, bias_bits=None, label="", argmax_min=
     xn = np.linalg.norm(F.e4m3_decode_signed(xq) * np.asarray(xs, np.float64)[:, None], axis=1)
     wn = np.linalg.norm(F.e4m3_decode_signed(wq) * np.asarray(ws, np.float64)[:, None], axis=1)
     ns = 1e-3 * xn[:, None] * wn[None, :] + 2.0 ** -8 * np.abs(y64)
-    assert np.all(np.abs(y - y64) <= ns), f"{label}: north-star bound"
+    assert np.all(np.abs(y - y64) <= ns), f"{label}: norm bound"
     k = xq.shape[1]
     acc = (2.0 ** -14 + (k + 4) * 2.0 ** -24) * yabs
     tight = 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133
@@ -169,7 +169,7 @@ def check_w4a4(y_bits, xp, xs, wp, ws, a, bias_bits=None, label="", argmax_min=0
     wn = np.linalg.norm(A.block_values(wp, ws), axis=1)
     ns = 1e-3 * float(a) * xn[:, None] * wn[None, :] + 2.0 ** -8 * np.abs(y64)
     err = np.abs(y - y64)
-    assert np.all(err <= ns), f"{label}: north-star bound"
+    assert np.all(err <= ns), f"{label}: norm bound"
     k = xp.shape[1] * 2
     acc = (k + 4) * 2.0 ** -24 * yabs
     tight = 1.01 * (acc + 2.0 ** -8 * (np.abs(y64) + acc)) + 2.0 ** -133

@@ -2,7 +2,7 @@
 
 Row quantization (weights per output row, activations per token): every byte
 and every scale bit.  GEMM: every logit against the float64 reference of the
-same quantized operands, within the benchmark spec's bound and a tight bound set by
+same quantized operands, within the norm bound and a tight bound set by
 the fp8 MFMA's accumulation precision (see check_fp8_gemm), and the argmax.
 """
 

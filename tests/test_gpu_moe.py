@@ -3,7 +3,7 @@ oracle/nvfp4_moe_oracle.py.
 
 Grouped GEMM: every output of every pair against the fp64 reference on the
 oracle's quantized experts, within the float32-accumulation bound plus one
-bf16 rounding, and the benchmark spec's bound; routing edge cases (experts with no
+bf16 rounding, and the norm bound; routing edge cases (experts with no
 pair, more than one 64-pair block, ids outside [0, E), ragged K and N).
 SiLU-and-mul and combine: every element on seeded inputs.  The whole layer:
 every output within the oracle's propagated bound.
@@ -55,7 +55,7 @@ def check_grouped(x_bits, row_div, ids, w, got, valid=None, label=""):
         g, y64, loose, tight = g[valid], y64[valid], loose[valid], tight[valid]
     err = np.abs(g - y64)
     assert np.all(err <= tight), f"{label}: tight bound, worst {np.max(err - tight):.3e}"
-    assert np.all(err <= loose), f"{label}: north-star bound"
+    assert np.all(err <= loose), f"{label}: norm bound"
 
 
 @pytest.mark.parametrize("E,H,N,T,topk", [
