@@ -1,4 +1,4 @@
-"""HIP-graph capture of the checkpoint, FP8 and W4A4 calls: each sequence is
+"""HIP-graph capture of the checkpoint, FP8, W4A4 and expert-layer calls: each sequence is
 captured once, then replayed with new inputs written into the captured
 buffers, with eager work between replays; every replay must equal the eager
 result (and, for the quantizers, the oracle)."""
@@ -105,3 +105,43 @@ def test_import_graph_replays():
         torch.cuda.synchronize()
         want_gs, want_f = I.import_report(part.cpu().numpy(), s, I.COMPRESSED_TENSORS)
         assert f32_bits(gs.item()) == f32_bits(want_gs) and int(flags.item()) == want_f
+
+
+def test_moe_forward_graph_replays_with_new_routing():
+    """The expert layer holds no host synchronisation (routing runs on the
+    device), so one captured forward replays with new activations, new ids
+    and new routing weights written into the captured buffers; every replay
+    equals the eager layer bit for bit (the kernels are deterministic)."""
+    import oracle.nvfp4_oracle as O
+
+    E, H, I, T, topk = 6, 512, 256, 12, 2
+    experts = []
+    for rows, k, s0 in ((2 * I, H, 10), (H, I, 1000)):
+        bits = wl.moe_expert_bits(rows, k, E, 0.02, 77, s0)
+        qs = [O.quantize(bits[e]) for e in range(E)]
+        experts.append((dev_u8(np.stack([q[0] for q in qs])), dev_u8(np.stack([q[1] for q in qs])),
+                        torch.tensor(np.array([q[2] for q in qs], np.float32), device=DEV)))
+    w13, w2 = experts
+    xbuf = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=DEV)
+    tw = torch.empty((T, topk), dtype=torch.float32, device=DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((int(B.load_library().nvfp4_moe_workspace_bytes(T, topk, E, H, I)),), dtype=torch.uint8,
+                     device=DEV)
+
+    def load(seed):
+        xbuf.copy_(dev_bf16(wl.random_activation_bits(T, H, seed=seed)))
+        i, w = wl.moe_routing(T, E, topk, seed)
+        ids.copy_(torch.from_numpy(i))
+        tw.copy_(torch.from_numpy(w))
+
+    load(40)
+    graph = capture(lambda: B.nvfp4_moe_w4a16_forward(xbuf, ids, tw, w13, w2, out=out, workspace=ws))
+    for seed in (41, 42, 43):
+        load(seed)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host_bits(out)
+        eager = host_bits(B.nvfp4_moe_w4a16_forward(xbuf.clone(), ids.clone(), tw.clone(), w13, w2))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager), f"replay {seed} differs from the eager layer"
