@@ -118,6 +118,52 @@ def cpu_baseline(wl, w, w_bits, x_bits, ms, budget_s: float):
     }
 
 
+def moe_cpu_baseline(mw, w13_bits, w2_bits, x_bits, budget_s: float):
+    """The oracle's whole expert layer, as it stands, on a bounded sample of
+    the workload: the intermediate dimension cut to its first ``i_s`` columns
+    (w13 rows [0, i_s) and [I, I + i_s), w2 columns [0, i_s)), every expert
+    and every token count, sized from a short calibration run to about
+    ``budget_s`` seconds.  The experts are quantized by the oracle first
+    (not timed)."""
+    import numpy as np
+
+    import oracle.nvfp4_oracle as O
+    import oracle.nvfp4_moe_oracle as MO
+    from nvfp4_w4a16_lm_amd import workloads as wl
+
+    E, H, I, topk = mw.experts, mw.hidden, mw.inter, mw.topk
+
+    def quant(bits):
+        qs = [O.quantize(bits[e]) for e in range(E)]
+        return (np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]),
+                np.array([q[2] for q in qs], dtype=np.float32))
+
+    def layer(i_s):
+        w13 = quant(np.concatenate([w13_bits[:, :i_s], w13_bits[:, I:I + i_s]], axis=1))
+        w2 = quant(np.ascontiguousarray(w2_bits[:, :, :i_s]))
+        t0 = time.perf_counter()
+        nbytes = 0.0
+        for T in mw.tokens:
+            ids, tw = wl.moe_routing(T, E, topk, mw.cfg)
+            MO.moe_ref(x_bits[:T], ids, tw, w13, w2)
+            b13, b2 = moe_active_bytes(ids, E, H, i_s)
+            nbytes += b13 + b2 + 4 * T * H
+        return time.perf_counter() - t0, nbytes
+
+    probe = 64
+    dt, _ = layer(probe)
+    i_s = int(min(I, max(probe, probe * budget_s / max(dt, 1e-6))) // 16 * 16)
+    dt, nbytes = layer(i_s)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(blas), "kind": "oracle",
+            "sample": (f"intermediate dimension {i_s} of {I} (all {E} experts, H {H}), T = {list(mw.tokens)}: "
+                       f"the fp64 layer; {dt:.1f} s; numpy elementwise on 1 thread, BLAS on {blas}")}
+
+
 def moe_active_bytes(ids, E: int, H: int, I: int):
     """NVFP4 bytes of the experts that receive at least one pair: (w13, w2)."""
     import numpy as np
@@ -161,7 +207,6 @@ def bench_moe(args, mw, dev) -> int:
 
     w13 = quant_experts(w13_bits, 2 * I, H)
     w2 = quant_experts(w2_bits, H, I)
-    del w13_bits, w2_bits
     X = to_dev(x_bits)
     torch.cuda.synchronize()
     per_t = {}
@@ -227,6 +272,9 @@ def bench_moe(args, mw, dev) -> int:
                      "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBPS, "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = moe_cpu_baseline(mw, w13_bits, w2_bits, x_bits, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

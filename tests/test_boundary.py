@@ -242,3 +242,19 @@ def test_moe_validation(lib):
     f = lib.nvfp4_moe_w4a16_forward
     assert f(X, T, H, B, G + 4096, k, P, S, G, W + 4096, S + 4096, G + 8192, E, 40, W, Y, None, None) == ERR_SHAPE
     assert f(X, T, H, B, G + 4096, k, P, S, G, W + 4096, S + 4096, G + 8192, E, I, 0, Y, None, None) == ERR_NULL
+
+
+def test_binding_collapses_w13_scale2_to_the_w1_column():
+    """ModelOpt's fused w13 keeps one global scale per expert, the w1 column,
+    with a warning when the w3 column differs (host logic, CPU tensors)."""
+    import warnings
+
+    import torch
+    same = torch.tensor([[0.5, 0.5], [0.25, 0.25]], dtype=torch.float32)
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        assert torch.equal(binding.moe_collapse_w13_scale2(same), torch.tensor([0.5, 0.25]))
+    differ = torch.tensor([[0.5, 0.5], [0.25, 0.375]], dtype=torch.float32)
+    with pytest.warns(UserWarning):
+        got = binding.moe_collapse_w13_scale2(differ)
+    assert torch.equal(got, torch.tensor([0.5, 0.25]))
