@@ -642,3 +642,45 @@ def _e4m3_ref(u):
 def test_planted_mistakes_are_caught(name, overrides, facts, worked):
     assert _pins_fail(O, facts, worked) == 0
     assert _pins_fail(mutant(**overrides), facts, worked) >= 1, name
+
+
+def _sweep_float32(top_value, chunk, fn):
+    """Run ``fn`` over every non-negative float32 up to ``top_value`` (bit
+    patterns 0 .. bits(top_value)) in chunks on a thread pool; returns the
+    summed counts ``fn`` reports."""
+    import concurrent.futures
+
+    top = int(np.float32(top_value).view(np.uint32))
+
+    def work(c0):
+        u = np.arange(c0, min(top + 1, c0 + chunk), dtype=np.uint32).view(np.float32)
+        return fn(u)
+
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        return sum(ex.map(work, range(0, top + 1, chunk)))
+
+
+@pytest.mark.slow
+def test_e4m3_rne_exhaustive_against_torch_cast():
+    """Every float32 of [0, 448] (1.14e9 values): the oracle's E4M3 rounding
+    equals torch's float8_e4m3fn cast, the cast the page applies."""
+    def bad(u):
+        theirs = torch.from_numpy(u).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        return int(np.count_nonzero(O.e4m3_encode_rne(u) != theirs))
+
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)                         # the sweep's own threads split the work
+    try:
+        assert _sweep_float32(448.0, 1 << 22, bad) == 0
+    finally:
+        torch.set_num_threads(threads)
+
+
+@pytest.mark.slow
+def test_e2m1_rne_exhaustive_against_search():
+    """Every float32 of [0, 6] (1.09e9 values): the oracle's interval form of
+    E2M1 rounding equals the nearest-grid-value search with ties to even."""
+    def bad(u):
+        return int(np.count_nonzero(O.e2m1_magnitude_code(u) != brute_e2m1(u)))
+
+    assert _sweep_float32(6.0, 1 << 20, bad) == 0
