@@ -282,7 +282,7 @@ def bench_moe(args, mw, dev) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b",
                     help="llama3_8b (default), llama3_70b, qwen_prefill, heavy_tail, tiny; "
@@ -378,6 +378,9 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
 
     avg_ms = {op: float(np.mean([a.elapsed_time(b) for a, b in ev[op]])) for op in ops}
+    # spread of the per-call times: min, median, 90th percentile
+    spread = {op: {"ms_min": float(np.min(t)), "ms_p50": float(np.median(t)), "ms_p90": float(np.percentile(t, 90))}
+              for op in ops for t in [[a.elapsed_time(b) for a, b in ev[op]]]}
 
     # Pre-quantized checkpoint import (not part of the step): global scale from
     # the partition scales + one NaN scan of the block scales, timed the same way.
@@ -456,7 +459,7 @@ def main() -> int:
     step_bytes = quant_bytes(n, k) + sum(gemm_bytes(m, n, k) for m in ms)
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
 
-    per_op = {"quantize": {"ms": avg_ms["quantize"],
+    per_op = {"quantize": {"ms": avg_ms["quantize"], **spread["quantize"],
                            "GB/s": quant_bytes(n, k) / (avg_ms["quantize"] * 1e-3) / 1e9}}
     per_op["import_checkpoint"] = {"ms": imp_ms, "GB/s": imp_bytes / (imp_ms * 1e-3) / 1e9,
                                    "kernels": "import_prepare (1 wavefront) + scale_nan_scan",
@@ -479,7 +482,7 @@ def main() -> int:
                                 "in_step": False}
     for m in ms:
         t = avg_ms[f"gemm_m{m}"] * 1e-3
-        per_op[f"gemm_m{m}"] = {"ms": avg_ms[f"gemm_m{m}"],
+        per_op[f"gemm_m{m}"] = {"ms": avg_ms[f"gemm_m{m}"], **spread[f"gemm_m{m}"],
                                 "TB/s": gemm_bytes(m, n, k) / t / 1e12,
                                 "TFLOP/s": gemm_flops(m, n, k) / t / 1e12}
 
