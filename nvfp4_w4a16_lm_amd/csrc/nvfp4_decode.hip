@@ -668,7 +668,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
     packed += (int64_t)e * N * (K >> 1);
     scales += (int64_t)e * N * (K >> 4);
     gs_ptr += e;
+    pk = min(K, (kPanelXBytes / M / 2) / 512 * 512);  // the widest panel this expert's rows fit
   }
+  static_assert(kPanelXBytes >= 16 * MT * 512 * 2, "a panel must hold 512 columns of 16 MT rows");
   constexpr int kRows = 16 * kPanelR;                   // weight rows per wavefront
   __shared__ __attribute__((aligned(16))) uint8_t xp[kPanelXBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wl[NW][kRows * 128];
