@@ -48,6 +48,19 @@ def test_shapes(m, n, k):
     check_gemm(y, x, packed, scales, gs, label=f"m={m} n={n} k={k}", argmax_min=0.99 if n < 20 else 0.999)
 
 
+# more 256 x 256 prefill tiles than the GPU has compute units (several waves
+# of workgroups), every logit checked: 3, 4 and 5 steps of 64 k per tile,
+# ragged M and N, odd N, bias
+@pytest.mark.parametrize("m,n,k,with_bias", [(1900, 20000, 192, False), (800, 33000, 256, False),
+                                             (1100, 30001, 320, True)])
+def test_prefill_many_tiles(m, n, k, with_bias):
+    w, packed, scales, gs, q = setup(n, k, seed=m)
+    x = wl.random_activation_bits(m, k, seed=n)
+    bias = wl.bias_bits(n, seed=k, sigma=0.5) if with_bias else None
+    y = gemm_gpu(x, q, bias)
+    check_gemm(y, x, packed, scales, gs, bias_bits=bias, label=f"tiles m={m} n={n} k={k}")
+
+
 @pytest.mark.parametrize("m", [1, 8, 64, 200])
 def test_bias(m):
     n, k = 515, 1024
