@@ -62,9 +62,9 @@ WORKLOADS = {
                                        "refresh after N(0,1e-3) noise"),
     "qwen_prefill": Workload("qwen_prefill", 4, 151936, 5120, 0.02, (4096,), 4096,
                              description="lm_head 151936x5120 N(0,0.02); prefill M=4096"),
-    "heavy_tail": Workload("heavy_tail", 5, 129280, 7168, 0.01, (8192, 1), 8192, "heavy",
+    "heavy_tail": Workload("heavy_tail", 5, 129280, 7168, 0.01, (1, 8192), 8192, "heavy",
                            description="lm_head 129280x7168 0.01*t(3), zero row 0, "
-                                       "E2M1-grid row N-1; M=8192 and M=1"),
+                                       "E2M1-grid row N-1; M=1 and M=8192"),
 }
 
 
