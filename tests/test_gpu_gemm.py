@@ -48,6 +48,19 @@ def test_shapes(m, n, k):
     check_gemm(y, x, packed, scales, gs, label=f"m={m} n={n} k={k}", argmax_min=0.99 if n < 20 else 0.999)
 
 
+# M <= 16 with x too large for LDS (and M <= 2 past the dot kernel's K): the
+# panel kernel, several 512-row blocks with a ragged last one, K of 20 and
+# 32 K columns, bias on one row count
+@pytest.mark.parametrize("m", [1, 2, 5, 12, 16])
+@pytest.mark.parametrize("n,k", [(1100, 16384), (700, 10240)])
+def test_decode_panel_rows_up_to_16(m, n, k):
+    w, packed, scales, gs, q = setup(n, k, seed=m + 7)
+    x = wl.random_activation_bits(m, k, seed=n + m)
+    bias = wl.bias_bits(n, seed=m, sigma=0.5) if m == 12 else None
+    y = gemm_gpu(x, q, bias)
+    check_gemm(y, x, packed, scales, gs, bias_bits=bias, label=f"panel m={m} n={n} k={k}")
+
+
 # more 256 x 256 prefill tiles than the GPU has compute units (several waves
 # of workgroups), every logit checked: 3, 4 and 5 steps of 64 k per tile,
 # ragged M and N, odd N, bias
