@@ -22,14 +22,11 @@
 //   (double buffered), and each wavefront reuses those fragments for R tiles
 //   of 16 weight rows, with the next chunk's weights prefetched into
 //   registers while the current one computes.
-#include <atomic>
-
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
 namespace nvfp4 {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0) alone / lgkmcnt(0) alone
 constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
@@ -41,29 +38,8 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
 __device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// E4M3 scale s (as fp32) = e2 * mu: e2 = 2^e (its exponent field), mu in
-// [1, 2) (its significand, 3 fraction bits) as an f16 pair; s = 0 gives mu 0.
-__device__ __forceinline__ void split_scale(float s, float* e2, f16x2* mu) {
-  const uint32_t b = __float_as_uint(s);
-  *e2 = __uint_as_float(b & 0x7F800000u);
-  const _Float16 m = (s == 0.0f) ? (_Float16)0.0f : (_Float16)__uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
-  *mu = f16x2{m, m};
-}
-
-// Codes 0..7 of w (low nibble first) times e2 * mu, exact in f16.
-__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float e2, f16x2 mu) {
-  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 0) * mu;
-  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 1) * mu;
-  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 2) * mu;
-  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 3) * mu;
-  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
 __device__ __forceinline__ uint32_t out_bf16(float acc, float gs, const uint16_t* __restrict__ bias, int n) {
@@ -881,11 +857,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_ragged_kernel(const uint16_t* _
 // ---------------------------------------------------------------------------
 // Workgroups of 256 threads that fit on the device at once (occupancy x CUs).
 static int resident_workgroups(const void* kernel) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1024;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
-  return cus * per_cu;
+  const int dev = current_device();
+  return device_cus(dev) * blocks_per_cu(kernel, dev, 256, 0);
 }
 
 template <int MR, int SEG>
@@ -940,25 +913,14 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
   const void* fn = (const void*)gemv_xres_kernel<NW>;
   const int lds = (int)xres_lds_bytes(M, K, NW);
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  // raise the dynamic LDS limit (the default allows less than the hardware's
-  // 160 KiB) once per kernel and device; concurrent first calls both set it
-  static std::atomic<uint64_t> attr_done{0};
-  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
-  if (bit == 0 || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kXresLdsMax);
-    if (e != hipSuccess) return e;
-    attr_done.fetch_or(bit, std::memory_order_release);
-  }
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const int dev = current_device();
+  const hipError_t e = ensure_dynamic_lds(fn, dev, kXresLdsMax);
+  if (e != hipSuccess) return e;
   const int ntiles = (N + 15) / 16;
-  const int grid = std::max(1, std::min((ntiles + NW - 1) / NW, cus * per_cu));
-  hipLaunchKernelGGL((gemv_xres_kernel<NW>), dim3(grid), dim3(64 * NW), lds, stream, (const uint16_t*)x, M, K,
-                     packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y, MoeRows{});
-  return hipGetLastError();
+  const int resident = device_cus(dev) * blocks_per_cu(fn, dev, 64 * NW, lds);
+  const int grid = std::max(1, std::min((ntiles + NW - 1) / NW, resident));
+  return launch_kernel_lds(fn, dim3(grid), dim3(64 * NW), lds, stream, (const uint16_t*)x, M, K, packed, scales, gs,
+                           N, (const uint16_t*)bias, (uint16_t*)y, MoeRows{});
 }
 
 // Expert layer: gemv_xres_kernel<NW, true, KS> over a (G, E) grid for the
@@ -976,10 +938,7 @@ static int64_t moe_xres_lds(int64_t m, int64_t K, int nw, int ks) {
 MoeXresPlan moe_xres_plan(int64_t P, int64_t E, int64_t K, int64_t N) {
   MoeXresPlan best{0, 0, 1};
   if (K % kChunk != 0 || P < 1) return best;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cus(current_device());
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
   const int64_t tiles = (N + 15) / 16 * active;
   const int64_t nchunks = K / kChunk;
@@ -999,18 +958,10 @@ static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32
                                   int E, int N, void* y, hipStream_t stream) {
   const void* fn = (const void*)gemv_xres_kernel<NW, true, KS>;
   const int lds = (int)moe_xres_lds(mcap, K, NW, KS);
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  static std::atomic<uint64_t> attr_done{0};
-  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
-  if (bit == 0 || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kXresLdsMax);
-    if (e != hipSuccess) return e;
-    attr_done.fetch_or(bit, std::memory_order_release);
-  }
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const int dev = current_device();
+  const hipError_t e = ensure_dynamic_lds(fn, dev, kXresLdsMax);
+  if (e != hipSuccess) return e;
+  const int cus = device_cus(dev), per_cu = blocks_per_cu(fn, dev, 64 * NW, lds);
   // at most min(E, P) experts have pairs: give each the workgroups that would
   // fill the GPU if all of them fell in this kernel's class, twice that when
   // the pairs average more than mcap / 2 per expert (then many experts have
@@ -1020,10 +971,9 @@ static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32
   const int ntiles = (N + 15) / 16, slots = NW / KS;
   const int64_t g = std::min<int64_t>((ntiles + slots - 1) / slots, (fill + active - 1) / active);
   const MoeRows moe{offsets, order, row_div, mcap, 1};
-  hipLaunchKernelGGL((gemv_xres_kernel<NW, true, KS>), dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E),
-                     dim3(64 * NW), lds, stream, (const uint16_t*)x, 0, K, packed, scales, gs, N,
-                     (const uint16_t*)nullptr, (uint16_t*)y, moe);
-  return hipGetLastError();
+  return launch_kernel_lds(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E), dim3(64 * NW), lds, stream,
+                           (const uint16_t*)x, 0, K, packed, scales, gs, N, (const uint16_t*)nullptr, (uint16_t*)y,
+                           moe);
 }
 
 hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
@@ -1056,12 +1006,8 @@ static hipError_t panel_launch(const void* x, int M, int K, const uint8_t* packe
                                const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
   const void* fn = (const void*)gemv_panel_kernel<MT, NW, R>;
   const int nblocks = (N + 16 * NW * R - 1) / (16 * NW * R);
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
-  const dim3 grid(std::min(nblocks, cus * per_cu));
+  const int dev = current_device();
+  const dim3 grid(std::min(nblocks, device_cus(dev) * blocks_per_cu(fn, dev, 64 * NW, 0)));
   return launch_kernel(fn, grid, dim3(64 * NW), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
                        (const uint16_t*)bias, (uint16_t*)y, panel_columns(M, K), MoeRows{});
 }
@@ -1073,11 +1019,8 @@ static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int3
                                    int mmin, int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales,
                                    const float* gs, int E, int N, void* y, hipStream_t stream) {
   const void* fn = (const void*)gemv_panel_kernel<MT, 8, R, true>;
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * 8, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  const int dev = current_device();
+  const int cus = device_cus(dev), per_cu = blocks_per_cu(fn, dev, 64 * 8, 0);
   // at most P / mmin experts fall in the class: give each twice the workgroups
   // that would fill the GPU if all of them did
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P / std::max(1, mmin)));

@@ -94,4 +94,30 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
   return __builtin_bit_cast(bf16x8, o);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// E4M3 scale s (as fp32) = e2 * mu: e2 = 2^e (its exponent field), mu in
+// [1, 2) (its significand, 3 fraction bits) as an f16 pair; s = 0 gives mu 0.
+// The fp4 converters below apply only the exponent of their fp32 scale, so
+// they take e2 and the mantissa mu is applied separately.
+__device__ __forceinline__ void split_scale(float s, float* e2, f16x2* mu) {
+  const uint32_t b = __float_as_uint(s);
+  *e2 = __uint_as_float(b & 0x7F800000u);
+  const _Float16 m = (s == 0.0f) ? (_Float16)0.0f : (_Float16)__uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
+  *mu = f16x2{m, m};
+}
+
+// Codes 0..7 of w (low nibble first) times e2 * mu, exact in f16: the
+// converter applies e2 exactly and code * e2 * mu has at most 6 significant
+// bits within [2^-10, 2688].
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float e2, f16x2 mu) {
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 0) * mu;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 1) * mu;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 2) * mu;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 3) * mu;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
 }  // namespace nvfp4
