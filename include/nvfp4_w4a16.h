@@ -114,9 +114,22 @@ nvfp4_status nvfp4_refresh_inplace(const void* W, int64_t N, int64_t K,
  *
  *   y[m, n] = bf16_rne( global_scale * sum_k x[m,k] * E2M1(code[n,k]) * e4m3(scale[n,k/16])
  *                       + bias[n] )
- * with fp32 accumulation (products of a bf16 and a dequantized weight are
- * exact in fp32; summation order is unspecified but deterministic).
- * M <= 64 runs the streaming decode kernel, larger M the MFMA prefill kernel.
+ * with fp32 accumulation; summation order is unspecified but deterministic.
+ * The dequantized weight E2M1 * e4m3 is exact (at most 6 significant bits).
+ * M <= 64 runs the streaming decode kernels, larger M the MFMA prefill kernel.
+ *
+ * Products: the prefill kernel and most decode kernels multiply the bf16
+ * activations as given, so every product is exact in fp32.  The decode kernel
+ * for 3 <= M <= 16 that holds the whole activation in LDS (K a multiple of
+ * 256 and M * (2K + 16) bytes small enough) stages each activation row
+ * m in f16 as x * 2^-p_m, with the power of two chosen from the row's largest
+ * magnitude so that it lands in [2^14, 2^15), and multiply the f16 results by
+ * 2^p_m in fp32.  An activation with |x| >= 2^-28 * max_k |x[m,k]| converts
+ * exactly (bf16's 8 significant bits fit f16's 11); a smaller one may move by
+ * at most max(2^-39 * max_k |x[m,k]|, 2^-151), half the f16 subnormal spacing
+ * at that scale.  Each y[m, n] may therefore differ from the exact-product
+ * sum by at most that bound times sum_k |w[n,k]| before the fp32 summation
+ * and bf16 rounding errors; no other rounding enters.
  */
 nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t M, int64_t K,
                               const uint8_t* packed, const uint8_t* scales,
