@@ -4,14 +4,91 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 namespace nvfp4 {
 
 // hipLaunchKernel with a typed argument pack.  The argument types must match
 // the kernel's parameter types exactly (callers cast at the call site).
+// Returns the launch's own status.
+template <typename... Args>
+inline hipError_t launch_kernel_lds(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                    Args... args) {
+  void* argv[] = {(void*)&args..., nullptr};
+  return hipLaunchKernel(fn, grid, block, argv, lds, stream);
+}
+
 template <typename... Args>
 inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
-  void* argv[] = {(void*)&args..., nullptr};
-  return hipLaunchKernel(fn, grid, block, argv, 0, stream);
+  return launch_kernel_lds(fn, grid, block, 0, stream, args...);
+}
+
+// The current device (0 if the query fails).
+inline int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess ? dev : 0;
+}
+
+// Compute units of device dev, queried once per device (256 if the query fails;
+// a failed query is not cached and its error is cleared so that it cannot be
+// reported by a later launch check).
+inline int device_cus(int dev) {
+  static std::atomic<int> cache[64];
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Resident workgroups per compute unit of kernel fn with `block` threads and
+// `lds` bytes of dynamic LDS on device dev, queried once per (kernel, device,
+// block, lds) (1 if the query fails; not cached, error cleared).
+inline int blocks_per_cu(const void* fn, int dev, int block, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, int, size_t>, int> cache;
+  const auto key = std::make_tuple(fn, dev, block, lds);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds) != hipSuccess || per_cu <= 0) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = per_cu;
+  return per_cu;
+}
+
+// Raise kernel fn's dynamic LDS limit to `bytes` once per (kernel, device)
+// (the default allows less than the hardware's 160 KiB).  Concurrent first
+// calls may both set it, which is harmless.
+inline hipError_t ensure_dynamic_lds(const void* fn, int dev, int bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> done;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    const auto it = done.find({fn, dev});
+    if (it != done.end() && it->second >= bytes) return hipSuccess;
+  }
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(mu);
+  int& v = done[{fn, dev}];
+  if (v < bytes) v = bytes;
+  return hipSuccess;
 }
 
 // Quantization: amax -> global scale -> block scales + packed codes.
