@@ -12,7 +12,10 @@ touched (the 8B-shape weights, 296 MB, would otherwise partly hit the
 
 Prints one JSON line: value = algorithmic bytes of the step / step time
 (TB/s), plus per-operation rates, the roofline of the dominant operation and
-the CPU oracle timed on a bounded sample.
+the CPU oracle timed on a bounded sample.  After the step, the prefill GEMM of
+the Qwen-shaped workload (151936 x 5120, M = 4096) is timed on its own and
+reported in per_op with its MFMA roofline (the TFLOP/s half of the metric).
+The SHA-256 of every input tensor and the oracle host's CPUs are recorded.
 """
 
 from __future__ import annotations
@@ -55,6 +58,83 @@ def decode_kernel_name(m: int, k: int) -> str:
     if 3 <= m <= 16 and m * (2 * k + 16) + 8 * 3072 + 64 <= 160 * 1024:
         return "gemv_xres_kernel"
     return "gemv_panel_kernel" if k % 512 == 0 else "gemv_mfma_kernel"
+
+
+def sha256_bits(a) -> str:
+    """SHA-256 of an input tensor's bytes (bf16 bit patterns, row-major)."""
+    import numpy as np
+
+    return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+
+
+def host_info() -> dict:
+    """The host the oracle runs on: logical CPUs, the ones this process may
+    use, and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count() or 1, "usable_cpus": usable, "cpu_model": model}
+
+
+def bench_prefill(args, dev, to_dev):
+    """The prefill GEMM of the Qwen-shaped workload (151936 x 5120, M = 4096),
+    timed outside the step: quantize once, then the GEMM per call with HIP
+    events on the stream it is launched on."""
+    import numpy as np
+    import torch
+
+    from nvfp4_w4a16_lm_amd import binding as B
+    from nvfp4_w4a16_lm_amd import workloads as wl
+
+    pw = wl.WORKLOADS[args.prefill_workload]
+    t0 = time.perf_counter()
+    pb = wl.weight_bits(pw)
+    px = wl.activation_bits(pw)
+    m = max(pw.ms)
+    inputs = {f"{pw.name}/W": sha256_bits(pb), f"{pw.name}/x": sha256_bits(px[:m])}
+    print(f"# prefill inputs generated and hashed in {time.perf_counter() - t0:.1f} s: W {pw.n}x{pw.k}, "
+          f"x {m}x{pw.k}", file=sys.stderr, flush=True)
+    W = to_dev(pb)
+    del pb
+    X = to_dev(px[:m])
+    q = B.nvfp4_quantize(W)
+    del W
+    Y = torch.empty((m, pw.n), dtype=torch.bfloat16, device=dev)
+    for _ in range(max(1, args.warmup)):
+        B.nvfp4_w4a16_gemm(X, *q, out=Y)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(args.prefill_steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.nvfp4_w4a16_gemm(X, *q, out=Y)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = float(np.mean(t))
+    achieved = gemm_flops(m, pw.n, pw.k) / (ms * 1e-3) / 1e12
+    rec = {"ms": ms, "ms_min": float(np.min(t)), "ms_p50": float(np.median(t)), "ms_p90": float(np.percentile(t, 90)),
+           "TFLOP/s": achieved, "TB/s": gemm_bytes(m, pw.n, pw.k) / (ms * 1e-3) / 1e12,
+           "calls": int(args.prefill_steps), "in_step": False,
+           "shape": {"N": pw.n, "K": pw.k, "M": m},
+           "roofline": {"op": f"nvfp4_w4a16_gemm M={m} ({pw.name})", "kernels": "gemm_prefill_kernel",
+                        "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": achieved / BF16_PEAK_TFLOPS, "traffic": load_traffic(pw.name, f"gemm_m{m}")}}
+    del q, X, Y
+    torch.cuda.synchronize()
+    return f"prefill_{pw.name}_m{m}", rec, inputs
 
 
 def kernel_source_hash() -> str:
@@ -115,6 +195,7 @@ def cpu_baseline(wl, w, w_bits, x_bits, ms, budget_s: float):
         "kind": "oracle",
         "sample": (f"{rows} of {w.n} weight rows ({w.k} columns): amax + quantize, then fp64 GEMM at "
                    f"M={list(ms)}; {dt:.1f} s; numpy elementwise on 1 thread, BLAS on {blas}"),
+        **host_info(),
     }
 
 
@@ -161,7 +242,8 @@ def moe_cpu_baseline(mw, w13_bits, w2_bits, x_bits, budget_s: float):
         blas = 1
     return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(blas), "kind": "oracle",
             "sample": (f"intermediate dimension {i_s} of {I} (all {E} experts, H {H}), T = {list(mw.tokens)}: "
-                       f"the fp64 layer; {dt:.1f} s; numpy elementwise on 1 thread, BLAS on {blas}")}
+                       f"the fp64 layer; {dt:.1f} s; numpy elementwise on 1 thread, BLAS on {blas}"),
+            **host_info()}
 
 
 def moe_active_bytes(ids, E: int, H: int, I: int):
@@ -292,6 +374,10 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=3, help="rotating quantized-weight copies")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--prefill-workload", default="qwen_prefill",
+                    help="workload whose prefill GEMM is timed after the step (its largest M)")
+    ap.add_argument("--prefill-steps", type=int, default=10, help="timed prefill GEMM calls")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM timing")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -333,6 +419,7 @@ def main() -> int:
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    inputs = {f"{w.name}/W": sha256_bits(w_bits), f"{w.name}/x": sha256_bits(x_bits)}
     W = to_dev(w_bits)
     X = to_dev(x_bits)
     copies = max(1, args.copies)
@@ -459,6 +546,11 @@ def main() -> int:
     step_bytes = quant_bytes(n, k) + sum(gemm_bytes(m, n, k) for m in ms)
     value = step_bytes / (ms_per_step * 1e-3) / 1e12
 
+    prefill = None
+    if not args.no_prefill and args.prefill_workload != w.name:
+        prefill = bench_prefill(args, dev, to_dev)
+        inputs.update(prefill[2])
+
     per_op = {"quantize": {"ms": avg_ms["quantize"], **spread["quantize"],
                            "GB/s": quant_bytes(n, k) / (avg_ms["quantize"] * 1e-3) / 1e9}}
     per_op["import_checkpoint"] = {"ms": imp_ms, "GB/s": imp_bytes / (imp_ms * 1e-3) / 1e9,
@@ -485,6 +577,9 @@ def main() -> int:
         per_op[f"gemm_m{m}"] = {"ms": avg_ms[f"gemm_m{m}"], **spread[f"gemm_m{m}"],
                                 "TB/s": gemm_bytes(m, n, k) / t / 1e12,
                                 "TFLOP/s": gemm_flops(m, n, k) / t / 1e12}
+
+    if prefill is not None:
+        per_op[prefill[0]] = prefill[1]
 
     dom = max(ops, key=lambda op: avg_ms[op])
     if dom == "quantize":
@@ -523,6 +618,7 @@ def main() -> int:
                    "step": "nvfp4_refresh_inplace + nvfp4_w4a16_gemm at each M", "weight_copies": copies},
         "per_op": per_op,
         "roofline": roof,
+        "inputs_sha256": inputs,
     }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
