@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemm_kernel(const uint16_t* _
                                                                const float* __restrict__ gs_arr, int N,
                                                                uint16_t* __restrict__ y, int large_min) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kMoeMBlock * kMoeChunk * 2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int e = blockIdx.y;
   const int first = offsets[e], cnt = offsets[e + 1] - first;
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void moe_gemv_kernel(const uint16_
                                                                    uint16_t* __restrict__ y, int splitk,
                                                                    int small_min) {
   __shared__ float red[kGemvWaves][4 * R][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int e = blockIdx.y;
   const int first = offsets[e], cnt = offsets[e + 1] - first;

@@ -14,7 +14,7 @@ import oracle.nvfp4_oracle as O
 from nvfp4_w4a16_lm_amd import binding as B
 from nvfp4_w4a16_lm_amd import workloads as wl
 
-from gpu_util import DEV, check_gemm, dev_bf16, gemm_gpu, host_bits, upload_quant
+from gpu_util import DEV, check_gemm, dev_bf16, gemm_gpu, host_bits, oracle_quantize_threaded, upload_quant
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,20 @@ def test_decode_panel_rows_up_to_16(m, n, k):
     bias = wl.bias_bits(n, seed=m, sigma=0.5) if m == 12 else None
     y = gemm_gpu(x, q, bias)
     check_gemm(y, x, packed, scales, gs, bias_bits=bias, label=f"panel m={m} n={n} k={k}")
+
+
+# decode with more 512-row blocks than the GPU has compute units, so that
+# workgroups walk several blocks (N = 140000 > 256 * 512), ragged last block
+@pytest.mark.parametrize("m", [3, 24, 33, 64])
+def test_decode_more_row_blocks_than_compute_units(m):
+    n, k = 140000, 1024
+    w = wl.random_weight_bits(n, k, sigma=0.02, seed=m + 40)
+    gs = O.global_scale(O.weight_amax(w))
+    packed, scales = oracle_quantize_threaded(w, gs)
+    q = upload_quant(packed, scales, gs)
+    x = wl.random_activation_bits(m, k, seed=m + 41)
+    y = gemm_gpu(x, q)
+    check_gemm(y, x, packed, scales, gs, label=f"blocks m={m} n={n} k={k}")
 
 
 # more 256 x 256 prefill tiles than the GPU has compute units (several waves
