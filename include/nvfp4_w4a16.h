@@ -48,7 +48,8 @@ typedef enum {
   NVFP4_ERR_ALIGN = 3,  /* a pointer breaks the alignment rules above                   */
   NVFP4_ERR_ALIAS = 4,  /* an output byte range overlaps an input or another output     */
   NVFP4_ERR_LAUNCH = 5, /* HIP reported an error while enqueueing                        */
-  NVFP4_ERR_ARG = 6     /* an enumerated argument (e.g. a scale convention) is out of range */
+  NVFP4_ERR_ARG = 6,    /* an enumerated argument (e.g. a scale convention) is out of range */
+  NVFP4_ERR_SCRATCH = 7 /* the call needs more scratch than the library's static array holds */
 } nvfp4_status;
 
 /* Group size along K: one E4M3 scale per 16 consecutive weights of a row
@@ -283,6 +284,29 @@ nvfp4_status nvfp4_w4a4_gemm(const uint8_t* x_packed, const uint8_t* x_scales, c
                              int64_t M, int64_t K, const uint8_t* packed, const uint8_t* scales,
                              const float* global_scale, int64_t N, const void* bias, void* workspace, void* y,
                              void* stream);
+
+/*
+ * nvfp4_w4a4_gemm_noalloc -- nvfp4_w4a4_gemm without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Same arguments (minus `workspace`), computation, result and errors as
+ * nvfp4_w4a4_gemm.  The workspace lives in a static device array of
+ * NVFP4_W4A4_SCRATCH_BYTES bytes that the library holds on each GPU it runs
+ * on until the process ends; calls whose workspace
+ * (nvfp4_w4a4_workspace_bytes(M, K) = 2*M*K + 16 bytes, i.e. M*K <= 2097144)
+ * would not fit return NVFP4_ERR_SCRATCH and enqueue nothing.  All calls on
+ * one GPU share that array: calls that may overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  The first
+ * call on a device looks up the array's address on that device (no
+ * allocation); every call writes the whole region it reads before reading it.
+ */
+#define NVFP4_W4A4_SCRATCH_BYTES (4 << 20)
+nvfp4_status nvfp4_w4a4_gemm_noalloc(const uint8_t* x_packed, const uint8_t* x_scales,
+                                     const float* input_global_scale, int64_t M, int64_t K,
+                                     const uint8_t* packed, const uint8_t* scales, const float* global_scale,
+                                     int64_t N, const void* bias, void* y, void* stream);
 
 /*
  * Mixture of experts, W4A16 NVFP4 (vLLM modelopt.py, ModelOptNvFp4FusedMoE with

@@ -14,7 +14,7 @@ import os
 import torch
 
 LIB_NAME = "libnvfp4_w4a16.so"
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS_NAMES = {
     0: "NVFP4_OK",
@@ -24,6 +24,7 @@ STATUS_NAMES = {
     4: "NVFP4_ERR_ALIAS",
     5: "NVFP4_ERR_LAUNCH",
     6: "NVFP4_ERR_ARG",
+    7: "NVFP4_ERR_SCRATCH",
 }
 
 #: Scale conventions of nvfp4_import_checkpoint (nvfp4_scale2_convention).
@@ -39,6 +40,7 @@ EXPORTED = ("nvfp4_quantize", "nvfp4_refresh_inplace", "nvfp4_w4a16_gemm",
             "nvfp4_fill_scale_sentinel", "nvfp4_import_checkpoint",
             "nvfp4_fp8_quantize_rows", "nvfp4_fp8_gemm",
             "nvfp4_quantize_activations", "nvfp4_w4a4_workspace_bytes", "nvfp4_w4a4_gemm",
+            "nvfp4_w4a4_gemm_noalloc",
             "nvfp4_moe_gemm_workspace_bytes", "nvfp4_moe_w4a16_gemm", "nvfp4_moe_silu_and_mul",
             "nvfp4_moe_combine", "nvfp4_moe_workspace_bytes", "nvfp4_moe_w4a16_forward",
             "nvfp4_status_string", "nvfp4_last_hip_error", "nvfp4_abi_version")
@@ -94,6 +96,8 @@ def load_library() -> ctypes.CDLL:
     lib.nvfp4_w4a4_workspace_bytes.restype = i64
     lib.nvfp4_w4a4_gemm.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, vp, vp]
     lib.nvfp4_w4a4_gemm.restype = ctypes.c_int
+    lib.nvfp4_w4a4_gemm_noalloc.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i64, vp, vp, vp]
+    lib.nvfp4_w4a4_gemm_noalloc.restype = ctypes.c_int
     lib.nvfp4_moe_gemm_workspace_bytes.argtypes = [i64, i64]
     lib.nvfp4_moe_gemm_workspace_bytes.restype = i64
     lib.nvfp4_moe_w4a16_gemm.argtypes = [vp, i64, i64, vp, i64, i64, vp, vp, vp, i64, i64, vp, vp, vp, vp]
@@ -373,6 +377,38 @@ def nvfp4_w4a4_gemm(x_packed: torch.Tensor, x_scales: torch.Tensor, input_global
            lib.nvfp4_w4a4_gemm(_ptr(x_packed), _ptr(x_scales), _ptr(input_global_scale), m, k, _ptr(packed),
                                _ptr(scales), _ptr(global_scale), n, _ptr(bias), _ptr(workspace), _ptr(out),
                                _stream_of(packed, stream)))
+    return out
+
+
+#: Bytes of the static scratch nvfp4_w4a4_gemm_noalloc uses (NVFP4_W4A4_SCRATCH_BYTES).
+W4A4_SCRATCH_BYTES = 4 << 20
+
+
+def nvfp4_w4a4_gemm_noalloc(x_packed: torch.Tensor, x_scales: torch.Tensor, input_global_scale: torch.Tensor,
+                            packed: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
+                            out: torch.Tensor, bias: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_w4a4_gemm with the library's static scratch as workspace: the caller
+    passes the output buffer and nothing is allocated (M*K <= 2097144)."""
+    if x_packed.dim() != 2 or packed.dim() != 2 or x_packed.shape[1] != packed.shape[1]:
+        raise ValueError(f"x_packed {tuple(x_packed.shape)} and packed {tuple(packed.shape)} do not match")
+    m, k = x_packed.shape[0], x_packed.shape[1] * 2
+    n = packed.shape[0]
+    dev = packed.device
+    _check_out(x_packed, (m, k // 2), (torch.uint8,), dev, "x_packed")
+    _check_out(x_scales, (m, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, "x_scales")
+    _check_out(packed, (n, k // 2), (torch.uint8,), dev, "packed")
+    _check_out(scales, (n, k // 16), (torch.float8_e4m3fn, torch.uint8), dev, "scales")
+    for t, what in ((input_global_scale, "input_global_scale"), (global_scale, "global_scale")):
+        if t.numel() != 1 or t.dtype != torch.float32 or t.device != dev:
+            raise ValueError(f"{what} must be one float32 on the weight's device")
+    if bias is not None:
+        _check_out(bias, (n,), (torch.bfloat16,), dev, "bias")
+    _check_out(out, (m, n), (torch.bfloat16,), dev, "out")
+    lib = load_library()
+    _check("nvfp4_w4a4_gemm_noalloc",
+           lib.nvfp4_w4a4_gemm_noalloc(_ptr(x_packed), _ptr(x_scales), _ptr(input_global_scale), m, k,
+                                       _ptr(packed), _ptr(scales), _ptr(global_scale), n, _ptr(bias), _ptr(out),
+                                       _stream_of(packed, stream)))
     return out
 
 

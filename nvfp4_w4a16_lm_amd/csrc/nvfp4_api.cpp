@@ -65,6 +65,51 @@ nvfp4_status run_quantize(const void* W, int64_t N, int64_t K, uint8_t* packed, 
   return finish(nvfp4::launch_quantize(W, N, K, packed, scales, global_scale, (hipStream_t)stream));
 }
 
+// nvfp4_w4a4_gemm with a caller workspace, or (use_scratch) with the
+// library's static scratch; validation first, then the two launches.
+nvfp4_status run_w4a4(const uint8_t* x_packed, const uint8_t* x_scales, const float* input_global_scale, int64_t M,
+                      int64_t K, const uint8_t* packed, const uint8_t* scales, const float* global_scale, int64_t N,
+                      const void* bias, void* workspace, bool use_scratch, void* y, void* stream) {
+  if (!packed || !scales || !global_scale ||
+      (M != 0 && (!x_packed || !x_scales || !input_global_scale || (!use_scratch && !workspace) || !y)))
+    return NVFP4_ERR_NULL;
+  nvfp4_status s = check_weight_shape(N, K);
+  if (s != NVFP4_OK) return s;
+  if (M < 0 || M > kMaxPrefillM || M * K > kMaxElems || M * N > kMaxElems) return NVFP4_ERR_SHAPE;
+  const int64_t ws_bytes = 2 * M * K + 16;
+  if (use_scratch && ws_bytes > nvfp4::kW4a4ScratchBytes) return NVFP4_ERR_SCRATCH;
+  if (M == 0) return NVFP4_OK;
+  if (!aligned(x_packed, 16) || !aligned(x_scales, 4) || !aligned(input_global_scale, 4) || !aligned(packed, 16) ||
+      !aligned(scales, 4) || !aligned(global_scale, 4) || (!use_scratch && !aligned(workspace, 16)) ||
+      !aligned(y, 16) || (bias && !aligned(bias, 2)))
+    return NVFP4_ERR_ALIGN;
+  const Range ry = span(y, M * N * 2);
+  const Range ins[] = {span(x_packed, M * K / 2), span(x_scales, M * K / 16), span(input_global_scale, 4),
+                       span(packed, N * K / 2),   span(scales, N * K / 16),   span(global_scale, 4),
+                       span(bias ? bias : y, bias ? N * 2 : 0)};
+  for (const Range& r : ins)
+    if (overlap(ry, r)) return NVFP4_ERR_ALIAS;
+  if (!use_scratch) {
+    const Range rw = span(workspace, ws_bytes);
+    if (overlap(ry, rw)) return NVFP4_ERR_ALIAS;
+    for (const Range& r : ins)
+      if (overlap(rw, r)) return NVFP4_ERR_ALIAS;
+  }
+  g_last_hip_error[0] = '\0';
+  if (use_scratch) {
+    const hipError_t e = nvfp4::w4a4_scratch_address(&workspace);
+    if (e != hipSuccess) return finish(e);
+  }
+  const hipStream_t st = (hipStream_t)stream;
+  uint8_t* const xd = static_cast<uint8_t*>(workspace);
+  float* const alpha = reinterpret_cast<float*>(xd + 2 * M * K);
+  hipError_t e = nvfp4::launch_w4a4_dequant_x(x_packed, x_scales, M, K, input_global_scale, global_scale, xd,
+                                              alpha, st);
+  if (e != hipSuccess) return finish(e);
+  if (M <= nvfp4::kDecodeMaxM) return finish(nvfp4::launch_gemv(xd, M, K, packed, scales, alpha, N, bias, y, st));
+  return finish(nvfp4::launch_gemm_prefill(xd, M, K, packed, scales, alpha, N, bias, y, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,33 +230,16 @@ nvfp4_status nvfp4_w4a4_gemm(const uint8_t* x_packed, const uint8_t* x_scales, c
                              int64_t M, int64_t K, const uint8_t* packed, const uint8_t* scales,
                              const float* global_scale, int64_t N, const void* bias, void* workspace, void* y,
                              void* stream) {
-  if (!packed || !scales || !global_scale ||
-      (M != 0 && (!x_packed || !x_scales || !input_global_scale || !workspace || !y)))
-    return NVFP4_ERR_NULL;
-  nvfp4_status s = check_weight_shape(N, K);
-  if (s != NVFP4_OK) return s;
-  if (M < 0 || M > kMaxPrefillM || M * K > kMaxElems || M * N > kMaxElems) return NVFP4_ERR_SHAPE;
-  if (M == 0) return NVFP4_OK;
-  if (!aligned(x_packed, 16) || !aligned(x_scales, 4) || !aligned(input_global_scale, 4) || !aligned(packed, 16) ||
-      !aligned(scales, 4) || !aligned(global_scale, 4) || !aligned(workspace, 16) || !aligned(y, 16) ||
-      (bias && !aligned(bias, 2)))
-    return NVFP4_ERR_ALIGN;
-  const Range ry = span(y, M * N * 2), rw = span(workspace, nvfp4_w4a4_workspace_bytes(M, K));
-  const Range ins[] = {span(x_packed, M * K / 2), span(x_scales, M * K / 16), span(input_global_scale, 4),
-                       span(packed, N * K / 2),   span(scales, N * K / 16),   span(global_scale, 4),
-                       span(bias ? bias : y, bias ? N * 2 : 0)};
-  if (overlap(ry, rw)) return NVFP4_ERR_ALIAS;
-  for (const Range& r : ins)
-    if (overlap(ry, r) || overlap(rw, r)) return NVFP4_ERR_ALIAS;
-  g_last_hip_error[0] = '\0';
-  const hipStream_t st = (hipStream_t)stream;
-  uint8_t* const xd = static_cast<uint8_t*>(workspace);
-  float* const alpha = reinterpret_cast<float*>(xd + 2 * M * K);
-  hipError_t e = nvfp4::launch_w4a4_dequant_x(x_packed, x_scales, M, K, input_global_scale, global_scale, xd,
-                                              alpha, st);
-  if (e != hipSuccess) return finish(e);
-  if (M <= nvfp4::kDecodeMaxM) return finish(nvfp4::launch_gemv(xd, M, K, packed, scales, alpha, N, bias, y, st));
-  return finish(nvfp4::launch_gemm_prefill(xd, M, K, packed, scales, alpha, N, bias, y, st));
+  return run_w4a4(x_packed, x_scales, input_global_scale, M, K, packed, scales, global_scale, N, bias, workspace,
+                  false, y, stream);
+}
+
+nvfp4_status nvfp4_w4a4_gemm_noalloc(const uint8_t* x_packed, const uint8_t* x_scales,
+                                     const float* input_global_scale, int64_t M, int64_t K, const uint8_t* packed,
+                                     const uint8_t* scales, const float* global_scale, int64_t N, const void* bias,
+                                     void* y, void* stream) {
+  return run_w4a4(x_packed, x_scales, input_global_scale, M, K, packed, scales, global_scale, N, bias, nullptr,
+                  true, y, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -369,6 +397,7 @@ const char* nvfp4_status_string(int status) {
              "global_scale, flags, partition scales: 4 B; bias: 2 B)";
     case NVFP4_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case NVFP4_ERR_LAUNCH: return "HIP error while enqueueing (see nvfp4_last_hip_error)";
+    case NVFP4_ERR_SCRATCH: return "the call needs more scratch than the library's static array holds";
     case NVFP4_ERR_ARG: return "an enumerated argument is out of range";
     default: return "unknown status";
   }
@@ -376,6 +405,6 @@ const char* nvfp4_status_string(int status) {
 
 const char* nvfp4_last_hip_error(void) { return g_last_hip_error; }
 
-int nvfp4_abi_version(void) { return 3; }
+int nvfp4_abi_version(void) { return 4; }
 
 }  // extern "C"

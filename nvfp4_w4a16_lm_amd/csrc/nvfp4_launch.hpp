@@ -125,6 +125,12 @@ hipError_t launch_quantize_given_scale(const void* X, int64_t M, int64_t K, cons
 hipError_t launch_w4a4_dequant_x(const uint8_t* x_packed, const uint8_t* x_scales, int64_t M, int64_t K,
                                  const float* gs_in, const float* gs_w, void* xd, float* alpha,
                                  hipStream_t stream);
+// Static scratch of the no-allocation W4A4 call: its size (the largest
+// workspace it serves, 2 M K + 16 bytes) and its device address on the
+// current device (looked up once per device).
+constexpr int64_t kW4a4ScratchBytes = (int64_t)4 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t w4a4_scratch_address(void** out);
 hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_t K, const uint8_t* wq,
                            const float* ws, int64_t N, const void* bias, void* y, hipStream_t stream);
 

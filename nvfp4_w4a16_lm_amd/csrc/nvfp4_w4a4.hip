@@ -22,6 +22,7 @@
 //   block): 8 bf16 values code * scale, one 16-byte store; the first thread
 //   also writes alpha = fl32(gs_in * gs_w) after the values.
 #include <algorithm>
+#include <mutex>
 
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
@@ -40,6 +41,33 @@ __global__ __launch_bounds__(256) void w4a4_dequant_x_kernel(const uint32_t* __r
   if (i >= nwords) return;
   const float s = NVFP4_E4M3_TO_F32((uint32_t)scales[i >> 1], 0);
   xd[i] = dequant8(packed[i], s);
+}
+
+// Scratch of nvfp4_w4a4_gemm_noalloc: the workspace of nvfp4_w4a4_gemm
+// (dequantized activations, then alpha) in static device memory, for callers
+// that cannot allocate.  Each device holds its own copy until the process
+// ends.  In host code `scratch` only names the symbol: its device address on
+// the current device comes from hipGetSymbolAddress, looked up once per
+// device and cached; kernels receive that address.
+static __device__ __align__(256) uint8_t scratch[kW4a4ScratchBytes];
+
+hipError_t w4a4_scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_w4a4_dequant_x(const uint8_t* x_packed, const uint8_t* x_scales, int64_t M, int64_t K,

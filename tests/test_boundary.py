@@ -18,7 +18,7 @@ from nvfp4_w4a16_lm_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4_w4a16.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_ARG = 0, 1, 2, 3, 4, 6
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_ARG, ERR_SCRATCH = 0, 1, 2, 3, 4, 6, 7
 
 # Fake, well-separated, 256-byte aligned addresses: only compared, never touched.
 W, P, S, G, X, Y, B = (0x10000000 * (i + 1) for i in range(7))
@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.nvfp4_abi_version() == binding.ABI_VERSION
-    for st in range(7):
+    for st in range(8):
         assert lib.nvfp4_status_string(st).decode()
     assert lib.nvfp4_status_string(99).decode() == "unknown status"
     assert lib.nvfp4_last_hip_error().decode() == ""
@@ -183,6 +183,21 @@ def test_w4a4_validation(lib):
     assert call(ws=Y + 64) == ERR_ALIAS
     assert call(ws=P - 1024) == ERR_ALIAS
     assert call(y=X + 256) == ERR_ALIAS
+    # the no-allocation variant: same checks without a workspace, plus the size of its static scratch
+    gn = lib.nvfp4_w4a4_gemm_noalloc
+
+    def call_n(**kw):
+        a = {**args, **kw}
+        return gn(a["xp"], a["xs"], a["gi"], a["m"], a["k"], a["p"], a["s"], a["g"], a["n"], a["b"], a["y"], None)
+    assert call_n(y=0) == ERR_NULL
+    assert call_n(m=0, xp=0, xs=0, gi=0, y=0) == OK
+    assert call_n(k=40) == ERR_SHAPE
+    assert call_n(y=Y + 8) == ERR_ALIGN
+    assert call_n(y=X + 256) == ERR_ALIAS
+    # 2 M K + 16 bytes must fit the 4 MiB array: M K <= 2097144
+    assert lib.nvfp4_w4a4_workspace_bytes(2048, 1024) > binding.W4A4_SCRATCH_BYTES
+    assert call_n(m=2048, k=1024) == ERR_SCRATCH
+    assert call_n(m=2048, k=1024, y=X + 256) == ERR_SCRATCH      # size is checked before aliasing
 
 
 def test_binding_import_rejects_unknown_convention():
