@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint8_t* __restrict
   constexpr int kXPieces = (BM * 4 + 255) / 256;                // 16-byte X pieces per thread per slab
   __shared__ __attribute__((aligned(16))) uint8_t wl[2][kFp8Rows * kFp8Slab];
   __shared__ __attribute__((aligned(16))) uint8_t xl[2][BM * kFp8Slab];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * kFp8Rows, m0 = blockIdx.y * BM;
   const int nslabs = (K + kFp8Slab - 1) / kFp8Slab;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
                                                              const uint16_t* __restrict__ bias,
                                                              uint16_t* __restrict__ y, int m_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFp8PLds];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int mt = blockIdx.x % m_tiles, nt = blockIdx.x / m_tiles;
   const int n0 = nt * kFp8PT, m0 = mt * kFp8PT;

@@ -13,6 +13,7 @@ namespace nvfp4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -118,6 +119,15 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float e2, f16x2 mu) {
   const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 2) * mu;
   const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, e2, 3) * mu;
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// E4M3 block scale s (fp32) -> the mantissa mu = s / 2^e as an f16 pair, for
+// dequant8_f16(w, s, mu): the fp4 converter takes s itself as its scale and
+// applies only its exponent (0 for s = 0, whose codes then convert to 0).
+__device__ __forceinline__ f16x2 scale_mantissa_f16(float s) {
+  const float m = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  const f16x2 mu = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(m, m));
+  return s == 0.0f ? f16x2{(_Float16)0.0f, (_Float16)0.0f} : mu;
 }
 
 }  // namespace nvfp4

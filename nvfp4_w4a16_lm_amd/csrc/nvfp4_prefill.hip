@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_small_kernel(const uint16_t*
                                                                  uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t Ws[kBN * kLdsPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kBM * kLdsPitch];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
   const int r = lane & 15, g = lane >> 4;
@@ -126,7 +126,6 @@ __global__ __launch_bounds__(256) void gemm_prefill_small_kernel(const uint16_t*
     }
 }
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kPT = 256;             // tile rows (n) and columns (m)
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
                                                                   const uint16_t* __restrict__ bias,
                                                                   uint16_t* __restrict__ y, int m_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mt = blockIdx.x % m_tiles, nt = blockIdx.x / m_tiles;
   const int n0 = nt * kPT, m0 = mt * kPT;
   const int nsteps = K / kPK;

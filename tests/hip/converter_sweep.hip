@@ -9,7 +9,8 @@
 // q = w * r.
 //
 // Dequantize (E2M1 code * E4M3 block scale): the fp32 route (dequant8), the
-// f16 route (split_scale + dequant8_f16) and the power-of-two bf16 converter
+// f16 route in both forms (split_scale or the scale itself +
+// scale_mantissa_f16, then dequant8_f16) and the power-of-two bf16 converter
 // the dot kernel feeds to v_dot2_f32_bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,11 +41,13 @@ __global__ void e2m1_sweep_kernel(uint32_t first, uint32_t sign, int64_t nwords,
 // pair of 16-bit results for the byte's two codes:
 //   f32route: bf16 bits of code * s (dequant8)
 //   f16route: f16 bits of code * s (split_scale + dequant8_f16)
+//   f16s:     f16 bits of code * s (the scale itself as the converter's scale,
+//             scale_mantissa_f16 + dequant8_f16)
 //   pow2bf16: bf16 bits of code * e2, e2 = 2^e of s (v_cvt_scalef32_pk_bf16_fp4)
 // and per scale byte e2 (fp32) and mu (f16 bits) of split_scale.
 __global__ void dequant_table_kernel(uint32_t* __restrict__ f32route, uint32_t* __restrict__ f16route,
-                                     uint32_t* __restrict__ pow2bf16, float* __restrict__ e2_out,
-                                     uint16_t* __restrict__ mu_out) {
+                                     uint32_t* __restrict__ f16s, uint32_t* __restrict__ pow2bf16,
+                                     float* __restrict__ e2_out, uint16_t* __restrict__ mu_out) {
   const uint32_t sbyte = blockIdx.x, cbyte = threadIdx.x;
   const float s = NVFP4_E4M3_TO_F32(sbyte, 0);
   float e2;
@@ -55,11 +58,14 @@ __global__ void dequant_table_kernel(uint32_t* __restrict__ f32route, uint32_t* 
   const uint32_t w = cbyte | ((cbyte ^ 0x5Au) << 8) | ((cbyte ^ 0xA5u) << 16) | ((cbyte ^ 0xFFu) << 24);
   const bf16x8 a = dequant8(w, s);
   const f16x8 h = dequant8_f16(w, e2, mu);
+  const f16x8 hs = dequant8_f16(w, s, scale_mantissa_f16(s));
   const bf16x2 p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, e2, 0);
   const int o = (int)(sbyte * 256 + cbyte);
   f32route[o] = __builtin_bit_cast(u32x4, a)[0];
   const f16x2 h01 = {h[0], h[1]};
   f16route[o] = __builtin_bit_cast(uint32_t, h01);
+  const f16x2 hs01 = {hs[0], hs[1]};
+  f16s[o] = __builtin_bit_cast(uint32_t, hs01);
   pow2bf16[o] = __builtin_bit_cast(uint32_t, p);
   if (cbyte == 0) {
     e2_out[sbyte] = e2;
@@ -84,10 +90,10 @@ int nvfp4_test_e2m1_sweep(uint32_t first, uint32_t sign_bit, int64_t count, uint
 }
 
 // outputs sized 127 * 256 (words) and 127 (e2, mu)
-int nvfp4_test_dequant_table(uint32_t* f32route, uint32_t* f16route, uint32_t* pow2bf16, float* e2, uint16_t* mu,
-                             void* stream) {
-  if (!f32route || !f16route || !pow2bf16 || !e2 || !mu) return -1;
-  hipLaunchKernelGGL(dequant_table_kernel, dim3(127), dim3(256), 0, (hipStream_t)stream, f32route, f16route,
+int nvfp4_test_dequant_table(uint32_t* f32route, uint32_t* f16route, uint32_t* f16s, uint32_t* pow2bf16, float* e2,
+                             uint16_t* mu, void* stream) {
+  if (!f32route || !f16route || !f16s || !pow2bf16 || !e2 || !mu) return -1;
+  hipLaunchKernelGGL(dequant_table_kernel, dim3(127), dim3(256), 0, (hipStream_t)stream, f32route, f16route, f16s,
                      pow2bf16, e2, mu);
   return (int)hipGetLastError();
 }

@@ -10,7 +10,7 @@ produce (about 9, from a subnormal block scale) -- and compares each code with
 the oracle's element step (``element_codes`` with scale 1, so q passes
 through unchanged).
 
-Dequantize: the fp32, f16 and power-of-two bf16 routes the GEMM kernels use,
+Dequantize: the fp32, f16 (both forms) and power-of-two bf16 routes the GEMM kernels use,
 for all 256 code bytes under all 127 finite E4M3 scale bytes, against the
 oracle's exact values of code * scale.
 """
@@ -40,7 +40,7 @@ def lib():
     lib = ctypes.CDLL(LIB)
     lib.nvfp4_test_e2m1_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p]
-    lib.nvfp4_test_dequant_table.argtypes = [ctypes.c_void_p] * 6
+    lib.nvfp4_test_dequant_table.argtypes = [ctypes.c_void_p] * 7
     return lib
 
 
@@ -91,11 +91,12 @@ def test_dequant_routes_exact_for_all_codes_and_scales(lib):
     stream = torch.cuda.current_stream().cuda_stream
     f32r = torch.empty(127 * 256, dtype=torch.int32, device="cuda")
     f16r = torch.empty_like(f32r)
+    f16s = torch.empty_like(f32r)
     p2r = torch.empty_like(f32r)
     e2 = torch.empty(127, dtype=torch.float32, device="cuda")
     mu = torch.empty(127, dtype=torch.int16, device="cuda")
-    rc = lib.nvfp4_test_dequant_table(f32r.data_ptr(), f16r.data_ptr(), p2r.data_ptr(), e2.data_ptr(),
-                                      mu.data_ptr(), stream)
+    rc = lib.nvfp4_test_dequant_table(f32r.data_ptr(), f16r.data_ptr(), f16s.data_ptr(), p2r.data_ptr(),
+                                      e2.data_ptr(), mu.data_ptr(), stream)
     assert rc == 0
     torch.cuda.synchronize()
     sbytes = np.arange(127, dtype=np.uint8)
@@ -115,6 +116,7 @@ def test_dequant_routes_exact_for_all_codes_and_scales(lib):
     got16 = halves(f16r, "f16")
     assert np.array_equal(got32, want), "fp32-route (bf16) dequantization differs from code * scale"
     assert np.array_equal(got16, want), "f16-route dequantization differs from code * scale"
+    assert np.array_equal(halves(f16s, "f16"), want), "f16 route with the scale as the converter's scale differs"
     # the power-of-two converter: code * e2 exactly, and e2 * mu == s
     e2h = e2.cpu().numpy().astype(np.float64)
     muh = mu.cpu().numpy().view(np.float16).astype(np.float64)
