@@ -785,82 +785,51 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// gemv_ring_kernel<MS>: 3 <= M <= MS activation rows (MS = 16, 32 or 64),
-// K % 1024 == 0.  Each workgroup of 8 wavefronts owns 512 weight rows, each
-// wavefront 64 of them, with the accumulators of all its rows in registers.
+// gemv_ring_kernel<MT, R>: 3 <= M <= 16 MT activation rows, K % 1024 == 0.
 //
-// Memory.  The weights land in registers, not LDS, so that each wavefront
-// keeps two 256-k chunks of its rows in flight (16 KiB; 128 KiB per compute
-// unit) while it computes a third:
+// The weights land in registers, not LDS, so that each wavefront keeps two
+// 256-k chunks of its R 16-row tiles in flight (R = 4: 16 KiB per wavefront,
+// 128 KiB per compute unit) while it computes a third:
 //  * weight loads take whole 128-byte lines, 8 lanes per row segment
-//    (lane l: row 8 j + l / 8 of a 16-row group, bytes 16 (l % 8) of the
-//    chunk), nontemporal, through a buffer resource over the wavefront's rows
-//    (rows past N lie outside it and read as zero; they are never stored);
-//  * each chunk is moved into the MFMA operand layout through the wavefront's
-//    own 8 KiB of LDS (16-byte pieces XOR-swizzled by row, no barrier);
+//    (lane l: row 8 j + l / 8, bytes 16 (l % 8) of the chunk), nontemporal;
+//  * each chunk is moved into the 16x16x32 operand layout through the
+//    wavefront's own 8 KiB of LDS (two 16-byte writes and two 16-byte reads
+//    per lane and tile; 16-byte pieces XOR-swizzled by row, no barrier);
 //  * block scales arrive 4 chunks at a time, one 16-byte load per lane and
-//    16-row group (lane (r, g) = (l % 16, l / 16): row r, the 16 scales of
-//    chunk 4 q + g), written once into the wavefront's 4 KiB scale region;
-//  * loads complete in issue order, so every wait is an exact vmcnt.
-//
-// Arithmetic (f16 route).  A block scale s = 2^e * mu (mu in [1, 2), 3
-// fraction bits): v_cvt_scalef32_pk_f16_fp4 takes s itself as its scale
-// operand, applies only its exponent, and gives code * 2^e exactly in f16;
-// one v_pk_mul_f16 applies mu (code * s has at most 6 significant bits within
-// [2^-10, 2688]: exact).  Two VALU instructions per weight pair.  The
-// activations are converted to f16 by the workgroup, one panel of 32 KiB at a
-// time (pk columns of MS rows, double buffered, one barrier per panel): each
-// wavefront copies its 4 KiB share of the next panel (bf16) straight into
-// the next buffer while the current one is used, and converts it in place at
-// the end of the panel.  Row m of a panel is stored as x * 2^-p_m, where p_m
-// is a running exponent: the smallest value, never below -126, for which
-// every element of the row seen so far has |x * 2^-p_m| < 2^15 (the element
-// that set it lands in [2^14, 2^15)).  Each wavefront converts whole row
-// segments, so the row maximum needs no exchange; the exponents go to a small
-// LDS table, and when a row's exponent grows every wavefront multiplies that
-// row's accumulators by 2^(p_old - p_new) (exact unless it underflows, which
-// drops only contributions below 2^-149 * 2^p_new).  An activation with
-// |x| >= 2^-28 max|x_m| converts exactly; smaller ones move by at most
-// max(2^-39 max|x_m|, 2^-151) (p_m never exceeds the exponent the whole row's
-// maximum would give).  f16 MFMA with fp32 accumulation; the epilogue
-// multiplies by 2^p_m and the global scale.
-//
-// Scales: lane (r, g) holds chunk 4 q + g's 16 scales of row r from the
-// group's load; chunk j's are written into one of two 1 KiB slots (chunks
-// 0 and 2 share one, 1 and 3 the other) just before chunk j is used, chunks 2
-// and 3 together before the next group's load reuses the registers.
-//
-// MFMA shape: MS = 16: v_mfma_f32_16x16x32_f16 on four 16-row weight tiles
-// (lane (r, g) = (l % 16, l / 16) holds row r, k = 64 g .. 64 g + 63 of a
-// chunk); MS = 32 / 64: v_mfma_f32_32x32x16_f16 on two 32-row tiles and
-// MS / 32 activation tiles (lane (r, h) = (l % 32, l / 32) holds row r,
-// k = 128 h .. 128 h + 127 of a chunk; MFMA step s takes k = 128 h + 8 s).
-// The activation fragments of each MFMA step serve all weight tiles.
+//    tile (lane (r, g) = (l % 16, l / 16): row r, the 16 scales of chunk 4q + g),
+//    written once into the wavefront's 4 KiB scale region; each chunk, lane
+//    (r, g) reads the 4 scales of its own k range (4 bytes per tile);
+//  * x is copied into LDS in panels of 32 KiB (pk columns of 16 MT rows; rows
+//    past M repeat row M - 1) by direct-to-LDS loads, double buffered: panel
+//    P + 1 is copied while panel P is used, with one workgroup barrier per
+//    panel;
+//  * loads complete in issue order, so every wait is an exact vmcnt: the
+//    batch of chunk c (the 4 scale loads first when c % 4 == 0, then 2 R
+//    weight loads) is issued two chunks ahead, and the x copies of panel P + 1
+//    right after the barrier that starts panel P.
+// Arithmetic as in gemv_panel_kernel: fp32-route dequantization (exact
+// code * scale in bf16) and bf16 MFMA with fp32 accumulation; each MFMA step's
+// activation fragments serve all R tiles.  Rows past N are read from row N - 1
+// and never stored.
 // ---------------------------------------------------------------------------
-constexpr int kRingRowsWG = 512;                        // weight rows per workgroup
-constexpr int kRingPanelBytes = 32 * 1024;              // one f16 activation panel
+constexpr int kRingNW = 8;                              // wavefronts per workgroup (two per SIMD)
 
-template <int MS>
+template <int MT>
 struct RingGeom {
-  static constexpr int pk = kRingPanelBytes / (2 * MS);          // panel columns: 1024, 512, 256
-  static constexpr int pchunks = pk / kChunk;                    // chunks per panel: 4, 2, 1
-  static constexpr int row_bytes = 2 * pk;                       // 2048, 1024, 512
+  static constexpr int rows = 16 * MT;                           // x rows in a panel (M rounded up)
+  static constexpr int pk = MT == 1 ? 1024 : MT == 2 ? 512 : 256;   // panel columns
+  static constexpr int pchunks = pk / kChunk;                    // chunks per panel: 4, 2, 1, 1
+  static constexpr int xbytes = rows * pk * 2;                   // one panel buffer (<= 32 KiB)
+  static constexpr int xcopies = xbytes / 1024 / kRingNW;        // 1 KiB copies per wavefront per panel
+  static_assert(xbytes % (1024 * kRingNW) == 0, "panel copies must split evenly over the wavefronts");
   static_assert(4 % pchunks == 0, "panel boundaries must fall on the unrolled 4-chunk steps");
 };
 
-// s_waitcnt vmcnt(N) alone, N chosen at run time among the even values below
-// 64 (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left open)
+// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt bits [3:0] and [15:14])
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
-}
-template <int... I>
-__device__ __forceinline__ void wait_vmcnt_even(int n, std::integer_sequence<int, I...>) {
-  ((n == 2 * I ? (wait_vmcnt<2 * I>(), 0) : 0), ...);
-}
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  wait_vmcnt_even(min(n, 62) & ~1, std::make_integer_sequence<int, 32>{});
 }
 
 // Workgroup barrier without the implicit wait for outstanding loads that
@@ -870,69 +839,49 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 template <int V>
 using Ic = std::integral_constant<int, V>;
 
-__device__ __forceinline__ f32x16 mfma32x32x16_f16(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// largest exponent field of 8 bf16 magnitudes in a 16-byte vector
-__device__ __forceinline__ uint32_t vec_max_mag(u32x4 v) {
-  const uint32_t m = pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
-                                pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu));
-  return max(m & 0xFFFFu, m >> 16);
-}
-
-template <int MS, int NW>
-__global__ __launch_bounds__(64 * NW) void gemv_ring_kernel(const uint16_t* __restrict__ x, int M, int K,
+template <int MT, int R>
+__global__ __launch_bounds__(64 * kRingNW) void gemv_ring_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                const uint8_t* __restrict__ packed,
                                                                const uint8_t* __restrict__ scales,
                                                                const float* __restrict__ gs_ptr, int N,
                                                                const uint16_t* __restrict__ bias,
                                                                uint16_t* __restrict__ y) {
-  using G = RingGeom<MS>;
-  constexpr int kRows = kRingRowsWG / NW;               // weight rows per wavefront: 64 or 32
-  constexpr int G16 = kRows / 16;                       // 16-row groups per wavefront
-  constexpr int XL = kRingPanelBytes / 1024 / NW;       // 1 KiB panel loads per wavefront: 4 or 2
-  constexpr bool kBig = MS > 16;                        // 32x32x16 MFMA
-  constexpr int MT = kBig ? MS / 32 : 1;                // activation tiles
-  constexpr int WT = kBig ? G16 / 2 : G16;              // weight tiles (32 or 16 rows)
-  constexpr int kBatchW = 2 * G16;                      // weight loads per chunk (kRows x 128 B)
-  static_assert(WT >= 1 && XL >= 2, "launch shape");
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kRingPanelBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t wt[NW][G16 * 2048];   // [16-row group][row][128 B]
-  __shared__ __attribute__((aligned(16))) uint8_t st[NW][G16 * 512];    // [group][slot][row][16 scales]
-  __shared__ int ptab[2][MS];                                          // running exponents, by panel buffer
+  using G = RingGeom<MT>;
+  constexpr int NW = kRingNW;
+  constexpr int kBatchW = 2 * R;                        // weight loads per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::xbytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wt[NW][R * 2048];
+  __shared__ __attribute__((aligned(16))) uint8_t st[NW][R * 1024];   // [tile][chunk of group][row][16 scales]
   // the wavefront index is uniform: keeping it in a scalar register keeps the
   // buffer resources below scalar (a per-lane resource costs a loop per load)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
   const int nchunks = K / kChunk;
   const int npanels = K / G::pk;
   const int64_t prow = K >> 1, srow = K >> 4;
   const float gs = *gs_ptr;
-  constexpr int kRowsWG = kRingRowsWG;
+  constexpr int kRowsWG = NW * R * 16;
   const int nblocks = (N + kRowsWG - 1) / kRowsWG;
   // transpose write: load lane l holds row 8 j + l / 8, piece l % 8 (slot piece ^ (row & 7))
   const int wwr = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+  // operand read: row r, pieces 2 g and 2 g + 1
+  const int wrd0 = 128 * r + 16 * ((2 * g) ^ (r & 7)), wrd1 = 128 * r + 16 * ((2 * g + 1) ^ (r & 7));
   uint8_t* const wmine = wt[wave];
   uint8_t* const smine = st[wave];
+  const int srd = 16 * r + 4 * g;                       // this lane's 4 scales of a chunk: + 1024 t + 256 (c % 4)
+
+  // byte offsets within this wavefront's rows: weight load lane (row 8 j + l / 8 of a
+  // tile, piece l % 8), scale load lane (row r, 16 bytes of chunk 4 q + g)
   const int wlane = (lane >> 3) * (int)prow + 16 * (lane & 7);
-  const int slane = (lane & 15) * (int)srow + 16 * (lane >> 4);
-  // this wavefront's share of a panel: KiB XL wave + i (i < XL), whole row segments
-  int xrow[XL], xsrc[XL];                               // panel row and element offset of each load
-#pragma unroll
-  for (int i = 0; i < XL; ++i) {
-    const int off = 1024 * (XL * wave + i) + 16 * lane;
-    xrow[i] = off / G::row_bytes;
-    const int slot = (off % G::row_bytes) >> 4;
-    xsrc[i] = 8 * (slot ^ (xrow[i] & 7));
-  }
-  // MFMA columns (activation rows) of this lane
-  const int mcol = kBig ? (lane & 31) : (lane & 15);
+  const int slane = r * (int)srow + 16 * g;
 
   for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
-    const int n_wave = blk * kRowsWG + wave * kRows;
+    const int n_wave = blk * kRowsWG + wave * (R * 16);
+    // buffer resources over this wavefront's rows: rows past N lie outside
+    // them and read as zero (their outputs are never stored)
     // (every field passes readfirstlane: a resource the compiler cannot prove
     // uniform is wrapped in a loop around each load)
-    const int rows_in = __builtin_amdgcn_readfirstlane(max(0, min(kRows, N - n_wave)));
+    const int rows_in = __builtin_amdgcn_readfirstlane(max(0, min(R * 16, N - n_wave)));
     const int row0 = __builtin_amdgcn_readfirstlane(min(n_wave, N - 1));
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(packed + (int64_t)row0 * prow), (short)0, __builtin_amdgcn_readfirstlane(rows_in * (int)prow),
@@ -941,108 +890,38 @@ __global__ __launch_bounds__(64 * NW) void gemv_ring_kernel(const uint16_t* __re
         (void*)(scales + (int64_t)row0 * srow), (short)0, __builtin_amdgcn_readfirstlane(rows_in * (int)srow),
         0x00020000);
 
-    u32x4 wr[2][G16][2];                                // the ring: chunks c (slot c % 2) and c + 1
-    u32x4 sraw[G16];                                    // scales of the next 4-chunk group, as loaded
-    int pown[XL];                                       // running exponents of the rows this lane converts
-    int pcol[MT];                                       // exponents of this lane's MFMA columns
+    u32x4 wr[2][R][2];                                  // the ring: chunks c (slot c % 2) and c + 1
+    u32x4 sraw[R];                                      // scales of the next 4-chunk group, as loaded
+    f32x4 acc[R][MT];
 #pragma unroll
-    for (int i = 0; i < XL; ++i) pown[i] = -126;
+    for (int t = 0; t < R; ++t)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) pcol[mt] = -126;
-    f32x4 acc4[kBig ? 1 : WT];
-    f32x16 acc16[kBig ? WT : 1][MT];
-    if constexpr (kBig) {
-#pragma unroll
-      for (int t = 0; t < WT; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc16[t][mt][v] = 0.0f;
-    } else {
-#pragma unroll
-      for (int t = 0; t < WT; ++t) acc4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // batch(c) into ring slot SLOT: the scales of group c / 4 first (c % 4 == 0), then the weights
+    // batch(c) into ring slot `slot`: the scales of group c / 4 first (c % 4 == 0), then the weights
     auto issue = [&](int c, auto SLOT, auto GROUP_START) {
       if constexpr (decltype(GROUP_START)::value) {
 #pragma unroll
-        for (int t = 0; t < G16; ++t)
+        for (int t = 0; t < R; ++t)
           sraw[t] = __builtin_amdgcn_raw_buffer_load_b128(sres, slane + 16 * t * (int)srow, 64 * (c >> 2), 0);
       }
 #pragma unroll
-      for (int t = 0; t < G16; ++t)
+      for (int t = 0; t < R; ++t)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           wr[decltype(SLOT)::value][t][j] = __builtin_amdgcn_raw_buffer_load_b128(
               wres, wlane + (16 * t + 8 * j) * (int)prow, 128 * c, kCachePolicyNT);
     };
-    auto batch_size = [&](int c) { return c < nchunks ? kBatchW + ((c & 3) == 0 ? G16 : 0) : 0; };
-    // this wavefront's 4 KiB of panel P, as bf16, straight into buffer P % 2
-    // (lane l of load i fills bytes 1 KiB (4 wave + i) + 16 l)
+    // x panel P into buffer P % 2: copy i of this wavefront fills panel bytes [1 KiB (i NW + wave), + 1 KiB)
     auto x_copy = [&](int P) {
-#pragma unroll
-      for (int i = 0; i < XL; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(x + (int64_t)min(xrow[i], M - 1) * K + P * G::pk + xsrc[i]),
-                                         (lds_ptr_t)(xs[P & 1] + 1024 * (XL * wave + i)), 16, 0, 0);
-    };
-    // this wavefront's share of panel P, in place: row maxima -> running
-    // exponents (published in ptab[P % 2]) -> f16 (x * 2^-p_m)
-    auto x_convert = [&](int P) {
       uint8_t* const buf = xs[P & 1];
-      u32x4 v[XL];
-      uint32_t mx[XL];
 #pragma unroll
-      for (int i = 0; i < XL; ++i) {
-        v[i] = *reinterpret_cast<const u32x4*>(buf + 1024 * (XL * wave + i) + 16 * lane);
-        mx[i] = vec_max_mag(v[i]);
-      }
-      if constexpr (G::row_bytes == 2048) {             // a row is two loads (i = 2 k, 2 k + 1)
-#pragma unroll
-        for (int i = 0; i < XL; i += 2) mx[i] = mx[i + 1] = max(mx[i], mx[i + 1]);
-      }
-      constexpr int span = G::row_bytes >= 1024 ? 64 : 32;   // lanes of one row within a load
-      int* const tab = ptab[P & 1];
-#pragma unroll
-      for (int i = 0; i < XL; ++i) {
-#pragma unroll
-        for (int o = 1; o < span; o <<= 1) mx[i] = max(mx[i], (uint32_t)__shfl_xor((int)mx[i], o, 64));
-        const int q = (mx[i] == 0u) ? -126 : max(-126, (int)(mx[i] >> 7) - 141);   // biased exponent - 127 - 14
-        pown[i] = max(pown[i], q);
-        if ((lane & (span - 1)) == 0) tab[xrow[i]] = pown[i];
-        const float down = __uint_as_float((uint32_t)(127 - pown[i]) << 23);
-        u32x4 h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f16x2 pair = {(_Float16)(bf16_lo(v[i][e]) * down), (_Float16)(bf16_hi(v[i][e]) * down)};
-          h[e] = __builtin_bit_cast(uint32_t, pair);
-        }
-        *reinterpret_cast<u32x4*>(buf + 1024 * (XL * wave + i) + 16 * lane) = h;
-      }
-    };
-    // after the barrier of panel P: this lane's columns' exponents; the
-    // accumulators of rows whose exponent grew are rescaled
-    auto take_exponents = [&](int P) {
-      const int* const tab = ptab[P & 1];
-      float f[MT];
-      bool grew = false;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int pn = tab[min(kBig ? 32 * mt + mcol : mcol, MS - 1)];
-        f[mt] = __builtin_ldexpf(1.0f, pcol[mt] - pn);
-        grew |= pn != pcol[mt];
-        pcol[mt] = pn;
-      }
-      if (__ballot(grew) != 0) {
-        if constexpr (kBig) {
-#pragma unroll
-          for (int t = 0; t < WT; ++t)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc16[t][mt] *= f[mt];
-        } else {
-#pragma unroll
-          for (int t = 0; t < WT; ++t) acc4[t] *= f[0];
-        }
+      for (int i = 0; i < G::xcopies; ++i) {
+        const int off = 1024 * (i * NW + wave) + 16 * lane;
+        const int m = off / (2 * G::pk), slot = (off % (2 * G::pk)) >> 4;
+        const int piece = slot ^ (m & 7);
+        __builtin_amdgcn_global_load_lds((const void*)(x + (int64_t)min(m, M - 1) * K + P * G::pk + 8 * piece),
+                                         (lds_ptr_t)(buf + 1024 * (i * NW + wave)), 16, 0, 0);
       }
     };
 
@@ -1051,116 +930,65 @@ __global__ __launch_bounds__(64 * NW) void gemv_ring_kernel(const uint16_t* __re
       constexpr int u = decltype(U_)::value;
       constexpr int cc = u % G::pchunks;                 // chunk within its panel
       const int P = c / G::pchunks;
-      const bool x_next = P + 1 < npanels;               // this panel converts the next one
-      // wait for batch(c) (at a panel start: and this wavefront's share of panel P
-      // was converted at the end of the previous step); everything issued after
-      // it may stay in flight
-      wait_vmcnt_dyn(batch_size(c + 1) + ((G::pchunks >= 2 && cc == 1 && x_next) ? XL : 0));
+      // wait for batch(c) (and, at a panel start, this wavefront's copies of panel P):
+      // everything issued after it may stay in flight
+      constexpr int nnext = kBatchW + (((u + 1) & 3) == 0 ? R : 0);   // size of batch(c + 1)
+      const bool has_next = c + 1 < nchunks;
+      const bool x_after = (G::pchunks >= 2 && cc == 1) && (P + 1 < npanels);   // copies of P + 1 follow batch(c)
+      if (has_next) {
+        if (x_after) wait_vmcnt<nnext + G::xcopies>();
+        else wait_vmcnt<nnext>();
+      } else {
+        wait_vmcnt<0>();
+      }
       if constexpr (cc == 0) {
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);          // this wavefront's panel writes are done
         ring_barrier();                                   // panel P is complete; panel P - 1 is no longer read
-        take_exponents(P);
-        if (x_next) x_copy(P + 1);
+        if (P + 1 < npanels) x_copy(P + 1);
       }
       // chunk c: registers -> this wavefront's LDS, then refill the slot with batch(c + 2)
 #pragma unroll
-      for (int t = 0; t < G16; ++t)
+      for (int t = 0; t < R; ++t)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           *reinterpret_cast<u32x4*>(wmine + 2048 * t + 1024 * j + wwr) = wr[u & 1][t][j];
-      // this chunk's scales (chunks 2 and 3 together, before batch(c + 2) reuses sraw)
-      {
-        const int g = lane >> 4;
-        const bool mine = (u == 0 && g == 0) || (u == 1 && g == 1) || (u == 2 && g >= 2);
-        if (mine) {
-#pragma unroll
-          for (int t = 0; t < G16; ++t) *reinterpret_cast<u32x4*>(smine + 512 * t + 256 * (g & 1) + 16 * (lane & 15)) = sraw[t];
-        }
-      }
       if (c + 2 < nchunks) issue(c + 2, Ic<u & 1>{}, std::integral_constant<bool, ((u + 2) & 3) == 0>{});
-      const uint8_t* const xb = xs[P & 1];
-      if constexpr (!kBig) {
-        const int r = lane & 15, g = lane >> 4;
-        uint32_t sw[WT];
+      if constexpr (u == 0) {
+        // the group's scales as loaded (lane (r, g): row r, chunk g) into this wavefront's region
 #pragma unroll
-        for (int t = 0; t < WT; ++t) sw[t] = *reinterpret_cast<const uint32_t*>(smine + 512 * t + 256 * (u & 1) + 16 * r + 4 * g);
-        const uint8_t* const xr = xb + r * G::row_bytes + 16 * (32 * cc + 8 * g);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 wd[WT];
-#pragma unroll
-          for (int t = 0; t < WT; ++t)
-            wd[t] = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + 128 * r + 16 * ((2 * g + hh) ^ (r & 7)));
-#pragma unroll
-          for (int s = 4 * hh; s < 4 * hh + 4; ++s) {
-            const f16x8 bx = *reinterpret_cast<const f16x8*>(xr + 16 * (s ^ (r & 7)));
-#pragma unroll
-            for (int t = 0; t < WT; ++t) {
-              const float sv = (s >> 1) == 0 ? NVFP4_E4M3_TO_F32(sw[t], 0) : (s >> 1) == 1 ? NVFP4_E4M3_TO_F32(sw[t], 1)
-                             : (s >> 1) == 2 ? NVFP4_E4M3_TO_F32(sw[t], 2) : NVFP4_E4M3_TO_F32(sw[t], 3);
-              const f16x8 a = dequant8_f16(wd[t][s & 3], sv, scale_mantissa_f16(sv));
-              acc4[t] = mfma16x16x32_f16(a, bx, acc4[t]);
-            }
-          }
-        }
-      } else {
-        const int r = lane & 31, h = lane >> 5;
-        // scales: row r of 32-row tile t is row r % 16 of 16-row group 2 t + r / 16; its 8 blocks
-        // of k = 128 h .. + 127 are bytes 8 h .. 8 h + 7 of the chunk's 16
-        uint2 sw[WT];
-#pragma unroll
-        for (int t = 0; t < WT; ++t)
-          sw[t] = *reinterpret_cast<const uint2*>(smine + 512 * (2 * t + (r >> 4)) + 256 * (u & 1) + 16 * (r & 15) + 8 * h);
-        const int rr = r & 15;
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {                  // 4 MFMA steps per 16-byte piece of codes
-          u32x4 wd[WT];
-#pragma unroll
-          for (int t = 0; t < WT; ++t)
-            wd[t] = *reinterpret_cast<const u32x4*>(wmine + 2048 * (2 * t + (r >> 4)) + 128 * rr +
-                                                    16 * ((4 * h + qd) ^ (rr & 7)));
-#pragma unroll
-          for (int s = 4 * qd; s < 4 * qd + 4; ++s) {
-            f16x8 bx[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const int m = 32 * mt + r;
-              bx[mt] = *reinterpret_cast<const f16x8*>(xb + m * G::row_bytes + 16 * ((32 * cc + 16 * h + s) ^ (m & 7)));
-            }
-#pragma unroll
-            for (int t = 0; t < WT; ++t) {
-              const uint32_t swd = (s >> 3) ? sw[t].y : sw[t].x;
-              const int sb = (s >> 1) & 3;
-              const float sv = sb == 0 ? NVFP4_E4M3_TO_F32(swd, 0) : sb == 1 ? NVFP4_E4M3_TO_F32(swd, 1)
-                             : sb == 2 ? NVFP4_E4M3_TO_F32(swd, 2) : NVFP4_E4M3_TO_F32(swd, 3);
-              const f16x8 a = dequant8_f16(wd[t][s & 3], sv, scale_mantissa_f16(sv));
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt) acc16[t][mt] = mfma32x32x16_f16(a, bx[mt], acc16[t][mt]);
-            }
-          }
-        }
+        for (int t = 0; t < R; ++t) *reinterpret_cast<u32x4*>(smine + 1024 * t + 16 * lane) = sraw[t];
       }
-      // end of panel P: the next panel's share has landed (it went out right after this
-      // panel's barrier, before batch(c_P + 2) .. batch(c + 2)); convert it
-      if constexpr (cc == G::pchunks - 1) {
-        if (x_next) {
-          int after = 0;
+      uint32_t sw[R];
 #pragma unroll
-          for (int d = 0; d < G::pchunks; ++d) after += batch_size(c - cc + 2 + d);
-          wait_vmcnt_dyn(after);
-          x_convert(P + 1);
+      for (int t = 0; t < R; ++t) sw[t] = *reinterpret_cast<const uint32_t*>(smine + 1024 * t + 256 * u + srd);
+      const uint8_t* const xb = xs[P & 1] + r * (2 * G::pk) + 16 * (32 * cc + 8 * g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {                       // the two 16-byte halves of each tile's operand
+        u32x4 wd[R];
+#pragma unroll
+        for (int t = 0; t < R; ++t) wd[t] = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + (h ? wrd1 : wrd0));
+#pragma unroll
+        for (int s = 4 * h; s < 4 * h + 4; ++s) {
+          bf16x8 bx[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            bx[mt] = *reinterpret_cast<const bf16x8*>(xb + mt * 16 * (2 * G::pk) + 16 * (s ^ (r & 7)));
+#pragma unroll
+          for (int t = 0; t < R; ++t) {
+            const float sv = (s >> 1) == 0 ? NVFP4_E4M3_TO_F32(sw[t], 0) : (s >> 1) == 1 ? NVFP4_E4M3_TO_F32(sw[t], 1)
+                           : (s >> 1) == 2 ? NVFP4_E4M3_TO_F32(sw[t], 2) : NVFP4_E4M3_TO_F32(sw[t], 3);
+            const bf16x8 a = dequant8(wd[t][s & 3], sv);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[mt], acc[t][mt]);
+          }
+          // keep later steps' operand reads from being hoisted here (register pressure at MT = 4)
+          if constexpr (MT >= 4) __builtin_amdgcn_sched_barrier(0);
         }
       }
     };
 
-    // prologue: panel 0's copy, then the first two batches, go out; panel 0
-    // is converted once its copy has landed (its exponents are taken after
-    // the first barrier)
     x_copy(0);
     issue(0, Ic<0>{}, std::true_type{});
     issue(1, Ic<1>{}, std::false_type{});
-    wait_vmcnt<2 * kBatchW + G16>();
-    x_convert(0);
     for (int c = 0; c < nchunks; c += 4) {
       step(c, Ic<0>{});
       step(c + 1, Ic<1>{});
@@ -1168,56 +996,26 @@ __global__ __launch_bounds__(64 * NW) void gemv_ring_kernel(const uint16_t* __re
       step(c + 3, Ic<3>{});
     }
 
-    // epilogue: y = acc * 2^p_m * gs (+ bias)
-    if constexpr (kBig) {
-      const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int n0 = n_wave + 16 * t + 4 * g;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int m = 32 * mt + r;
+        const int m = 16 * mt + r;
         if (m >= M) continue;
-        const float up = __uint_as_float((uint32_t)(127 + pcol[mt]) << 23);
         uint16_t* yrow = y + (int64_t)m * N;
+        if ((N & 3) == 0 && n0 + 3 < N) {
+          const uint32_t lo = out_bf16(acc[t][mt][0], gs, bias, n0) | (out_bf16(acc[t][mt][1], gs, bias, n0 + 1) << 16);
+          const uint32_t hi = out_bf16(acc[t][mt][2], gs, bias, n0 + 2) | (out_bf16(acc[t][mt][3], gs, bias, n0 + 3) << 16);
+          *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
+        } else {
 #pragma unroll
-        for (int t = 0; t < WT; ++t)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n0 = n_wave + 32 * t + 8 * q + 4 * h;
-            f32x4 v4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) v4[v] = acc16[t][mt][4 * q + v] * up;
-            if ((N & 3) == 0 && n0 + 3 < N) {
-              const uint32_t lo = out_bf16(v4[0], gs, bias, n0) | (out_bf16(v4[1], gs, bias, n0 + 1) << 16);
-              const uint32_t hi = out_bf16(v4[2], gs, bias, n0 + 2) | (out_bf16(v4[3], gs, bias, n0 + 3) << 16);
-              *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
-            } else {
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(v4[v], gs, bias, n0 + v);
-            }
-          }
-      }
-    } else {
-      const int r = lane & 15, g = lane >> 4;
-      if (r < M) {
-        const float up = __uint_as_float((uint32_t)(127 + pcol[0]) << 23);
-        uint16_t* yrow = y + (int64_t)r * N;
-#pragma unroll
-        for (int t = 0; t < WT; ++t) {
-          const int n0 = n_wave + 16 * t + 4 * g;
-          const f32x4 v4 = acc4[t] * up;
-          if ((N & 3) == 0 && n0 + 3 < N) {
-            const uint32_t lo = out_bf16(v4[0], gs, bias, n0) | (out_bf16(v4[1], gs, bias, n0 + 1) << 16);
-            const uint32_t hi = out_bf16(v4[2], gs, bias, n0 + 2) | (out_bf16(v4[3], gs, bias, n0 + 3) << 16);
-            *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
-          } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(v4[v], gs, bias, n0 + v);
-          }
+          for (int v = 0; v < 4; ++v)
+            if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[t][mt][v], gs, bias, n0 + v);
         }
       }
     }
-    __syncthreads();                                    // the panel buffers are reused by the next block
+    __syncthreads();                                    // the x buffers are reused by the next block
   }
 }
 
@@ -1489,14 +1287,14 @@ hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int
 #undef NVFP4_MOE_PANEL
 }
 
-template <int MS, int NW>
+template <int MT, int R>
 static hipError_t ring_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  const void* fn = (const void*)gemv_ring_kernel<MS, NW>;
-  const int nblocks = (N + kRingRowsWG - 1) / kRingRowsWG;
+  const void* fn = (const void*)gemv_ring_kernel<MT, R>;
+  const int nblocks = (N + kRingNW * R * 16 - 1) / (kRingNW * R * 16);
   const int dev = current_device();
-  const dim3 grid(std::min(nblocks, device_cus(dev) * blocks_per_cu(fn, dev, 64 * NW, 0)));
-  return launch_kernel(fn, grid, dim3(64 * NW), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
+  const dim3 grid(std::min(nblocks, device_cus(dev) * blocks_per_cu(fn, dev, 64 * kRingNW, 0)));
+  return launch_kernel(fn, grid, dim3(64 * kRingNW), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
                        (const uint16_t*)bias, (uint16_t*)y);
 }
 
@@ -1525,9 +1323,12 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     default: break;
   }
   if (K % 1024 == 0) {
-    if (M <= 16) return ring_launch<16, 16>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    if (M <= 32) return ring_launch<32, 8>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    return ring_launch<64, 8>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    switch ((M + 15) / 16) {
+      case 1: return ring_launch<1, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+      case 2: return ring_launch<2, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+      case 3: return ring_launch<3, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+      default: return ring_launch<4, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    }
   }
   if (K % 512 == 0) {
     switch ((M + 15) / 16) {
