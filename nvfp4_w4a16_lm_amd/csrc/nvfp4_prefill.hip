@@ -14,6 +14,8 @@
 // k-group l / 16; accumulator v of lane l holds D[4 (l / 16) + v][l % 16].
 // 32x32x16 (main kernel): lane l holds row/column l % 32 and 8 k of half
 // l / 32; accumulator v holds D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+#include <type_traits>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -224,9 +226,12 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
   // scale copies: wavefront w fills rows 64 w + l, 4 bytes each
   const uint8_t* ssrc = scales + (int64_t)min(n0 + 64 * wave + lane, N - 1) * (K >> 4);
 
-  // copy d (0..10) of step st into its ring buffer; steps past the last re-read the last
-  auto copy_one = [&](int st, int d) __attribute__((always_inline)) {
-    uint8_t* const buf = lds + (st % kDRing) * kDBuf;
+  // The ring buffer of step st is st % 3; callers pass it as `ph`, a
+  // compile-time constant in the unrolled loop below, so that every LDS
+  // address is a base plus an immediate offset.
+  // copy d (0..10) of step st into ring buffer ph; steps past the last re-read the last
+  auto copy_one = [&](int st, int ph, int d) __attribute__((always_inline)) {
+    uint8_t* const buf = lds + ph * kDBuf;
     const int sc = min(st, nsteps - 1);
     if (d < 8) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_ptr_t)(buf + kDX + (4 * d + wave) * 1024), 16, xdv[d],
@@ -245,13 +250,13 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
   // activation fragment of column tile j (rows 32 j + r) for sub-step u
   const int wrow = 64 * wave + r;
   const int xt = (r & 7) ^ ((r >> 3) & 1);
-  auto read_code = [&](int st, int i, DCodes& d) __attribute__((always_inline)) {
-    const uint8_t* const buf = lds + (st % kDRing) * kDBuf;
+  auto read_code = [&](int ph, int i, DCodes& d) __attribute__((always_inline)) {
+    const uint8_t* const buf = lds + ph * kDBuf;
     d.code[i] = *reinterpret_cast<const u32x4*>(buf + kDW + (wrow + 32 * i) * 32 + 16 * h);
     d.sc[i] = *reinterpret_cast<const uint16_t*>(buf + kDS + (wrow + 32 * i) * 4 + 2 * h);
   };
-  auto read_x = [&](int st, int j, int u) __attribute__((always_inline)) {
-    const uint8_t* const buf = lds + (st % kDRing) * kDBuf;
+  auto read_x = [&](int ph, int j, int u) __attribute__((always_inline)) {
+    const uint8_t* const buf = lds + ph * kDBuf;
     return *reinterpret_cast<const bf16x8*>(buf + kDX + (32 * j + r) * 128 + 16 * ((4 * h + u) ^ xt));
   };
 
@@ -281,7 +286,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 
   // One step st with its codes in cc; fills nc with the codes of step st + 1.
   // MFMA q of a sub-step is tile (i, j) = (q >> 3, q & 7).
-  auto kstep = [&](int st, const DCodes& cc, DCodes& nc) __attribute__((always_inline)) {
+  auto kstep = [&](int st, auto PH, const DCodes& cc, DCodes& nc) __attribute__((always_inline)) {
+    constexpr int ph = decltype(PH)::value, ph1 = (ph + 1) % kDRing;   // ring buffers of steps st, st + 1
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       u32x4(&wcur)[2] = (u & 1) ? wb : wa;
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         acc[q >> 3][q & 7] = mfma32x32x16(__builtin_bit_cast(bf16x8, wcur[q >> 3]), xcur[q & 7], acc[q >> 3][q & 7]);
-        if (q < 8) xnext[q] = read_x(st, q, u + 1);
+        if (q < 8) xnext[q] = read_x(ph, q, u + 1);
         if (q & 1) dequant_pair(cc, q >> 3, u + 1, (q >> 1) & 3, wnext[q >> 3]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -303,9 +309,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       acc[q >> 3][q & 7] = mfma32x32x16(__builtin_bit_cast(bf16x8, wb[q >> 3]), xb[q & 7], acc[q >> 3][q & 7]);
-      if (q < 2) read_code(st + 1, q, nc);
-      if (q < 8) xa[q] = read_x(st + 1, q, 0);
-      if (q >= 2 && q < 2 + kDCopies) copy_one(st + 3, q - 2);
+      if (q < 2) read_code(ph1, q, nc);
+      if (q < 8) xa[q] = read_x(ph1, q, 0);
+      if (q >= 2 && q < 2 + kDCopies) copy_one(st + 3, ph, q - 2);
       if (q >= 8) dequant_pair(nc, (q - 8) >> 2, 0, q & 3, wa[(q - 8) >> 2]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
   // prologue: steps 0..2 in flight; step 0 landed; its codes, first
   // activation fragments and first weight fragments in registers
 #pragma unroll
-  for (int t = 0; t < 3 * kDCopies; ++t) copy_one(t / kDCopies, t % kDCopies);
+  for (int t = 0; t < 3 * kDCopies; ++t) copy_one(t / kDCopies, t / kDCopies, t % kDCopies);
   __builtin_amdgcn_s_waitcnt(kWaitVm22Lgkm0);
   dma_ring_barrier();
   DCodes ca, cb;
@@ -325,12 +331,25 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
 #pragma unroll
   for (int q = 0; q < 8; ++q) dequant_pair(ca, q >> 2, 0, q & 3, wa[q >> 2]);
 
+  // six steps per iteration: ring buffers 0, 1, 2, 0, 1, 2 and the code
+  // registers alternate, all known at compile time; then up to five more
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   int st = 0;
-  for (; st + 2 <= nsteps; st += 2) {
-    kstep(st, ca, cb);
-    kstep(st + 1, cb, ca);
+  for (; st + 6 <= nsteps; st += 6) {
+    kstep(st, I0{}, ca, cb);
+    kstep(st + 1, I1{}, cb, ca);
+    kstep(st + 2, I2{}, ca, cb);
+    kstep(st + 3, I0{}, cb, ca);
+    kstep(st + 4, I1{}, ca, cb);
+    kstep(st + 5, I2{}, cb, ca);
   }
-  if (st < nsteps) kstep(st, ca, cb);
+  if (st < nsteps) kstep(st, I0{}, ca, cb);
+  if (st + 1 < nsteps) kstep(st + 1, I1{}, cb, ca);
+  if (st + 2 < nsteps) kstep(st + 2, I2{}, ca, cb);
+  if (st + 3 < nsteps) kstep(st + 3, I0{}, cb, ca);
+  if (st + 4 < nsteps) kstep(st + 4, I1{}, ca, cb);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);            // the last (unused) copies land before LDS is reused
   __syncthreads();
 
