@@ -76,10 +76,13 @@ def test_decode_more_row_blocks_than_compute_units(m):
 
 
 # more 256 x 256 prefill tiles than the GPU has compute units (several waves
-# of workgroups), every logit checked: 3, 4 and 5 steps of 64 k per tile,
-# ragged M and N, odd N, bias
+# of workgroups), every logit checked: 2 to 6 steps of 64 k per tile, ragged
+# M and N, odd N, bias.  On a 256-CU GPU the last partial round of tiles is
+# split 2 ways (1900 x 20000, 1100 x 30001), 4 ways (1000 x 35228) and 8 ways
+# (800 x 33000) over narrower workgroups; 200 x 102400 runs unsplit.
 @pytest.mark.parametrize("m,n,k,with_bias", [(1900, 20000, 192, False), (800, 33000, 256, False),
-                                             (1100, 30001, 320, True)])
+                                             (1100, 30001, 320, True), (1000, 35228, 384, True),
+                                             (200, 102400, 128, False)])
 def test_prefill_many_tiles(m, n, k, with_bias):
     w, packed, scales, gs, q = setup(n, k, seed=m)
     x = wl.random_activation_bits(m, k, seed=n)
