@@ -57,6 +57,8 @@ def decode_kernel_name(m: int, k: int) -> str:
         return "gemv_mfma_ragged_kernel"
     if 3 <= m <= 16 and m * (2 * k + 16) + 8 * 3072 + 64 <= 160 * 1024:
         return "gemv_xres_kernel"
+    if k % 1024 == 0:
+        return "gemv_ring_kernel"
     return "gemv_panel_kernel" if k % 512 == 0 else "gemv_mfma_kernel"
 
 

@@ -73,9 +73,10 @@ __device__ __forceinline__ float wave_sum4(const float p[4], int lane) {
 
 // ---------------------------------------------------------------------------
 // gemv_dot_kernel<MR, SEG>: M = MR (1 or 2) rows of x; SEG = 16-byte segments
-// per lane per row (K <= 2048 * SEG, K % 32 == 0).  Each wavefront owns
-// rows [w * rows_per_wave, ...), processed 4 at a time with the next 4 in
-// flight; the grid holds one wavefront per resident slot.
+// per lane per row (K <= 2048 * SEG, K % 32 == 0).  The rows are dealt in
+// batches of 4: wavefront w of W takes batches w, w + W, w + 2W, ..., so at
+// any moment the GPU streams one compact band of rows (measured faster than
+// giving each wavefront one contiguous run), with the next batch in flight.
 // ---------------------------------------------------------------------------
 template <int MR, int SEG>
 __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restrict__ x, int M, int K,
@@ -83,12 +84,13 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ gs_ptr, int N,
                                                        const uint16_t* __restrict__ bias,
-                                                       uint16_t* __restrict__ y, int rows_per_wave) {
+                                                       uint16_t* __restrict__ y, int nwaves) {
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int r_begin = wid * rows_per_wave;
-  if (r_begin >= N) return;
-  const int r_end = min(N, r_begin + rows_per_wave);
+  const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r_begin = 4 * wid;
+  if (wid >= nwaves || r_begin >= N) return;
+  const int r_end = N;
+  const int rstep = 4 * nwaves;                     // rows between this wavefront's batches
   const int nseg = K >> 5;
   const int64_t prow = K >> 1, srow = K >> 4;
 
@@ -97,20 +99,23 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
   // weights the clamped loads below fetch for them contribute nothing.
   // All loads are unconditional (clamped addresses, then a select): a
   // branch around a load makes the compiler wait for it before going on.
+  // The first batch of weights is requested before x.
   u32x4 xr[MR][SEG][4];
+  auto load_x = [&]() {
 #pragma unroll
-  for (int m = 0; m < MR; ++m)
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int j = 0; j < SEG; ++j) {
-      const int seg = lane + 64 * j;
-      const bool ok = (seg < nseg) && (m < M);
-      const int64_t base = (int64_t)min(m, M - 1) * K + 32 * min(seg, nseg - 1);
+      for (int j = 0; j < SEG; ++j) {
+        const int seg = lane + 64 * j;
+        const bool ok = (seg < nseg) && (m < M);
+        const int64_t base = (int64_t)min(m, M - 1) * K + 32 * min(seg, nseg - 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(x + base + 8 * q);
-        xr[m][j][q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(x + base + 8 * q);
+          xr[m][j][q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        }
       }
-    }
+  };
   const float gs = *gs_ptr;
 
   auto load_batch = [&](int r0, u32x4 (&pk)[4][SEG], uint32_t (&sc)[4][SEG]) {
@@ -179,13 +184,14 @@ __global__ __launch_bounds__(256) void gemv_dot_kernel(const uint16_t* __restric
   u32x4 pkA[4][SEG], pkB[4][SEG];
   uint32_t scA[4][SEG], scB[4][SEG];
   load_batch(r_begin, pkA, scA);
-  for (int r0 = r_begin; r0 < r_end; r0 += 8) {
-    const bool hasB = r0 + 4 < r_end;
-    if (hasB) load_batch(r0 + 4, pkB, scB);
+  load_x();
+  for (int r0 = r_begin; r0 < r_end; r0 += 2 * rstep) {
+    const bool hasB = r0 + rstep < r_end;
+    if (hasB) load_batch(r0 + rstep, pkB, scB);
     compute_batch(r0, pkA, scA);
     if (!hasB) break;
-    if (r0 + 8 < r_end) load_batch(r0 + 8, pkA, scA);
-    compute_batch(r0 + 4, pkB, scB);
+    if (r0 + 2 * rstep < r_end) load_batch(r0 + 2 * rstep, pkA, scA);
+    compute_batch(r0 + rstep, pkB, scB);
   }
 }
 
@@ -1101,15 +1107,16 @@ static int resident_workgroups(const void* kernel) {
 template <int MR, int SEG>
 static hipError_t dot_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
                              const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  // One contiguous run of rows per resident wavefront, a multiple of 8 rows
-  // (two batches of 4), so every wavefront finishes in the same round.
+  // Batches of 4 rows dealt round-robin to the wavefronts: as many
+  // wavefronts as fit at once, trimmed so that each takes the same number of
+  // batches (within one).
   const void* fn = (const void*)gemv_dot_kernel<MR, SEG>;
-  const int waves = 4 * resident_workgroups(fn);
-  int rpw = (N + waves - 1) / waves;
-  rpw = (rpw + 7) & ~7;
-  const int used = (N + rpw - 1) / rpw;
-  return launch_kernel(fn, dim3((used + 3) / 4), dim3(256), stream, (const uint16_t*)x, M, K, packed, scales, gs,
-                       N, (const uint16_t*)bias, (uint16_t*)y, rpw);
+  const int resident = 4 * resident_workgroups(fn);
+  const int batches = (N + 3) / 4;
+  const int per_wave = (batches + resident - 1) / resident;
+  const int waves = (batches + per_wave - 1) / per_wave;
+  return launch_kernel(fn, dim3((waves + 3) / 4), dim3(256), stream, (const uint16_t*)x, M, K, packed, scales, gs,
+                       N, (const uint16_t*)bias, (uint16_t*)y, waves);
 }
 
 template <int MR>
