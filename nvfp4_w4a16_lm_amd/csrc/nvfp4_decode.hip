@@ -32,6 +32,7 @@ namespace nvfp4 {
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0) alone / lgkmcnt(0) alone
 constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
+constexpr int kWaitVm2 = 0x0F72, kWaitVm3 = 0x0F73;   // vmcnt(2) / vmcnt(3) alone
 constexpr int kCachePolicyNT = 2;   // cache-policy operand of direct-to-LDS loads: nontemporal
 constexpr int kScaleGroup = 4;      // chunks of scales per direct-to-LDS scale copy
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -372,15 +373,22 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// gemv_xres_kernel<NW>: 2 < M <= 16 with the whole activation resident in LDS
-// (M * (2K + 16) bytes; K % 256 == 0).  NW wavefronts per workgroup; x is
-// copied into LDS once, then every wavefront streams whole 16-row weight
-// tiles over all of K with no further synchronisation.  Each 256-k chunk of
-// a tile's weights (and every 4 chunks its scales) is copied by
-// direct-to-LDS loads into the wavefront's own swizzled regions, one chunk
-// ahead (across tiles too), and read in the 16x16x32 operand layout, as in
-// gemv_panel_kernel.  MFMA columns m >= M read row M - 1 of x and are never
-// stored.
+// gemv_xres_kernel<NW, kMoe, KS, kRing>: 2 < M <= 16 with the whole
+// activation resident in LDS (M * (2K + 16) bytes; K % 256 == 0).  NW
+// wavefronts per workgroup; x is copied into LDS once, then every wavefront
+// streams whole 16-row weight tiles over all of K with no further
+// synchronisation.  Each 256-k chunk of a tile's weights (and every 4 chunks
+// its scales) is copied by direct-to-LDS loads into the wavefront's own
+// swizzled regions and read in the 16x16x32 operand layout, as in
+// gemv_panel_kernel:
+//  * kRing = false: one chunk region; the next chunk's copies are issued once
+//    the current chunk has been read out of it (across tiles too);
+//  * kRing = true (K % 1024 == 0): two chunk regions; chunk i + 2's copies
+//    are issued as soon as chunk i has been read, before chunk i is
+//    computed, so a wavefront always has the next two chunks in flight (the
+//    scale words of a 4-chunk group are read into registers at its first
+//    chunk, and the next group's copy goes out two chunks ahead).
+// MFMA columns m >= M read row M - 1 of x and are never stored.
 //
 // The arithmetic is f16 MFMA with fp32 accumulation:
 //  * weights: code * s is exact in f16 (at most 6 significant bits, within
@@ -409,7 +417,7 @@ struct MoeRows {
   int mmin;
 };
 
-template <int NW, bool kMoe = false, int KS = 1>
+template <int NW, bool kMoe = false, int KS = 1, bool kRing = false>
 __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                           const uint8_t* __restrict__ packed,
                                                           const uint8_t* __restrict__ scales,
@@ -427,12 +435,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     scales += (int64_t)e * N * (K >> 4);
     gs_ptr += e;
   }
+  static_assert(!kRing || KS == 1, "the two-region pipeline is for whole tiles");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int xpitch = 2 * K + 16;                    // bytes per x row (the pad spreads rows over banks)
+  constexpr int kWBytes = kRing ? 4096 : 2048;      // per wavefront: 1 or 2 x (16 rows x 128 B) of weights
   uint8_t* const xl = lds;
-  uint8_t* const wmine = lds + M * xpitch + 2048 * wave;               // 16 rows x 128 B of weights
-  uint8_t* const smine = lds + M * xpitch + 2048 * NW + 1024 * wave;   // 16 rows x 64 B of scales
-  float* const xup = reinterpret_cast<float*>(lds + M * xpitch + 3072 * NW);   // 2^p_m
+  uint8_t* const wmine = lds + M * xpitch + kWBytes * wave;
+  uint8_t* const smine = lds + M * xpitch + kWBytes * NW + 1024 * wave;   // 16 rows x 64 B of scales
+  float* const xup = reinterpret_cast<float*>(lds + M * xpitch + (kWBytes + 1024) * NW);   // 2^p_m
   const int r = lane & 15, g = lane >> 4;
   const int nchunks = K / kChunk;
   const int64_t prow = K >> 1, srow = K >> 4;
@@ -444,12 +454,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
 
   const int ntiles = (N + 15) / 16;
   const int stride = gridDim.x * NW;
-  auto w_copy = [&](int tile, int c) {
+  // chunk c of `tile` (rows past N read row N - 1) into weight region `slot`
+  auto w_copy = [&](int tile, int c, int slot) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t row = min(16 * tile + 8 * j + (lane >> 3), N - 1);
       __builtin_amdgcn_global_load_lds((const void*)(packed + row * prow + 128 * c + 16 * wpiece),
-                                       (lds_ptr_t)(wmine + 1024 * j), 16, 0, kCachePolicyNT);
+                                       (lds_ptr_t)(wmine + 2048 * slot + 1024 * j), 16, 0, kCachePolicyNT);
     }
   };
   auto s_copy = [&](int tile, int grp) {
@@ -464,8 +475,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   // the first chunk's copies fly while x is converted
   int tile = blockIdx.x * slots + slot;
   if (tile < ntiles && ph < nchunks) {
-    w_copy(tile, ph);
-    s_copy(tile, ph / kScaleGroup);
+    if constexpr (kRing) {                          // scale group 0, chunks 0 and 1
+      s_copy(tile, 0);
+      w_copy(tile, 0, 0);
+      w_copy(tile, 1, 1);
+    } else {
+      w_copy(tile, ph, 0);
+      s_copy(tile, ph / kScaleGroup);
+    }
   }
 
   // x -> f16 rows in LDS: wavefront w handles rows w, w + NW, ...: the row's
@@ -502,7 +519,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   const uint8_t* const xrow = xl + min(r, M - 1) * xpitch + 128 * g;   // this lane's k-group, chunk 0
 
   if constexpr (KS > 1) {
-    f32x4* const red = reinterpret_cast<f32x4*>(lds + M * xpitch + 3072 * NW + 64);   // [NW][64]
+    f32x4* const red = reinterpret_cast<f32x4*>(lds + M * xpitch + (kWBytes + 1024) * NW + 64);   // [NW][64]
     const int kstride = gridDim.x * slots;
     for (int t0 = blockIdx.x * slots; t0 < ntiles; t0 += kstride) {
       tile = t0 + slot;
@@ -516,10 +533,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
           __builtin_amdgcn_s_waitcnt(kWaitLgkm0);    // the regions may now be overwritten
           const int cn = c + KS;
           if (cn < nchunks) {                         // next chunk, or the next tile's first one
-            w_copy(tile, cn);
+            w_copy(tile, cn, 0);
             if (cn / kScaleGroup != c / kScaleGroup) s_copy(tile, cn / kScaleGroup);
           } else if (tile + kstride < ntiles) {
-            w_copy(tile + kstride, ph);
+            w_copy(tile + kstride, ph, 0);
             s_copy(tile + kstride, ph / kScaleGroup);
           }
           float e2[4];
@@ -563,41 +580,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     return;
   }
 
-  for (; tile < ntiles; tile += stride) {
-    const int n_base = tile * 16;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nchunks; ++c) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this chunk's copies have landed
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wmine + wrd0);
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(wmine + wrd1);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * ((c % kScaleGroup) ^ skey));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // the regions may now be overwritten
-      if (c + 1 < nchunks) {                          // next chunk, or the next tile's first one
-        w_copy(tile, c + 1);
-        if ((c + 1) % kScaleGroup == 0) s_copy(tile, (c + 1) / kScaleGroup);
-      } else if (tile + stride < ntiles) {
-        w_copy(tile + stride, 0);
-        s_copy(tile + stride, 0);
-      }
-      float e2[4];
-      f16x2 mu[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float sb = b == 0 ? NVFP4_E4M3_TO_F32(sw, 0) : b == 1 ? NVFP4_E4M3_TO_F32(sw, 1)
-                       : b == 2 ? NVFP4_E4M3_TO_F32(sw, 2) : NVFP4_E4M3_TO_F32(sw, 3);
-        split_scale(sb, &e2[b], &mu[b]);
-      }
-      const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      const uint8_t* const xc = xrow + 2 * kChunk * c;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
-        acc = mfma16x16x32_f16(dequant8_f16(wd[s], e2[s >> 1], mu[s >> 1]), bx, acc);
-      }
-    }
+  // y row block of `tile` from its accumulators (scaled back by 2^p_m)
+  auto store_tile = [&](int t, f32x4 acc) __attribute__((always_inline)) {
     if (r < M) {
       acc *= up;
-      const int n0 = n_base + 4 * g;
+      const int n0 = t * 16 + 4 * g;
       uint16_t* yrow = y + (kMoe ? (int64_t)moe.order[first + r] : (int64_t)r) * N;
       if ((N & 3) == 0 && n0 + 3 < N) {
         const uint32_t lo = out_bf16(acc[0], gs, bias, n0) | (out_bf16(acc[1], gs, bias, n0 + 1) << 16);
@@ -609,6 +596,91 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
           if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[v], gs, bias, n0 + v);
       }
     }
+  };
+  // 8 MFMAs of one chunk: weight words w0, w1, the chunk's scale word sw, x
+  // chunk xc; even and odd MFMAs accumulate into acc[0] and acc[1] (two
+  // independent chains).  The fp4 converter takes each block scale itself
+  // (it applies the exponent) and one packed multiply the mantissa.
+  auto chunk_mfma = [&](const u32x4& w0, const u32x4& w1, uint32_t sw, const uint8_t* xc, f32x4 (&acc)[2])
+      __attribute__((always_inline)) {
+    float sb[4];
+    f16x2 mu[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sb[b] = b == 0 ? NVFP4_E4M3_TO_F32(sw, 0) : b == 1 ? NVFP4_E4M3_TO_F32(sw, 1)
+            : b == 2 ? NVFP4_E4M3_TO_F32(sw, 2) : NVFP4_E4M3_TO_F32(sw, 3);
+      mu[b] = scale_mantissa_f16(sb[b]);
+    }
+    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
+      acc[s & 1] = mfma16x16x32_f16(dequant8_f16(wd[s], sb[s >> 1], mu[s >> 1]), bx, acc[s & 1]);
+    }
+  };
+
+  if constexpr (kRing) {
+    // Chunk i of this wavefront's sequence (tile, c) lives in region i % 2 =
+    // c % 2 (nchunks is a multiple of 4).  Its copies were issued two
+    // chunks earlier, the scale group of c % 4 == 0 with those of c - 2; the
+    // copies issued after them are chunk i + 1's (2, plus the next scale
+    // group when c % 4 == 3), which may stay in flight.
+    uint32_t swg[4];
+    auto step = [&](auto P, int t, int c, f32x4 (&acc)[2]) __attribute__((always_inline)) {
+      constexpr int p = decltype(P)::value;          // c % 4
+      __builtin_amdgcn_s_waitcnt(p == 3 ? kWaitVm3 : kWaitVm2);
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wmine + 2048 * (p & 1) + wrd0);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(wmine + 2048 * (p & 1) + wrd1);
+      if (p == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) swg[b] = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * (b ^ skey));
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // region p & 1 (and the scales) may now be refilled
+      int t2 = t, c2 = c + 2;                         // chunk i + 2 (past the last: clamped rows, never read)
+      if (c2 >= nchunks) {
+        c2 -= nchunks;
+        t2 += stride;
+      }
+      w_copy(t2, c2, p & 1);
+      if (p == 2) s_copy(t2, c2 / kScaleGroup);
+      chunk_mfma(w0, w1, swg[p], xrow + 2 * kChunk * c, acc);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    for (; tile < ntiles; tile += stride) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      for (int c = 0; c < nchunks; c += 4) {
+        step(P0{}, tile, c, acc);
+        step(P1{}, tile, c + 1, acc);
+        step(P2{}, tile, c + 2, acc);
+        step(P3{}, tile, c + 3, acc);
+      }
+      store_tile(tile, acc[0] + acc[1]);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);            // the trailing copies land before the workgroup ends
+    return;
+  }
+
+  for (; tile < ntiles; tile += stride) {
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int c = 0; c < nchunks; ++c) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this chunk's copies have landed
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wmine + wrd0);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(wmine + wrd1);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * ((c % kScaleGroup) ^ skey));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // the regions may now be overwritten
+      if (c + 1 < nchunks) {                          // next chunk, or the next tile's first one
+        w_copy(tile, c + 1, 0);
+        if ((c + 1) % kScaleGroup == 0) s_copy(tile, (c + 1) / kScaleGroup);
+      } else if (tile + stride < ntiles) {
+        w_copy(tile + stride, 0, 0);
+        s_copy(tile + stride, 0);
+      }
+      chunk_mfma(w0, w1, sw, xrow + 2 * kChunk * c, acc);
+    }
+    store_tile(tile, acc[0] + acc[1]);
   }
 }
 
@@ -1146,17 +1218,18 @@ static hipError_t mfma_launch(const void* x, int M, int K, const uint8_t* packed
 // The dot kernel keeps the lane's slice of x in registers (16 * ceil(K/2048)
 // VGPRs per activation row), so it takes M = 1 up to K = 8192 and M = 2 up to
 // K = 4096; everything else goes to the MFMA kernel.
-// Dynamic LDS of gemv_xres_kernel<NW> for (M, K): x rows, NW per-wavefront
-// weight (2 KiB) and scale (1 KiB) regions, 16 row scales.
-static int64_t xres_lds_bytes(int64_t M, int64_t K, int nw) {
-  return M * (2 * K + 16) + (int64_t)nw * 3072 + 16 * sizeof(float);
+// Dynamic LDS of gemv_xres_kernel<NW, false, 1, ring> for (M, K): x rows, NW
+// per-wavefront weight (2 KiB, 4 KiB with the two-region pipeline) and scale
+// (1 KiB) regions, 16 row scales.
+static int64_t xres_lds_bytes(int64_t M, int64_t K, int nw, bool ring) {
+  return M * (2 * K + 16) + (int64_t)nw * (ring ? 5120 : 3072) + 16 * sizeof(float);
 }
 
-template <int NW>
+template <int NW, bool kRing>
 static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  const void* fn = (const void*)gemv_xres_kernel<NW>;
-  const int lds = (int)xres_lds_bytes(M, K, NW);
+  const void* fn = (const void*)gemv_xres_kernel<NW, false, 1, kRing>;
+  const int lds = (int)xres_lds_bytes(M, K, NW, kRing);
   const int dev = current_device();
   const hipError_t e = ensure_dynamic_lds(fn, dev, kXresLdsMax);
   if (e != hipSuccess) return e;
@@ -1305,11 +1378,20 @@ static hipError_t ring_launch(const void* x, int M, int K, const uint8_t* packed
                        (const uint16_t*)bias, (uint16_t*)y);
 }
 
-// 0 = the activation does not fit in LDS; else the wavefronts per workgroup
-static int xres_waves(int64_t M, int64_t K) {
+// x-resident configuration for (M, K): 10 * wavefronts + 1 with the
+// two-region pipeline (K % 1024 == 0), + 0 without; 0 to leave (M, K) to the
+// streaming kernels.  Measured on the 8B shape (K = 4096): 8 wavefronts with
+// the pipeline are fastest up to M = 8, 16 beyond; when only 8 wavefronts
+// without it fit, gemv_ring_kernel (K % 1024 == 0) is faster (M = 16: 58 vs
+// 67 us).
+static int xres_config(int64_t M, int64_t K) {
   if (M < 3 || M > 16 || K % kChunk != 0) return 0;
-  if (xres_lds_bytes(M, K, 16) <= kXresLdsMax) return 16;
-  if (xres_lds_bytes(M, K, 8) <= kXresLdsMax) return 8;
+  const bool ring = K % (4 * kChunk) == 0;
+  static constexpr int kSmall[][2] = {{8, 1}, {16, 1}, {16, 0}};
+  static constexpr int kLarge[][2] = {{16, 1}, {16, 0}, {8, 1}};
+  for (const auto& c : (M <= 8 ? kSmall : kLarge))
+    if ((c[1] == 0 || ring) && xres_lds_bytes(M, K, c[0], c[1] != 0) <= kXresLdsMax) return 10 * c[0] + c[1];
+  if (!ring && xres_lds_bytes(M, K, 8, false) <= kXresLdsMax) return 80;
   return 0;
 }
 
@@ -1324,9 +1406,11 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     if (M == 1) return dot_dispatch<1>(x, M, K, packed, scales, gs, N, bias, y, stream);
     return dot_dispatch<2>(x, M, K, packed, scales, gs, N, bias, y, stream);
   }
-  switch (xres_waves(M, K)) {
-    case 16: return xres_launch<16>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    case 8: return xres_launch<8>(x, M, K, packed, scales, gs, N, bias, y, stream);
+  switch (xres_config(M, K)) {
+    case 161: return xres_launch<16, true>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 160: return xres_launch<16, false>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 81: return xres_launch<8, true>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 80: return xres_launch<8, false>(x, M, K, packed, scales, gs, N, bias, y, stream);
     default: break;
   }
   if (K % 1024 == 0) {

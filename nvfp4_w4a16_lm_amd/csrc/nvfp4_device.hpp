@@ -123,11 +123,13 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float e2, f16x2 mu) {
 
 // E4M3 block scale s (fp32) -> the mantissa mu = s / 2^e as an f16 pair, for
 // dequant8_f16(w, s, mu): the fp4 converter takes s itself as its scale and
-// applies only its exponent (0 for s = 0, whose codes then convert to 0).
+// applies only its exponent.  mu = 1.f with f the top 10 fraction bits of s
+// (an E4M3 value has at most 3, so mu is exact).  For s = 0 the converter's
+// scale is 2^-127, every code converts to a signed f16 zero, and mu = 1
+// leaves it zero.
 __device__ __forceinline__ f16x2 scale_mantissa_f16(float s) {
-  const float m = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
-  const f16x2 mu = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(m, m));
-  return s == 0.0f ? f16x2{(_Float16)0.0f, (_Float16)0.0f} : mu;
+  const uint32_t h = 0x3C00u | ((__float_as_uint(s) >> 13) & 0x3FFu);
+  return __builtin_bit_cast(f16x2, h | (h << 16));
 }
 
 }  // namespace nvfp4
