@@ -56,9 +56,9 @@ def decode_kernel_name(m: int, k: int) -> str:
     if k % 256 != 0:
         return "gemv_mfma_ragged_kernel"
     if 3 <= m <= 16:
-        fits = lambda nw, ring: m * (2 * k + 16) + nw * (5120 if ring else 3072) + 64 <= 160 * 1024
-        ring = k % 1024 == 0
-        if (ring and (fits(8, True) or fits(16, True))) or fits(16, False) or (not ring and fits(8, False)):
+        fits = lambda nw, depth: m * (2 * k + 16) + nw * (2048 * max(depth, 1) + 1024) + 64 <= 160 * 1024
+        deep = k % 1024 == 0
+        if (deep and (fits(8, 2) or fits(16, 2))) or fits(16, 0) or (not deep and fits(8, 0)):
             return "gemv_xres_kernel"
     if k % 1024 == 0:
         return "gemv_ring_kernel"

@@ -44,6 +44,8 @@
 //   through LDS for row-contiguous 16-byte stores.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -276,8 +278,9 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
   }
   // copy instruction c (0..7) of step st: c < 4 weight rows, c >= 4 activation
   // rows; steps past the last re-read the last step (never used)
-  auto copy_one = [&](int st, int c) __attribute__((always_inline)) {
-    uint8_t* const buf = lds + (st % kFp8PRing) * kFp8PBuf;
+  // `ph` is the ring buffer st % 4, a compile-time constant in the unrolled loop
+  auto copy_one = [&](int st, int ph, int c) __attribute__((always_inline)) {
+    uint8_t* const buf = lds + ph * kFp8PBuf;
     const int64_t off = 64 * (int64_t)min(st, nsteps - 1);
     const int i = c & 3;
     if (c < 4)
@@ -306,27 +309,28 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   typedef fp8_i32x8 Frag[4];
-  auto read_frags = [&](int st, int f, Frag& a, Frag& b) __attribute__((always_inline)) {
-    const uint8_t* const wb = lds + (st % kFp8PRing) * kFp8PBuf;
+  auto read_frags = [&](int ph, int f, Frag& a, Frag& b) __attribute__((always_inline)) {
+    const uint8_t* const wb = lds + ph * kFp8PBuf;
     if (f < 4)
       a[f] = frag32(wb, 128 * wn + 32 * f + r);
     else
       b[f - 4] = frag32(wb + kFp8PStep, 128 * wm + 32 * (f - 4) + r);
   };
-  // One k step st: 16 MFMAs on the fragments (ca, cb) of step st.  Between
-  // them, the fragments of step st + 1 are read into (na, nb) and the copies
-  // of step st + 3 are issued into the buffer step st - 1 used.  Then the
-  // copies of step st + 2 are waited for (the 8 of step st + 3 stay in
-  // flight) and the barrier publishes them.
-  auto kstep = [&](int st, const Frag& ca, const Frag& cb, Frag& na, Frag& nb) __attribute__((always_inline)) {
+  // One k step st (ring buffer PH = st % 4, a compile-time constant): 16
+  // MFMAs on the fragments (ca, cb) of step st.  Between them, the fragments
+  // of step st + 1 are read into (na, nb) and the copies of step st + 3 are
+  // issued, one after every other MFMA, into the buffer step st - 1 used
+  // (its fragments were read during step st - 2).  Then the copies of step
+  // st + 2 are waited for (the 8 of step st + 3 stay in flight) and the
+  // barrier publishes them.
+  auto kstep = [&](int st, auto PH, const Frag& ca, const Frag& cb, Frag& na, Frag& nb) __attribute__((always_inline)) {
+    constexpr int ph = decltype(PH)::value;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ca[q >> 2], cb[q & 3], acc[q >> 2][q & 3], 0,
                                                                            0, 0, kFp8UnitScales, 0, kFp8UnitScales);
-      if (q < 8)
-        read_frags(st + 1, q, na, nb);
-      else
-        copy_one(st + 3, q - 8);
+      if (q < 8) read_frags((ph + 1) % kFp8PRing, q, na, nb);
+      if (q & 1) copy_one(st + 3, (ph + 3) % kFp8PRing, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);
@@ -335,18 +339,26 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
 
   // prologue: steps 0..2 in flight, then steps 0 and 1 landed and step 0's fragments read
 #pragma unroll
-  for (int c = 0; c < 24; ++c) copy_one(c >> 3, c & 7);
+  for (int c = 0; c < 24; ++c) copy_one(c >> 3, c >> 3, c & 7);
   __builtin_amdgcn_s_waitcnt(kFp8WaitVm8);
   ring_barrier();
   Frag fa, fb, ga, gb;
 #pragma unroll
   for (int f = 0; f < 8; ++f) read_frags(0, f, fa, fb);
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
   int st = 0;
-  for (; st + 2 <= nsteps; st += 2) {
-    kstep(st, fa, fb, ga, gb);
-    kstep(st + 1, ga, gb, fa, fb);
+  for (; st + 4 <= nsteps; st += 4) {
+    kstep(st, Q0{}, fa, fb, ga, gb);
+    kstep(st + 1, Q1{}, ga, gb, fa, fb);
+    kstep(st + 2, Q2{}, fa, fb, ga, gb);
+    kstep(st + 3, Q3{}, ga, gb, fa, fb);
   }
-  if (st < nsteps) kstep(st, fa, fb, ga, gb);
+  if (st < nsteps) kstep(st, Q0{}, fa, fb, ga, gb);
+  if (st + 1 < nsteps) kstep(st + 1, Q1{}, ga, gb, fa, fb);
+  if (st + 2 < nsteps) kstep(st + 2, Q2{}, fa, fb, ga, gb);
   __builtin_amdgcn_s_waitcnt(kFp8WaitVm0);           // the last (unused) copies land before LDS is reused
   __syncthreads();                                    // the ring is free for the output tile
 

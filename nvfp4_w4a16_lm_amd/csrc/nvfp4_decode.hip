@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// gemv_xres_kernel<NW, kMoe, KS, kRing>: 2 < M <= 16 with the whole
+// gemv_xres_kernel<NW, kMoe, KS, kDepth>: 2 < M <= 16 with the whole
 // activation resident in LDS (M * (2K + 16) bytes; K % 256 == 0).  NW
 // wavefronts per workgroup; x is copied into LDS once, then every wavefront
 // streams whole 16-row weight tiles over all of K with no further
@@ -381,13 +381,13 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const uint16_t* __restri
 // its scales) is copied by direct-to-LDS loads into the wavefront's own
 // swizzled regions and read in the 16x16x32 operand layout, as in
 // gemv_panel_kernel:
-//  * kRing = false: one chunk region; the next chunk's copies are issued once
+//  * kDepth = 0: one chunk region; the next chunk's copies are issued once
 //    the current chunk has been read out of it (across tiles too);
-//  * kRing = true (K % 1024 == 0): two chunk regions; chunk i + 2's copies
-//    are issued as soon as chunk i has been read, before chunk i is
-//    computed, so a wavefront always has the next two chunks in flight (the
-//    scale words of a 4-chunk group are read into registers at its first
-//    chunk, and the next group's copy goes out two chunks ahead).
+//  * kDepth = D = 2 or 3 (K % 1024 == 0): D chunk regions used in turn;
+//    chunk i + D's copies are issued as soon as chunk i has been read,
+//    before chunk i is computed, so a wavefront always has the next D chunks
+//    in flight (the scale words of a 4-chunk group are read into registers
+//    at its first chunk, and the next group's copy goes out D chunks ahead).
 // MFMA columns m >= M read row M - 1 of x and are never stored.
 //
 // The arithmetic is f16 MFMA with fp32 accumulation:
@@ -417,7 +417,7 @@ struct MoeRows {
   int mmin;
 };
 
-template <int NW, bool kMoe = false, int KS = 1, bool kRing = false>
+template <int NW, bool kMoe = false, int KS = 1, int kDepth = 0>
 __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                           const uint8_t* __restrict__ packed,
                                                           const uint8_t* __restrict__ scales,
@@ -435,10 +435,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     scales += (int64_t)e * N * (K >> 4);
     gs_ptr += e;
   }
-  static_assert(!kRing || KS == 1, "the two-region pipeline is for whole tiles");
+  static_assert(kDepth == 0 || (KS == 1 && (kDepth == 2 || kDepth == 3)), "pipeline depth 2 or 3, whole tiles");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int xpitch = 2 * K + 16;                    // bytes per x row (the pad spreads rows over banks)
-  constexpr int kWBytes = kRing ? 4096 : 2048;      // per wavefront: 1 or 2 x (16 rows x 128 B) of weights
+  constexpr int kWBytes = 2048 * (kDepth ? kDepth : 1);   // per wavefront: regions of 16 rows x 128 B of weights
   uint8_t* const xl = lds;
   uint8_t* const wmine = lds + M * xpitch + kWBytes * wave;
   uint8_t* const smine = lds + M * xpitch + kWBytes * NW + 1024 * wave;   // 16 rows x 64 B of scales
@@ -475,10 +475,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   // the first chunk's copies fly while x is converted
   int tile = blockIdx.x * slots + slot;
   if (tile < ntiles && ph < nchunks) {
-    if constexpr (kRing) {                          // scale group 0, chunks 0 and 1
+    if constexpr (kDepth > 0) {                     // scale group 0, chunks 0 .. kDepth - 1
       s_copy(tile, 0);
-      w_copy(tile, 0, 0);
-      w_copy(tile, 1, 1);
+#pragma unroll
+      for (int c = 0; c < kDepth; ++c) w_copy(tile, c, c);
     } else {
       w_copy(tile, ph, 0);
       s_copy(tile, ph / kScaleGroup);
@@ -619,30 +619,37 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     }
   };
 
-  if constexpr (kRing) {
-    // Chunk i of this wavefront's sequence (tile, c) lives in region i % 2 =
-    // c % 2 (nchunks is a multiple of 4).  Its copies were issued two
-    // chunks earlier, the scale group of c % 4 == 0 with those of c - 2; the
-    // copies issued after them are chunk i + 1's (2, plus the next scale
-    // group when c % 4 == 3), which may stay in flight.
+  if constexpr (kDepth > 0) {
+    // Chunk i of this wavefront's sequence (tile, c) lives in region i % D.
+    // Its copies were issued D chunks earlier, the scale group of a chunk
+    // with c % 4 == 0 with them (at chunk position (4 - D) % 4); the copies
+    // issued after them, 2 per chunk plus that scale copy when it falls in
+    // between, may stay in flight.
+    constexpr int D = kDepth;
     uint32_t swg[4];
+    int slot = 0;                                     // i % D
     auto step = [&](auto P, int t, int c, f32x4 (&acc)[2]) __attribute__((always_inline)) {
       constexpr int p = decltype(P)::value;          // c % 4
-      __builtin_amdgcn_s_waitcnt(p == 3 ? kWaitVm3 : kWaitVm2);
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wmine + 2048 * (p & 1) + wrd0);
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(wmine + 2048 * (p & 1) + wrd1);
+      constexpr int ps = (4 - D) % 4;                // position whose step also copies the next scale group
+      constexpr bool s_between = ((p - ps + 4) % 4) >= 1 && ((p - ps + 4) % 4) <= D - 1;
+      constexpr int vm = 2 * (D - 1) + (s_between ? 1 : 0);
+      __builtin_amdgcn_s_waitcnt((vm & 15) | 0x0F70);
+      uint8_t* const wreg = wmine + 2048 * slot;
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wreg + wrd0);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(wreg + wrd1);
       if (p == 0) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) swg[b] = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * (b ^ skey));
       }
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // region p & 1 (and the scales) may now be refilled
-      int t2 = t, c2 = c + 2;                         // chunk i + 2 (past the last: clamped rows, never read)
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // the region (and the scales) may now be refilled
+      int t2 = t, c2 = c + D;                         // chunk i + D (past the last: clamped rows, never read)
       if (c2 >= nchunks) {
         c2 -= nchunks;
         t2 += stride;
       }
-      w_copy(t2, c2, p & 1);
-      if (p == 2) s_copy(t2, c2 / kScaleGroup);
+      w_copy(t2, c2, slot);
+      if (p == ps) s_copy(t2, c2 / kScaleGroup);
+      slot = (slot + 1 == D) ? 0 : slot + 1;
       chunk_mfma(w0, w1, swg[p], xrow + 2 * kChunk * c, acc);
     };
     using P0 = std::integral_constant<int, 0>;
@@ -1218,18 +1225,18 @@ static hipError_t mfma_launch(const void* x, int M, int K, const uint8_t* packed
 // The dot kernel keeps the lane's slice of x in registers (16 * ceil(K/2048)
 // VGPRs per activation row), so it takes M = 1 up to K = 8192 and M = 2 up to
 // K = 4096; everything else goes to the MFMA kernel.
-// Dynamic LDS of gemv_xres_kernel<NW, false, 1, ring> for (M, K): x rows, NW
-// per-wavefront weight (2 KiB, 4 KiB with the two-region pipeline) and scale
+// Dynamic LDS of gemv_xres_kernel<NW, false, 1, depth> for (M, K): x rows,
+// NW per-wavefront weight (2 KiB per region: max(depth, 1) regions) and scale
 // (1 KiB) regions, 16 row scales.
-static int64_t xres_lds_bytes(int64_t M, int64_t K, int nw, bool ring) {
-  return M * (2 * K + 16) + (int64_t)nw * (ring ? 5120 : 3072) + 16 * sizeof(float);
+static int64_t xres_lds_bytes(int64_t M, int64_t K, int nw, int depth) {
+  return M * (2 * K + 16) + (int64_t)nw * (2048 * (depth ? depth : 1) + 1024) + 16 * sizeof(float);
 }
 
-template <int NW, bool kRing>
+template <int NW, int kDepth>
 static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
                               const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  const void* fn = (const void*)gemv_xres_kernel<NW, false, 1, kRing>;
-  const int lds = (int)xres_lds_bytes(M, K, NW, kRing);
+  const void* fn = (const void*)gemv_xres_kernel<NW, false, 1, kDepth>;
+  const int lds = (int)xres_lds_bytes(M, K, NW, kDepth);
   const int dev = current_device();
   const hipError_t e = ensure_dynamic_lds(fn, dev, kXresLdsMax);
   if (e != hipSuccess) return e;
@@ -1378,20 +1385,20 @@ static hipError_t ring_launch(const void* x, int M, int K, const uint8_t* packed
                        (const uint16_t*)bias, (uint16_t*)y);
 }
 
-// x-resident configuration for (M, K): 10 * wavefronts + 1 with the
-// two-region pipeline (K % 1024 == 0), + 0 without; 0 to leave (M, K) to the
-// streaming kernels.  Measured on the 8B shape (K = 4096): 8 wavefronts with
-// the pipeline are fastest up to M = 8, 16 beyond; when only 8 wavefronts
-// without it fit, gemv_ring_kernel (K % 1024 == 0) is faster (M = 16: 58 vs
-// 67 us).
+// x-resident configuration for (M, K): 10 * wavefronts + pipeline depth (2
+// or 3 regions, K % 1024 == 0; 0 for the single-region form), or 0 to leave
+// (M, K) to the streaming kernels.  Measured on the 8B shape (K = 4096): 8
+// wavefronts with two regions are fastest up to M = 8 (three regions are no
+// faster), 16 beyond; when only 8 single-region wavefronts fit,
+// gemv_ring_kernel (K % 1024 == 0) is faster (M = 16: 58 vs 67 us).
 static int xres_config(int64_t M, int64_t K) {
   if (M < 3 || M > 16 || K % kChunk != 0) return 0;
-  const bool ring = K % (4 * kChunk) == 0;
-  static constexpr int kSmall[][2] = {{8, 1}, {16, 1}, {16, 0}};
-  static constexpr int kLarge[][2] = {{16, 1}, {16, 0}, {8, 1}};
+  const bool deep = K % (4 * kChunk) == 0;
+  static constexpr int kSmall[][2] = {{8, 2}, {16, 2}, {16, 0}};
+  static constexpr int kLarge[][2] = {{16, 2}, {16, 0}, {8, 2}};
   for (const auto& c : (M <= 8 ? kSmall : kLarge))
-    if ((c[1] == 0 || ring) && xres_lds_bytes(M, K, c[0], c[1] != 0) <= kXresLdsMax) return 10 * c[0] + c[1];
-  if (!ring && xres_lds_bytes(M, K, 8, false) <= kXresLdsMax) return 80;
+    if ((c[1] == 0 || deep) && xres_lds_bytes(M, K, c[0], c[1]) <= kXresLdsMax) return 10 * c[0] + c[1];
+  if (!deep && xres_lds_bytes(M, K, 8, 0) <= kXresLdsMax) return 80;
   return 0;
 }
 
@@ -1407,10 +1414,10 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     return dot_dispatch<2>(x, M, K, packed, scales, gs, N, bias, y, stream);
   }
   switch (xres_config(M, K)) {
-    case 161: return xres_launch<16, true>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    case 160: return xres_launch<16, false>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    case 81: return xres_launch<8, true>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    case 80: return xres_launch<8, false>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 82: return xres_launch<8, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 162: return xres_launch<16, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 160: return xres_launch<16, 0>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    case 80: return xres_launch<8, 0>(x, M, K, packed, scales, gs, N, bias, y, stream);
     default: break;
   }
   if (K % 1024 == 0) {
