@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(const uint16_t* __
     const u32x4 v = *reinterpret_cast<const u32x4*>(&out[ml][8 * c]);
     uint16_t* dst = y + (int64_t)m * N + n;
     if ((N & 7) == 0 && n + 8 <= N) {
-      *reinterpret_cast<u32x4*>(dst) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));   // logits are not read back here
     } else {
       const uint16_t* hh = reinterpret_cast<const uint16_t*>(&out[ml][8 * c]);
       for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = hh[e];
