@@ -1253,14 +1253,19 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
 // gives every wavefront slot of the GPU a tile when at most min(E, P)
 // experts hold pairs, and the largest mcap (<= 16, <= P) whose activation
 // rows fit in LDS next to the weight regions (and, for KS > 1, the partial
-// tiles); the wider mcap wins, 16 wavefronts on a tie.  mcap = 0: none fits
-// or K % 256 != 0.
-static int64_t moe_xres_lds(int64_t m, int64_t K, int nw, int ks) {
-  return m * (2 * K + 16) + (int64_t)nw * 3072 + 64 + (ks > 1 ? (int64_t)nw * 1024 : 0);
+// tiles); the wider mcap wins, 16 wavefronts on a tie.  Without a K split
+// (KS = 1) and with K % 1024 == 0, the two-region pipeline (depth 2) is used
+// when the rows it can still hold cover twice the mean pair count of an
+// active expert (its larger weight regions leave room for fewer activation
+// rows; experts beyond mcap go to the panel kernel).  mcap = 0: none fits or
+// K % 256 != 0.
+static int64_t moe_xres_lds(int64_t m, int64_t K, int nw, int ks, int depth = 0) {
+  return m * (2 * K + 16) + (int64_t)nw * (2048 * (depth ? depth : 1) + 1024) + 64 +
+         (ks > 1 ? (int64_t)nw * 1024 : 0);
 }
 
 MoeXresPlan moe_xres_plan(int64_t P, int64_t E, int64_t K, int64_t N) {
-  MoeXresPlan best{0, 0, 1};
+  MoeXresPlan best{0, 0, 1, 0};
   if (K % kChunk != 0 || P < 1) return best;
   const int cus = device_cus(current_device());
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
@@ -1271,17 +1276,23 @@ MoeXresPlan moe_xres_plan(int64_t P, int64_t E, int64_t K, int64_t N) {
     while (ks < 4 && tiles * ks < (int64_t)cus * nw && nchunks >= 8 * ks) ks *= 2;
     int m = (int)std::min<int64_t>(16, P);
     while (m >= 1 && moe_xres_lds(m, K, nw, ks) > kXresLdsMax) --m;
-    if (m > best.mcap) best = MoeXresPlan{m, nw, ks};
+    if (m > best.mcap) best = MoeXresPlan{m, nw, ks, 0};
+  }
+  if (best.ks == 1 && K % (4 * kChunk) == 0) {
+    int m = best.mcap;
+    while (m >= 1 && moe_xres_lds(m, K, best.nw, 1, 2) > kXresLdsMax) --m;
+    const int64_t want = 2 * ((P + active - 1) / active);   // twice the mean pairs per active expert
+    if (m >= std::min<int64_t>(best.mcap, want)) best = MoeXresPlan{m, best.nw, 1, 2};
   }
   return best;
 }
 
-template <int NW, int KS>
+template <int NW, int KS, int D = 0>
 static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32_t* offsets, const int32_t* order,
                                   int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales, const float* gs,
                                   int E, int N, void* y, hipStream_t stream) {
-  const void* fn = (const void*)gemv_xres_kernel<NW, true, KS>;
-  const int lds = (int)moe_xres_lds(mcap, K, NW, KS);
+  const void* fn = (const void*)gemv_xres_kernel<NW, true, KS, D>;
+  const int lds = (int)moe_xres_lds(mcap, K, NW, KS, D);
   const int dev = current_device();
   const hipError_t e = ensure_dynamic_lds(fn, dev, kXresLdsMax);
   if (e != hipSuccess) return e;
@@ -1307,6 +1318,13 @@ hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int3
 #define NVFP4_MOE_XRES(NW_, KS_)                                                                              \
   return moe_xres_launch<NW_, KS_>(x, (int)row_div, (int)K, offsets, order, plan.mcap, P, packed, scales, gs, \
                                    (int)E, (int)N, y, stream)
+  if (plan.depth == 2) {
+    if (plan.nw == 16)
+      return moe_xres_launch<16, 1, 2>(x, (int)row_div, (int)K, offsets, order, plan.mcap, P, packed, scales, gs,
+                                       (int)E, (int)N, y, stream);
+    return moe_xres_launch<8, 1, 2>(x, (int)row_div, (int)K, offsets, order, plan.mcap, P, packed, scales, gs,
+                                    (int)E, (int)N, y, stream);
+  }
   if (plan.nw == 16) {
     if (plan.ks == 4) NVFP4_MOE_XRES(16, 4);
     if (plan.ks == 2) NVFP4_MOE_XRES(16, 2);

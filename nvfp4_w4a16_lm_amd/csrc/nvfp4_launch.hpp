@@ -151,6 +151,7 @@ struct MoeXresPlan {
   int mcap;   // largest pair count it takes
   int nw;     // wavefronts per workgroup
   int ks;     // wavefronts sharing one tile's K
+  int depth;  // chunk regions per wavefront (0: one, refilled after the read; 2: the two-region pipeline)
 };
 MoeXresPlan moe_xres_plan(int64_t P, int64_t E, int64_t K, int64_t N);
 hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
