@@ -628,6 +628,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     constexpr int D = kDepth;
     uint32_t swg[4];
     int slot = 0;                                     // i % D
+    // this lane's copy sources in the current tile and in the next one
+    // (rows clamped to N - 1): per chunk only a constant offset is added
+    const uint8_t* wsrc[2][2];
+    const uint8_t* ssrc[2];
+    auto set_sources = [&](int t, int which) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wsrc[which][j] = packed + (int64_t)min(16 * t + 8 * j + (lane >> 3), N - 1) * prow + 16 * wpiece;
+      ssrc[which] = scales + (int64_t)min(16 * t + (lane >> 2), N - 1) * srow;
+    };
     auto step = [&](auto P, int t, int c, f32x4 (&acc)[2]) __attribute__((always_inline)) {
       constexpr int p = decltype(P)::value;          // c % 4
       constexpr int ps = (4 - D) % 4;                // position whose step also copies the next scale group
@@ -642,13 +652,19 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
         for (int b = 0; b < 4; ++b) swg[b] = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * (b ^ skey));
       }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // the region (and the scales) may now be refilled
-      int t2 = t, c2 = c + D;                         // chunk i + D (past the last: clamped rows, never read)
+      int which = 0, c2 = c + D;                      // chunk i + D (past the last: clamped rows, never read)
       if (c2 >= nchunks) {
         c2 -= nchunks;
-        t2 += stride;
+        which = 1;
       }
-      w_copy(t2, c2, slot);
-      if (p == ps) s_copy(t2, c2 / kScaleGroup);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(wsrc[which][j] + 128 * c2),
+                                         (lds_ptr_t)(wmine + 2048 * slot + 1024 * j), 16, 0, kCachePolicyNT);
+      if (p == ps) {
+        const int64_t off = min((int64_t)16 * (kScaleGroup * (c2 / kScaleGroup) + spiece), srow - 16);
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc[which] + off), (lds_ptr_t)smine, 16, 0, 0);
+      }
       slot = (slot + 1 == D) ? 0 : slot + 1;
       chunk_mfma(w0, w1, swg[p], xrow + 2 * kChunk * c, acc);
     };
@@ -657,6 +673,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
     for (; tile < ntiles; tile += stride) {
+      set_sources(tile, 0);
+      set_sources(tile + stride, 1);
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       for (int c = 0; c < nchunks; c += 4) {
         step(P0{}, tile, c, acc);
