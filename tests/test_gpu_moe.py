@@ -65,6 +65,8 @@ def check_grouped(x_bits, row_div, ids, w, got, valid=None, label=""):
     (3, 272, 48, 7, 3),         # K % 32 == 16 (8-byte code loads), partial chunk, N < 64
     (5, 48, 300, 9, 1),         # K = 48: one partial chunk
     (2, 768, 256, 30, 2),       # K % 512 != 0: experts with 17..48 pairs take the split-K kernel
+    (8, 1024, 4096, 16, 2),     # 8 x 256 tiles fill every wavefront slot (no K split), K % 1024 == 0: the
+                                # x-resident kernel's two-region pipeline
 ])
 def test_grouped_gemm_first_layer(E, H, N, T, topk):
     w = experts(E, N, H, E * 100 + N)
