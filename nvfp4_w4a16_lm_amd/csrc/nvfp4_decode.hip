@@ -408,13 +408,16 @@ constexpr int kXresLdsMax = 160 * 1024;
 // expert e; its activation rows are the expert's pairs order[offsets[e] ..
 // offsets[e + 1]) (row p reads x[p / row_div], writes y[p]); experts with
 // fewer than mmin (at least 1) or more than mcap pairs are left to the other
-// expert kernels.  gemv_panel_kernel takes the same rows.
+// expert kernels.  gemv_panel_kernel takes the same rows.  When zero_group
+// is E (the group of pairs whose id lies outside [0, E)), the workgroups of
+// row E write zeros to those pairs' rows instead.
 struct MoeRows {
   const int32_t* offsets;
   const int32_t* order;
   int row_div;
   int mcap;
   int mmin;
+  int zero_group;   // -1: none
 };
 
 template <int NW, bool kMoe = false, int KS = 1, int kDepth = 0>
@@ -430,6 +433,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
     const int e = blockIdx.y;
     first = moe.offsets[e];
     M = moe.offsets[e + 1] - (int)first;
+    if (e == moe.zero_group) {                        // pairs with an invalid id: zero rows, this workgroup's tiles
+      const int slots = NW / KS, ntiles = (N + 15) / 16;
+      for (int t0 = blockIdx.x * slots; t0 < ntiles; t0 += gridDim.x * slots) {
+        const int n0 = 16 * t0, cols = min(16 * slots, N - n0);
+        for (int i = threadIdx.x; i < M * cols; i += 64 * NW) {
+          const int q = i / cols, c = i - q * cols;
+          y[(int64_t)moe.order[first + q] * N + n0 + c] = 0;
+        }
+      }
+      return;
+    }
     if (M < max(1, moe.mmin) || M > moe.mcap) return;
     packed += (int64_t)e * N * (K >> 1);
     scales += (int64_t)e * N * (K >> 4);
@@ -1262,12 +1276,13 @@ static hipError_t xres_launch(const void* x, int M, int K, const uint8_t* packed
   const int resident = device_cus(dev) * blocks_per_cu(fn, dev, 64 * NW, lds);
   const int grid = std::max(1, std::min((ntiles + NW - 1) / NW, resident));
   return launch_kernel_lds(fn, dim3(grid), dim3(64 * NW), lds, stream, (const uint16_t*)x, M, K, packed, scales, gs,
-                           N, (const uint16_t*)bias, (uint16_t*)y, MoeRows{});
+                           N, (const uint16_t*)bias, (uint16_t*)y, MoeRows{nullptr, nullptr, 1, 0, 0, -1});
 }
 
 // Expert layer: gemv_xres_kernel<NW, true, KS> over a (G, E) grid for the
-// experts with 1..mcap pairs.  The plan picks, for 16 and for 8 wavefronts,
-// the K split KS (1, 2 or 4, each wavefront keeping at least 4 chunks) that
+// experts with 1..mcap pairs (grid row E: the invalid ids' zero rows).  The
+// plan picks, for 16 and for 8 wavefronts, the K split KS (2 or 4 keeping at
+// least 8 chunks per wavefront, 8 keeping at least 4) that
 // gives every wavefront slot of the GPU a tile when at most min(E, P)
 // experts hold pairs, and the largest mcap (<= 16, <= P) whose activation
 // rows fit in LDS next to the weight regions (and, for KS > 1, the partial
@@ -1290,8 +1305,12 @@ MoeXresPlan moe_xres_plan(int64_t P, int64_t E, int64_t K, int64_t N) {
   const int64_t tiles = (N + 15) / 16 * active;
   const int64_t nchunks = K / kChunk;
   for (int nw : {16, 8}) {
+    // split K while the tiles leave wavefront slots empty: in 2 or 4 while
+    // each part keeps at least 8 chunks, in 8 (few active experts with long
+    // rows, e.g. the down projection of one token) while it keeps 4
     int ks = 1;
     while (ks < 4 && tiles * ks < (int64_t)cus * nw && nchunks >= 8 * ks) ks *= 2;
+    if (ks == 4 && tiles * ks < (int64_t)cus * nw && nchunks >= 32) ks = 8;
     int m = (int)std::min<int64_t>(16, P);
     while (m >= 1 && moe_xres_lds(m, K, nw, ks) > kXresLdsMax) --m;
     if (m > best.mcap) best = MoeXresPlan{m, nw, ks, 0};
@@ -1323,8 +1342,8 @@ static hipError_t moe_xres_launch(const void* x, int row_div, int K, const int32
   const int64_t fill = (2 * P > (int64_t)mcap * active ? 2 : 1) * (int64_t)cus * per_cu;
   const int ntiles = (N + 15) / 16, slots = NW / KS;
   const int64_t g = std::min<int64_t>((ntiles + slots - 1) / slots, (fill + active - 1) / active);
-  const MoeRows moe{offsets, order, row_div, mcap, 1};
-  return launch_kernel_lds(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E), dim3(64 * NW), lds, stream,
+  const MoeRows moe{offsets, order, row_div, mcap, 1, E};   // row E of the grid: the invalid ids' zero rows
+  return launch_kernel_lds(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E + 1), dim3(64 * NW), lds, stream,
                            (const uint16_t*)x, 0, K, packed, scales, gs, N, (const uint16_t*)nullptr, (uint16_t*)y,
                            moe);
 }
@@ -1344,10 +1363,12 @@ hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int3
                                     (int)E, (int)N, y, stream);
   }
   if (plan.nw == 16) {
+    if (plan.ks == 8) NVFP4_MOE_XRES(16, 8);
     if (plan.ks == 4) NVFP4_MOE_XRES(16, 4);
     if (plan.ks == 2) NVFP4_MOE_XRES(16, 2);
     NVFP4_MOE_XRES(16, 1);
   }
+  if (plan.ks == 8) NVFP4_MOE_XRES(8, 8);
   if (plan.ks == 4) NVFP4_MOE_XRES(8, 4);
   if (plan.ks == 2) NVFP4_MOE_XRES(8, 2);
   NVFP4_MOE_XRES(8, 1);
@@ -1369,7 +1390,7 @@ static hipError_t panel_launch(const void* x, int M, int K, const uint8_t* packe
   const int dev = current_device();
   const dim3 grid(std::min(nblocks, device_cus(dev) * blocks_per_cu(fn, dev, 64 * NW, 0)));
   return launch_kernel(fn, grid, dim3(64 * NW), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
-                       (const uint16_t*)bias, (uint16_t*)y, panel_columns(M, K), MoeRows{});
+                       (const uint16_t*)bias, (uint16_t*)y, panel_columns(M, K), MoeRows{nullptr, nullptr, 1, 0, 0, -1});
 }
 
 // Expert layer: gemv_panel_kernel<MT, 8, R, true> over a (G, E) grid for the
@@ -1386,7 +1407,7 @@ static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int3
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P / std::max(1, mmin)));
   const int nblocks = (N + 16 * 8 * R - 1) / (16 * 8 * R);
   const int64_t g = std::min<int64_t>(nblocks, (2 * cus * per_cu + active - 1) / active);
-  const MoeRows moe{offsets, order, row_div, mcap, mmin};
+  const MoeRows moe{offsets, order, row_div, mcap, mmin, -1};
   return launch_kernel(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E), dim3(64 * 8), stream,
                        (const uint16_t*)x, 0, K, packed, scales, gs, N, (const uint16_t*)nullptr, (uint16_t*)y,
                        panel_columns(mcap, K), moe);

@@ -18,8 +18,9 @@
 //   LDS) run the lm_head path's x-resident decode kernel (gemv_xres_kernel in
 //   nvfp4_decode.hip, over a (workgroups, E) grid with the expert's gathered
 //   rows converted to f16 in LDS and weights copied straight to LDS; when the
-//   active experts have few 16-row tiles it splits each tile's K over 2 or 4
-//   wavefronts).
+//   active experts have few 16-row tiles it splits each tile's K over 2, 4
+//   or 8 wavefronts).  Its grid has a row E more, which writes the zero rows
+//   of pairs whose id is outside [0, E).
 // With K % 512 == 0, experts with more pairs, up to 64, run the lm_head
 //   path's panel decode kernel (gemv_panel_kernel, same row gathering).
 // moe_gemv_kernel (otherwise, the other experts with at most 48 pairs): a
@@ -29,8 +30,9 @@
 //   buffers) and its activation fragments per chunk, with no barrier,
 //   dequantizes exactly (code * scale is a bf16 value) and runs bf16 MFMA
 //   (v_mfma_f32_16x16x32_bf16, 16 pairs per column tile); the partial tiles
-//   are summed through LDS in wavefront order.  It also writes the zero rows
-//   of pairs whose id is outside [0, E).
+//   are summed through LDS in wavefront order.  When the x-resident kernel
+//   does not run (K % 256 != 0, or no activation row fits in LDS), it writes
+//   the zero rows of pairs whose id is outside [0, E).
 // moe_gemm_kernel (experts with more than 64 pairs, or 48 when K % 512 !=
 //   0): a workgroup of 4 wavefronts streams 256 weight rows of one expert
 //   once per block of 64 pairs; each wavefront owns 4 tiles of 16 rows, loads
@@ -562,17 +564,23 @@ hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int3
       err = launch_moe_panel(x, row_div, K, offsets, order, std::max(mcap + 1, 33), 64, P, packed, scales, gs, E, N,
                              y, stream);
     if (err != hipSuccess) return err;
-    small_min = kMoeSmallMax;                         // the split-K kernel only writes the zero rows
+    small_min = kMoeSmallMax;                         // no expert left for the split-K kernel
     large_min = 64;
   }
-  // K split over 1, 2 or 4 wavefronts so that each streams at least 8 chunks
-  const int64_t nchunks = (K + kMoeChunk - 1) / kMoeChunk;
-  const int splitk = nchunks >= 32 ? 4 : nchunks >= 16 ? 2 : 1;
-  const int64_t wg_rows = 16 * kGemvTiles * (kGemvWaves / splitk);
-  const dim3 grid_small((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)(E + 1));
-  err = launch_kernel((const void*)moe_gemv_kernel<kGemvTiles>, grid_small, dim3(64 * kGemvWaves), stream,
-                      reinterpret_cast<const uint16_t*>(x), (int)row_div, (int)K, offsets, order, packed, scales, gs,
-                      (int)E, (int)N, reinterpret_cast<uint16_t*>(y), splitk, small_min);
+  // the split-K kernel takes experts with small_min < pairs <= 48 and the
+  // invalid ids' zero rows; the x-resident kernel, when it runs, writes those
+  // rows itself, so the split-K kernel is then launched only if an expert
+  // can fall in its class
+  if (mcap < 1 || (small_min < kMoeSmallMax && P > small_min)) {
+    // K split over 1, 2 or 4 wavefronts so that each streams at least 8 chunks
+    const int64_t nchunks = (K + kMoeChunk - 1) / kMoeChunk;
+    const int splitk = nchunks >= 32 ? 4 : nchunks >= 16 ? 2 : 1;
+    const int64_t wg_rows = 16 * kGemvTiles * (kGemvWaves / splitk);
+    const dim3 grid_small((unsigned)((N + wg_rows - 1) / wg_rows), (unsigned)(E + 1));
+    err = launch_kernel((const void*)moe_gemv_kernel<kGemvTiles>, grid_small, dim3(64 * kGemvWaves), stream,
+                        reinterpret_cast<const uint16_t*>(x), (int)row_div, (int)K, offsets, order, packed, scales,
+                        gs, (int)E, (int)N, reinterpret_cast<uint16_t*>(y), splitk, small_min);
+  }
   if (err != hipSuccess || P <= large_min) return err;   // no expert can have more pairs
   const dim3 grid((unsigned)((N + kMoeRows - 1) / kMoeRows), (unsigned)E);
   return launch_kernel((const void*)moe_gemm_kernel, grid, dim3(kMoeThreads), stream,

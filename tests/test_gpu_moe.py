@@ -89,8 +89,11 @@ def test_grouped_gemm_second_layer_reads_one_row_per_pair():
     check_grouped(a, 1, ids, w, y, label="second layer")
 
 
-def test_invalid_ids_give_zero_rows_and_are_counted():
-    E, K, N, T, topk = 4, 256, 260, 6, 2
+@pytest.mark.parametrize("K", [256, 1024, 272])
+def test_invalid_ids_give_zero_rows_and_are_counted(K):
+    """K = 256 and 1024: the x-resident kernel writes the zero rows (no split-K
+    launch); K = 272: the split-K kernel does."""
+    E, N, T, topk = 4, 260, 6, 2
     w = experts(E, N, K, 21)
     x = wl.random_activation_bits(T, K, seed=22)
     ids, _ = wl.moe_routing(T, E, topk, 23)
@@ -141,11 +144,12 @@ def test_wide_experts_take_the_512_row_panel_blocks():
     check_grouped(x, 1, ids, w, y, label="wide experts")
 
 
-@pytest.mark.parametrize("K,N,E", [(2048, 100, 3), (4096, 300, 2), (8192, 40, 2)])
+@pytest.mark.parametrize("K,N,E", [(2048, 100, 3), (4096, 300, 2), (8192, 40, 2), (14336, 4096, 8)])
 def test_few_tiles_split_k_between_wavefronts(K, N, E):
     """Experts with few rows (few 16-row tiles) and few pairs: the x-resident
-    kernel splits each tile's K between 2 or 4 wavefronts and sums their
-    partial tiles; tile rounds include slots past the last tile."""
+    kernel splits each tile's K between 2, 4 or 8 wavefronts (8 at K = 8192
+    and 14336, the second layer of one token) and sums their partial tiles;
+    tile rounds include slots past the last tile."""
     w = experts(E, N, K, 98 + K)
     ids = (np.arange(3 * E) % E).astype(np.int32)
     x = wl.random_activation_bits(ids.size, K, seed=99)
