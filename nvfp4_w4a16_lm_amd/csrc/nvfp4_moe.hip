@@ -15,7 +15,9 @@
 //   (expert, segment) cells, count, prefix-sum the cells in order, then
 //   scatter).  Pairs whose id is outside [0, E) form an extra group E.
 // Experts with 1..mcap pairs (mcap <= 16: as many activation rows as fit in
-//   LDS) run the lm_head path's x-resident decode kernel (gemv_xres_kernel in
+//   LDS; none when, with K % 512 == 0, the pairs average more than mcap / 2
+//   per active expert, so that one panel launch covers them all) run the
+//   lm_head path's x-resident decode kernel (gemv_xres_kernel in
 //   nvfp4_decode.hip, over a (workgroups, E) grid with the expert's gathered
 //   rows converted to f16 in LDS and weights copied straight to LDS; when the
 //   active experts have few 16-row tiles it splits each tile's K over 2, 4
@@ -552,7 +554,15 @@ hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int3
   // experts with 1..mcap pairs: the x-resident decode kernel; with K % 512 == 0
   // the panel decode kernel takes the rest up to 64 pairs, else the split-K
   // kernel up to 48; moe_gemm_kernel takes larger experts
-  const MoeXresPlan plan = moe_xres_plan(P, E, K, N);
+  MoeXresPlan plan = moe_xres_plan(P, E, K, N);
+  {
+    // when the pairs average more than mcap / 2 per active expert, most
+    // experts exceed mcap and the x-resident kernel would run only the few
+    // left: the panel kernel then takes every expert, one launch over all of
+    // them (moe_8x4096, 16 tokens: down projection 136 -> ~80 us)
+    const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
+    if (K % 512 == 0 && 2 * P > (int64_t)plan.mcap * active) plan.mcap = 0;
+  }
   const int mcap = plan.mcap;
   hipError_t err = launch_moe_xres(x, row_div, K, offsets, order, plan, P, packed, scales, gs, E, N, y, stream);
   if (err != hipSuccess) return err;
