@@ -759,6 +759,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
     const int e = blockIdx.y;
     first = moe.offsets[e];
     M = moe.offsets[e + 1] - (int)first;
+    if (e == moe.zero_group) {                        // pairs with an invalid id: zero rows, this workgroup's blocks
+      constexpr int kBlockRows = NW * 16 * kPanelR;
+      for (int n0 = blockIdx.x * kBlockRows; n0 < N; n0 += gridDim.x * kBlockRows) {
+        const int cols = min(kBlockRows, N - n0);
+        for (int i = threadIdx.x; i < M * cols; i += 64 * NW) {
+          const int q = i / cols, c = i - q * cols;
+          y[(int64_t)moe.order[first + q] * N + n0 + c] = 0;
+        }
+      }
+      return;
+    }
     if (M < max(1, moe.mmin) || M > moe.mcap) return;
     packed += (int64_t)e * N * (K >> 1);
     scales += (int64_t)e * N * (K >> 4);
@@ -1398,7 +1409,7 @@ static hipError_t panel_launch(const void* x, int M, int K, const uint8_t* packe
 template <int MT, int R>
 static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int32_t* offsets, const int32_t* order,
                                    int mmin, int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales,
-                                   const float* gs, int E, int N, void* y, hipStream_t stream) {
+                                   const float* gs, int E, int N, void* y, bool zero_rows, hipStream_t stream) {
   const void* fn = (const void*)gemv_panel_kernel<MT, 8, R, true>;
   const int dev = current_device();
   const int cus = device_cus(dev), per_cu = blocks_per_cu(fn, dev, 64 * 8, 0);
@@ -1407,24 +1418,26 @@ static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int3
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P / std::max(1, mmin)));
   const int nblocks = (N + 16 * 8 * R - 1) / (16 * 8 * R);
   const int64_t g = std::min<int64_t>(nblocks, (2 * cus * per_cu + active - 1) / active);
-  const MoeRows moe{offsets, order, row_div, mcap, mmin, -1};
-  return launch_kernel(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E), dim3(64 * 8), stream,
+  // with zero_rows, grid row E writes the invalid ids' zero rows
+  const MoeRows moe{offsets, order, row_div, mcap, mmin, zero_rows ? E : -1};
+  return launch_kernel(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E + (zero_rows ? 1 : 0)), dim3(64 * 8),
+                       stream,
                        (const uint16_t*)x, 0, K, packed, scales, gs, N, (const uint16_t*)nullptr, (uint16_t*)y,
                        panel_columns(mcap, K), moe);
 }
 
 hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
                             int mmin, int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales,
-                            const float* gs, int64_t E, int64_t N, void* y, hipStream_t stream) {
+                            const float* gs, int64_t E, int64_t N, void* y, bool zero_rows, hipStream_t stream) {
   if (mmin > mcap || K % 512 != 0) return hipSuccess;
   // 512 rows per workgroup (4 tiles per wavefront) when the expert has enough
   // rows to fill the GPU with such blocks, else 128 (one tile per wavefront)
   const bool wide = N >= 16384;
 #define NVFP4_MOE_PANEL(MT_, CAP_)                                                                              \
   (wide ? moe_panel_launch<MT_, 4>(x, (int)row_div, (int)K, offsets, order, mmin, CAP_, P, packed, scales, gs,   \
-                                   (int)E, (int)N, y, stream)                                                   \
+                                   (int)E, (int)N, y, zero_rows, stream)                                        \
         : moe_panel_launch<MT_, 1>(x, (int)row_div, (int)K, offsets, order, mmin, CAP_, P, packed, scales, gs,   \
-                                   (int)E, (int)N, y, stream))
+                                   (int)E, (int)N, y, zero_rows, stream))
   if (mcap <= 16) return NVFP4_MOE_PANEL(1, mcap);
   if (mcap <= 32) return NVFP4_MOE_PANEL(2, mcap);
   return NVFP4_MOE_PANEL(4, std::min(mcap, 64));

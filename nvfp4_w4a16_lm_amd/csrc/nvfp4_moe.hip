@@ -566,22 +566,25 @@ hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int3
   const int mcap = plan.mcap;
   hipError_t err = launch_moe_xres(x, row_div, K, offsets, order, plan, P, packed, scales, gs, E, N, y, stream);
   if (err != hipSuccess) return err;
+  bool zero_done = mcap >= 1;                         // the x-resident kernel writes the invalid ids' zero rows
   int small_min = mcap, large_min = kMoeSmallMax;
   if (K % 512 == 0) {
-    if (P > mcap) err = launch_moe_panel(x, row_div, K, offsets, order, mcap + 1, 32, P, packed, scales, gs, E, N, y,
-                                         stream);
+    if (P > mcap) {                                   // else the first panel kernel writes them
+      err = launch_moe_panel(x, row_div, K, offsets, order, mcap + 1, 32, P, packed, scales, gs, E, N, y, !zero_done,
+                             stream);
+      zero_done = true;
+    }
     if (err == hipSuccess && P > 32)
       err = launch_moe_panel(x, row_div, K, offsets, order, std::max(mcap + 1, 33), 64, P, packed, scales, gs, E, N,
-                             y, stream);
+                             y, false, stream);
     if (err != hipSuccess) return err;
     small_min = kMoeSmallMax;                         // no expert left for the split-K kernel
     large_min = 64;
   }
-  // the split-K kernel takes experts with small_min < pairs <= 48 and the
-  // invalid ids' zero rows; the x-resident kernel, when it runs, writes those
-  // rows itself, so the split-K kernel is then launched only if an expert
-  // can fall in its class
-  if (mcap < 1 || (small_min < kMoeSmallMax && P > small_min)) {
+  // the split-K kernel takes experts with small_min < pairs <= 48 and writes
+  // the invalid ids' zero rows; it is launched only if an expert can fall in
+  // its class or no other kernel writes those rows
+  if (!zero_done || (small_min < kMoeSmallMax && P > small_min)) {
     // K split over 1, 2 or 4 wavefronts so that each streams at least 8 chunks
     const int64_t nchunks = (K + kMoeChunk - 1) / kMoeChunk;
     const int splitk = nchunks >= 32 ? 4 : nchunks >= 16 ? 2 : 1;

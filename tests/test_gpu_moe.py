@@ -89,11 +89,13 @@ def test_grouped_gemm_second_layer_reads_one_row_per_pair():
     check_grouped(a, 1, ids, w, y, label="second layer")
 
 
-@pytest.mark.parametrize("K", [256, 1024, 272])
-def test_invalid_ids_give_zero_rows_and_are_counted(K):
-    """K = 256 and 1024: the x-resident kernel writes the zero rows (no split-K
-    launch); K = 272: the split-K kernel does."""
-    E, N, T, topk = 4, 260, 6, 2
+@pytest.mark.parametrize("K,T", [(256, 6), (1024, 6), (272, 6), (1024, 40)])
+def test_invalid_ids_give_zero_rows_and_are_counted(K, T):
+    """K = 256 and 1024 with 6 tokens: the x-resident kernel writes the zero
+    rows (no split-K launch); K = 272: the split-K kernel does; 40 tokens (20
+    pairs per expert on average): the panel kernel takes every expert and
+    writes them."""
+    E, N, topk = 4, 260, 2
     w = experts(E, N, K, 21)
     x = wl.random_activation_bits(T, K, seed=22)
     ids, _ = wl.moe_routing(T, E, topk, 23)
