@@ -774,8 +774,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
     packed += (int64_t)e * N * (K >> 1);
     scales += (int64_t)e * N * (K >> 4);
     gs_ptr += e;
-    pk = min(K, (kPanelXBytes / M / 2) / 512 * 512);  // the widest panel this expert's rows fit
+    // the widest panel that a pass over the expert's rows (at most 16 MT) fits
+    pk = min(K, (kPanelXBytes / min(M, 16 * MT) / 2) / 512 * 512);
   }
+  // expert layer: more than 16 MT pairs are taken in passes of 16 MT rows over each weight block
+  const int m_all = M;
+  const int64_t first_all = first;
   static_assert(kPanelXBytes >= 16 * MT * 512 * 2, "a panel must hold 512 columns of 16 MT rows");
   constexpr int kRows = 16 * kPanelR;                   // weight rows per wavefront
   __shared__ __attribute__((aligned(16))) uint8_t xp[kPanelXBytes];
@@ -799,7 +803,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
   uint8_t* const wmine = wl[wave];
   uint8_t* const smine = sl[wave];
 
-  for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+  for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x)
+  for (int m_pass = 0; m_pass < m_all; m_pass += 16 * MT) {
+    M = min(16 * MT, m_all - m_pass);
+    first = first_all + m_pass;
     const int n_wave = blk * (NW * kRows) + wave * kRows;
     auto w_copy = [&](int c) {
 #pragma unroll
@@ -908,7 +915,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
         }
       }
     }
-    __syncthreads();                                    // the x region is reused by the next block
+    __syncthreads();                                    // the x region is reused by the next pass or block
   }
 }
 
@@ -1423,24 +1430,24 @@ static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int3
   return launch_kernel(fn, dim3((unsigned)std::max<int64_t>(1, g), (unsigned)E + (zero_rows ? 1 : 0)), dim3(64 * 8),
                        stream,
                        (const uint16_t*)x, 0, K, packed, scales, gs, N, (const uint16_t*)nullptr, (uint16_t*)y,
-                       panel_columns(mcap, K), moe);
+                       panel_columns(std::min(mcap, 16 * MT), K), moe);
 }
 
 hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
-                            int mmin, int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales,
+                            int mmin, int mcap, int rows, int64_t P, const uint8_t* packed, const uint8_t* scales,
                             const float* gs, int64_t E, int64_t N, void* y, bool zero_rows, hipStream_t stream) {
   if (mmin > mcap || K % 512 != 0) return hipSuccess;
   // 512 rows per workgroup (4 tiles per wavefront) when the expert has enough
   // rows to fill the GPU with such blocks, else 128 (one tile per wavefront)
   const bool wide = N >= 16384;
-#define NVFP4_MOE_PANEL(MT_, CAP_)                                                                              \
-  (wide ? moe_panel_launch<MT_, 4>(x, (int)row_div, (int)K, offsets, order, mmin, CAP_, P, packed, scales, gs,   \
+#define NVFP4_MOE_PANEL(MT_)                                                                                     \
+  (wide ? moe_panel_launch<MT_, 4>(x, (int)row_div, (int)K, offsets, order, mmin, mcap, P, packed, scales, gs,   \
                                    (int)E, (int)N, y, zero_rows, stream)                                        \
-        : moe_panel_launch<MT_, 1>(x, (int)row_div, (int)K, offsets, order, mmin, CAP_, P, packed, scales, gs,   \
+        : moe_panel_launch<MT_, 1>(x, (int)row_div, (int)K, offsets, order, mmin, mcap, P, packed, scales, gs,   \
                                    (int)E, (int)N, y, zero_rows, stream))
-  if (mcap <= 16) return NVFP4_MOE_PANEL(1, mcap);
-  if (mcap <= 32) return NVFP4_MOE_PANEL(2, mcap);
-  return NVFP4_MOE_PANEL(4, std::min(mcap, 64));
+  if (rows <= 16) return NVFP4_MOE_PANEL(1);
+  if (rows <= 32) return NVFP4_MOE_PANEL(2);
+  return NVFP4_MOE_PANEL(4);
 #undef NVFP4_MOE_PANEL
 }
 

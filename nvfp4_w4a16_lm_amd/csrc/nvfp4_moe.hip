@@ -569,17 +569,29 @@ hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int3
   bool zero_done = mcap >= 1;                         // the x-resident kernel writes the invalid ids' zero rows
   int small_min = mcap, large_min = kMoeSmallMax;
   if (K % 512 == 0) {
-    if (P > mcap) {                                   // else the first panel kernel writes them
-      err = launch_moe_panel(x, row_div, K, offsets, order, mcap + 1, 32, P, packed, scales, gs, E, N, y, !zero_done,
-                             stream);
+    const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, P));
+    if (P > mcap && P <= 16 * active) {
+      // at most 16 pairs per active expert on average: one launch of the
+      // 32-row panel kernel takes every expert beyond mcap, the rare one
+      // with more than 32 pairs in several passes, instead of two more
+      // launches that would mostly find no expert in their class
+      err = launch_moe_panel(x, row_div, K, offsets, order, mcap + 1, INT32_MAX, 32, P, packed, scales, gs, E, N, y,
+                             !zero_done, stream);
       zero_done = true;
+      large_min = INT32_MAX;
+    } else {
+      if (P > mcap) {                                 // else the first panel kernel writes them
+        err = launch_moe_panel(x, row_div, K, offsets, order, mcap + 1, 32, 32, P, packed, scales, gs, E, N, y,
+                               !zero_done, stream);
+        zero_done = true;
+      }
+      if (err == hipSuccess && P > 32)
+        err = launch_moe_panel(x, row_div, K, offsets, order, std::max(mcap + 1, 33), 64, 64, P, packed, scales, gs,
+                               E, N, y, false, stream);
+      large_min = 64;
     }
-    if (err == hipSuccess && P > 32)
-      err = launch_moe_panel(x, row_div, K, offsets, order, std::max(mcap + 1, 33), 64, P, packed, scales, gs, E, N,
-                             y, false, stream);
     if (err != hipSuccess) return err;
     small_min = kMoeSmallMax;                         // no expert left for the split-K kernel
-    large_min = 64;
   }
   // the split-K kernel takes experts with small_min < pairs <= 48 and writes
   // the invalid ids' zero rows; it is launched only if an expert can fall in

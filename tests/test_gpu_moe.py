@@ -135,6 +135,23 @@ def test_expert_classes_in_one_call():
     check_grouped(x, 1, ids, w, y, label="mixed classes")
 
 
+@pytest.mark.parametrize("counts,N", [((40, 10, 12, 8, 14, 0, 20, 16), 300),
+                                      ((70, 6, 6, 6, 6, 6, 6, 6), 300),
+                                      ((40, 10, 12, 8, 14, 0, 20, 16), 16400)])
+def test_panel_passes_for_experts_beyond_32_pairs(counts, N):
+    """At most 16 pairs per active expert on average: one launch of the
+    32-row panel kernel takes every expert, those with more than 32 pairs in
+    passes of 32 rows over their weights (2 and 3 passes here)."""
+    E, K = len(counts), 512
+    w = experts(E, N, K, 101 + N)
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    ids = ids[np.random.default_rng(102).permutation(ids.size)]
+    x = wl.random_activation_bits(ids.size, K, seed=103)
+    y = B.nvfp4_moe_w4a16_gemm(dev_bf16(x), torch.from_numpy(ids).to(DEV), 1, *upload(w))
+    torch.cuda.synchronize()
+    check_grouped(x, 1, ids, w, y, label=f"panel passes {counts[0]}")
+
+
 def test_wide_experts_take_the_512_row_panel_blocks():
     """N >= 16384: experts with 17..64 pairs run the panel kernel with 512-row blocks."""
     E, K, N = 2, 512, 16400
