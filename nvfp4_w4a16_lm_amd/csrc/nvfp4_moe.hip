@@ -24,7 +24,10 @@
 //   or 8 wavefronts).  Its grid has a row E more, which writes the zero rows
 //   of pairs whose id is outside [0, E).
 // With K % 512 == 0, experts with more pairs, up to 64, run the lm_head
-//   path's panel decode kernel (gemv_panel_kernel, same row gathering).
+//   path's panel decode kernel (gemv_panel_kernel, same row gathering); when
+//   the pairs average at most 16 per active expert, one launch of its 32-row
+//   form takes every such expert, one with more than 32 pairs in passes of
+//   32 rows over its weights.
 // moe_gemv_kernel (otherwise, the other experts with at most 48 pairs): a
 //   workgroup of 4 wavefronts owns 32 to 128 weight rows of one expert and
 //   splits K between 1, 2 or 4 of its wavefronts; each streams its weights
@@ -552,7 +555,8 @@ hipError_t launch_moe_gemm(const void* x, int64_t row_div, int64_t K, const int3
   const int32_t* offsets = route_ws;
   const int32_t* order = route_ws + moe_route_offsets_words(E);
   // experts with 1..mcap pairs: the x-resident decode kernel; with K % 512 == 0
-  // the panel decode kernel takes the rest up to 64 pairs, else the split-K
+  // the panel decode kernel takes the rest (up to 64 pairs, or all of them
+  // in passes of 32 at <= 16 pairs per active expert), else the split-K
   // kernel up to 48; moe_gemm_kernel takes larger experts
   MoeXresPlan plan = moe_xres_plan(P, E, K, N);
   {
