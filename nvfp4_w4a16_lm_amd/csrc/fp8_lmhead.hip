@@ -31,17 +31,19 @@
 //   Pieces past K are zero in both operands.  Epilogue: acc * s_x[m] *
 //   s_w[n] (+ bias[n]) in float32, one rounding to bf16.
 // fp8_prefill_kernel (M > 64, K >= 64, K % 64 == 0): a 256 x 256 output tile per
-//   workgroup of 4 wavefronts (2 x 2, 128 x 128 each, v_mfma_f32_32x32x16_fp8_fp8
-//   with the accumulators of 4 x 4 MFMA tiles in registers).  K is walked in
-//   64-byte steps; both operand tiles (256 rows x 64 bytes each) arrive by
-//   direct-to-LDS copies two steps ahead into a ring of three buffers, so
-//   each step waits only for its own copies, and one barrier per step both
-//   publishes the next tile and frees the buffer the copy after it refills.
-//   Rows are 64 bytes, 16-byte piece p of row r at slot p ^ ((r >> 2) & 3).
-//   Lane (r, h) = (l % 32, l / 32) reads pieces h and h + 2 of its row of
-//   each operand; MFMA step (c, j) uses bytes 8 j .. 8 j + 7 of piece
-//   h + 2 c (the same k order for both operands).  The output tile goes
-//   through LDS for row-contiguous 16-byte stores.
+//   workgroup of 4 wavefronts (2 x 2, 128 x 128 each; 16 MFMAs of
+//   v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales per 64-k step,
+//   the f8f6f4 form being the one that runs fp8 at the doubled rate; the
+//   accumulators of the 4 x 4 tiles in registers).  K is walked in 64-byte
+//   steps; both operand tiles (256 rows x 64 bytes each) arrive by
+//   direct-to-LDS copies three steps ahead into a ring of four buffers, one
+//   copy after every other MFMA of the step before, so each step waits only
+//   for its own copies, and one barrier per step both publishes the next
+//   tile and frees the buffer the copy after it refills.  Rows are 64 bytes,
+//   16-byte piece p of row r at slot p ^ ((r >> 2) & 3).  Lane (r, h) =
+//   (l % 32, l / 32) feeds pieces 2 h and 2 h + 1 of its row of each operand
+//   (32 k) to each MFMA, the same k order for both operands.  The output
+//   tile goes through LDS for row-contiguous 16-byte stores.
 #include <algorithm>
 
 #include <type_traits>
