@@ -6,22 +6,27 @@
 // E2M1(code) * e4m3(scale) * global_scale; the global scale is applied once
 // per output in fp32.
 //
-// Two kernels, both HBM-bound by design (0.5625 B of weight per element):
+// Kernels, all streaming the weights once (0.5625 B per element), chosen by
+// launch_gemv from M and K (each is described where it is defined):
 //
-// gemv_dot_kernel (M <= 2): one wavefront streams whole rows, each lane a
-//   fixed set of 16-byte segments (32 k) of every row, so the lane's slice of
-//   x stays in registers for the kernel's lifetime.  Per 16-block the E4M3
-//   scale is split into its power of two 2^e and its mantissa mu in [1, 2):
-//   the fp4->bf16 converter applies 2^e exactly (it only uses a scale's
+// gemv_dot_kernel (M <= 2, K % 32 == 0; K <= 8192 at M = 1, 4096 at M = 2): VALU dot
+//   products.  One wavefront streams whole rows, each lane a fixed set of
+//   16-byte segments (32 k) of every row, so the lane's slice of x stays in
+//   registers for the kernel's lifetime.  Per 16-block the E4M3 scale is
+//   split into its power of two 2^e and its mantissa mu in [1, 2): the
+//   fp4->bf16 converter applies 2^e exactly (it only uses a scale's
 //   exponent), v_dot2_f32_bf16 accumulates a block partial, and mu is applied
 //   once per block.  About 1.4 VALU ops per weight at M = 1.
-//
-// gemv_mfma_kernel (M > 2): bf16 MFMA (v_mfma_f32_16x16x32_bf16) on weights
-//   dequantized in registers (exact code*scale in bf16).  A 256-thread
-//   workgroup stages each 256-k chunk of x (M rounded up to 16) in LDS once
-//   (double buffered), and each wavefront reuses those fragments for R tiles
-//   of 16 weight rows, with the next chunk's weights prefetched into
-//   registers while the current one computes.
+// The others run bf16 / f16 MFMA (16x16x32) on weights dequantized in
+// registers (code * scale is exact in either type):
+// gemv_xres_kernel (3 <= M <= 16 when x fits in LDS): x resident in LDS as
+//   f16 rows scaled by a power of two, weights copied straight to LDS.
+// gemv_ring_kernel (other M <= 64, K % 1024 == 0): weights in a register
+//   ring two chunks deep, x in LDS panels.
+// gemv_panel_kernel (other M, K % 512 == 0), gemv_mfma_kernel (K % 256 == 0)
+//   and gemv_mfma_ragged_kernel (any K % 16 == 0): the general forms.
+// The x-resident and panel kernels also run the expert layer's grouped GEMM
+// on gathered activation rows (kMoe).
 #include <type_traits>
 
 #include "nvfp4_device.hpp"
