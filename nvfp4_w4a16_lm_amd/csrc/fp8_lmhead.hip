@@ -419,6 +419,132 @@ hipError_t launch_fp8_quant_rows(const void* a, int64_t R, int64_t K, uint8_t* q
   return launch_kernel(fn, dim3((unsigned)blocks), dim3(256), stream, (const uint16_t*)a, R, (int)K, q, scales);
 }
 
+// fp8_dot_kernel<MR, SEG>: M = MR (1 or 2) rows, K % 16 == 0, K <= 1024 SEG.
+// VALU dot products: weight rows are dealt in batches of 4 to the wavefronts
+// round-robin (wavefront w takes batches w, w + W, ...), two batches in
+// flight; lane l covers the 16-byte segments l, l + 64, ... of every row, so
+// its slice of the activation rows stays in registers, converted once to
+// bf16 pairs.  e4m3 -> bf16 is exact (NVFP4_E4M3X2_TO_BF16), and so is the
+// product of two such values in fp32; v_dot2_f32_bf16
+// accumulates, a wavefront reduction sums the lanes, and the epilogue is the
+// MFMA kernels' (acc * s_x[m] * s_w[n] + bias[n], one bf16 rounding).
+// Segments past K hold zero activations, so the clamped weight loads that
+// fill them contribute nothing.
+template <int MR, int SEG>
+__global__ __launch_bounds__(256) void fp8_dot_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                      int M, int K, const uint8_t* __restrict__ wq,
+                                                      const float* __restrict__ ws, int N,
+                                                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+                                                      int nwaves) {
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r_begin = 4 * wid;
+  if (wid >= nwaves || r_begin >= N) return;
+  const int rstep = 4 * nwaves;
+  const int nseg = K >> 4;
+
+  // this lane's activation slice as bf16 pairs: pair 2 q + h of segment j
+  // holds bytes 2 h, 2 h + 1 of word q of the segment's 16 bytes
+  bf16x2 xb[MR][SEG][8];
+  auto load_batch = [&](int r0, u32x4 (&pk)[4][SEG]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = min(r0 + i, N - 1);       // duplicates are computed, never stored
+#pragma unroll
+      for (int j = 0; j < SEG; ++j)
+        pk[i][j] = load_stream16(wq + row * K + 16 * min(lane + 64 * j, nseg - 1));
+    }
+  };
+  u32x4 pkA[4][SEG], pkB[4][SEG];
+  load_batch(r_begin, pkA);                         // the first weights are requested before x
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+      const int seg = lane + 64 * j;
+      const bool ok = seg < nseg && m < M;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xq + (int64_t)min(m, M - 1) * K + 16 * min(seg, nseg - 1));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t wv = ok ? v[q] : 0u;
+        xb[m][j][2 * q] = NVFP4_E4M3X2_TO_BF16(wv, false);
+        xb[m][j][2 * q + 1] = NVFP4_E4M3X2_TO_BF16(wv, true);
+      }
+    }
+  float sx[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) sx[m] = xs[min(m, M - 1)];
+
+  auto compute_batch = [&](int r0, const u32x4 (&pk)[4][SEG]) {
+    float p[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[m][i] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < SEG; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // copy the vector element to a scalar first (see gemv_dot_kernel)
+          const uint32_t w = pk[i][j][q];
+          const bf16x2 a0 = NVFP4_E4M3X2_TO_BF16(w, false);
+          const bf16x2 a1 = NVFP4_E4M3X2_TO_BF16(w, true);
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            p[m][i] = __builtin_amdgcn_fdot2_f32_bf16(a0, xb[m][j][2 * q], p[m][i], false);
+            p[m][i] = __builtin_amdgcn_fdot2_f32_bf16(a1, xb[m][j][2 * q + 1], p[m][i], false);
+          }
+        }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float tot = wave_sum4(p[m], lane);
+      const int row = r0 + ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+      if ((lane & 15) == 0 && row < N && m < M) {
+        float val = tot * sx[m] * ws[row];
+        if (bias != nullptr) val += __uint_as_float((uint32_t)bias[row] << 16);
+        y[(int64_t)m * N + row] = (uint16_t)f32_to_bf16_rne(val);
+      }
+    }
+  };
+
+  for (int r0 = r_begin; r0 < N; r0 += 2 * rstep) {
+    const bool hasB = r0 + rstep < N;
+    if (hasB) load_batch(r0 + rstep, pkB);
+    compute_batch(r0, pkA);
+    if (!hasB) break;
+    if (r0 + 2 * rstep < N) load_batch(r0 + 2 * rstep, pkA);
+    compute_batch(r0 + rstep, pkB);
+  }
+}
+
+template <int MR, int SEG>
+static hipError_t fp8_dot_launch(const uint8_t* xq, const float* xs, int M, int K, const uint8_t* wq,
+                                 const float* ws, int N, const void* bias, void* y, hipStream_t stream) {
+  // as many wavefronts as fit at once, trimmed so that each takes the same
+  // number of batches (within one)
+  const void* fn = (const void*)fp8_dot_kernel<MR, SEG>;
+  const int dev = current_device();
+  const int resident = 4 * device_cus(dev) * blocks_per_cu(fn, dev, 256, 0);
+  const int batches = (N + 3) / 4;
+  const int per_wave = (batches + resident - 1) / resident;
+  const int waves = (batches + per_wave - 1) / per_wave;
+  return launch_kernel(fn, dim3((waves + 3) / 4), dim3(256), stream, xq, xs, M, K, wq, ws, N,
+                       (const uint16_t*)bias, (uint16_t*)y, waves);
+}
+
+template <int MR>
+static hipError_t fp8_dot_dispatch(const uint8_t* xq, const float* xs, int M, int K, const uint8_t* wq,
+                                   const float* ws, int N, const void* bias, void* y, hipStream_t stream) {
+  switch ((K + 1023) / 1024) {
+    case 1: return fp8_dot_launch<MR, 1>(xq, xs, M, K, wq, ws, N, bias, y, stream);
+    case 2: return fp8_dot_launch<MR, 2>(xq, xs, M, K, wq, ws, N, bias, y, stream);
+    case 3: return fp8_dot_launch<1, 3>(xq, xs, M, K, wq, ws, N, bias, y, stream);   // M = 1 only
+    default: return fp8_dot_launch<1, 4>(xq, xs, M, K, wq, ws, N, bias, y, stream);
+  }
+}
+
 template <int MT>
 static hipError_t fp8_gemm_launch(const uint8_t* xq, const float* xs, int M, int K, const uint8_t* wq,
                                   const float* ws, int N, const void* bias, void* y, hipStream_t stream) {
@@ -434,6 +560,12 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_
     const int m_tiles = (int)((M + kFp8PT - 1) / kFp8PT), n_tiles = (int)((N + kFp8PT - 1) / kFp8PT);
     return launch_kernel((const void*)fp8_prefill_kernel, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), stream,
                          xq, xs, m, k, wq, ws, n, (const uint16_t*)bias, (uint16_t*)y, m_tiles);
+  }
+  // one activation row (K <= 4096) or two (K <= 2048: their registers and
+  // two batches of weights stay under 256 VGPRs): the VALU dot kernel
+  if (K % 16 == 0 && ((M == 1 && K <= 4096) || (M == 2 && K <= 2048))) {
+    if (M == 1) return fp8_dot_dispatch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+    return fp8_dot_dispatch<2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
   }
   switch (std::min<int64_t>((M + 15) / 16, 8)) {
     case 1: return fp8_gemm_launch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);

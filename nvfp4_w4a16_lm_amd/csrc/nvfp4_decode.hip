@@ -56,27 +56,6 @@ __device__ __forceinline__ uint32_t out_bf16(float acc, float gs, const uint16_t
   return f32_to_bf16_rne(v);
 }
 
-// Sum over the 16 lanes of each DPP row (quad swaps, then half-row and row mirrors).
-__device__ __forceinline__ float dpp_row_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half-row mirror
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row mirror
-  return v;
-}
-
-// Four per-lane partials (rows 0..3 of a batch) -> full wavefront sums, with
-// row i ending up in every lane whose bits 5,4 equal (i >> 1, i & 1).
-__device__ __forceinline__ float wave_sum4(const float p[4], int lane) {
-  const bool h5 = lane & 32, h4 = lane & 16;
-  const float s0 = h5 ? p[0] : p[2], k0 = h5 ? p[2] : p[0];
-  const float s1 = h5 ? p[1] : p[3], k1 = h5 ? p[3] : p[1];
-  const float w0 = k0 + __shfl_xor(s0, 32, 64);
-  const float w1 = k1 + __shfl_xor(s1, 32, 64);
-  const float s = h4 ? w0 : w1, k = h4 ? w1 : w0;
-  return dpp_row_sum(k + __shfl_xor(s, 16, 64));
-}
-
 // ---------------------------------------------------------------------------
 // gemv_dot_kernel<MR, SEG>: M = MR (1 or 2) rows of x; SEG = 16-byte segments
 // per lane per row (K <= 2048 * SEG, K % 32 == 0).  The rows are dealt in

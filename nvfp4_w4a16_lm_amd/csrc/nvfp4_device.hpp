@@ -27,6 +27,27 @@ __device__ __forceinline__ u32x4 load_stream16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Sum over the 16 lanes of each DPP row (quad swaps, then half-row and row mirrors).
+__device__ __forceinline__ float dpp_row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half-row mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row mirror
+  return v;
+}
+
+// Four per-lane partials (rows 0..3 of a batch) -> full wavefront sums, with
+// row i ending up in every lane whose bits 5,4 equal (i >> 1, i & 1).
+__device__ __forceinline__ float wave_sum4(const float p[4], int lane) {
+  const bool h5 = lane & 32, h4 = lane & 16;
+  const float s0 = h5 ? p[0] : p[2], k0 = h5 ? p[2] : p[0];
+  const float s1 = h5 ? p[1] : p[3], k1 = h5 ? p[3] : p[1];
+  const float w0 = k0 + __shfl_xor(s0, 32, 64);
+  const float w1 = k1 + __shfl_xor(s1, 32, 64);
+  const float s = h4 ? w0 : w1, k = h4 ? w1 : w0;
+  return dpp_row_sum(k + __shfl_xor(s, 16, 64));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
@@ -72,6 +93,10 @@ __device__ __forceinline__ uint32_t fix_zero_signs(uint32_t w) {
 
 // E4M3 byte SEL of a 32-bit word -> float (gfx950 converter, OCP e4m3fn).
 #define NVFP4_E4M3_TO_F32(word, SEL) __builtin_amdgcn_cvt_f32_fp8((int)(word), (SEL))
+
+// E4M3 bytes 2 SEL and 2 SEL + 1 of a 32-bit word -> a pair of bf16 (gfx950
+// converter with scale 1; every finite e4m3fn value is exact in bf16).
+#define NVFP4_E4M3X2_TO_BF16(word, SEL) __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((word), 1.0f, (SEL))
 
 // Byte j of `w` (two codes, the low nibble first) -> the two values
 // code * s as a packed pair of bf16.  The converter gives the exact E2M1

@@ -12,6 +12,10 @@
 // f16 route in both forms (split_scale or the scale itself +
 // scale_mantissa_f16, then dequant8_f16) and the power-of-two bf16 converter
 // the dot kernel feeds to v_dot2_f32_bf16.
+//
+// FP8 copy: the e4m3 -> bf16 pair converter (NVFP4_E4M3X2_TO_BF16) that the
+// FP8 dot kernel applies to weights and activations, for every pair of bytes
+// in both halves of a word.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,6 +77,14 @@ __global__ void dequant_table_kernel(uint32_t* __restrict__ f32route, uint32_t* 
   }
 }
 
+// thread t (0..65535): the byte pair (t & 0xFF, t >> 8) in the low half of a
+// word (lo) and in the high half (hi), the other half holding different bytes
+__global__ void e4m3_bf16_table_kernel(uint32_t* __restrict__ lo, uint32_t* __restrict__ hi) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  lo[t] = __builtin_bit_cast(uint32_t, NVFP4_E4M3X2_TO_BF16(t | ((t ^ 0x5A5Au) << 16), false));
+  hi[t] = __builtin_bit_cast(uint32_t, NVFP4_E4M3X2_TO_BF16((t << 16) | (t ^ 0xA5A5u), true));
+}
+
 extern "C" {
 
 // count values starting at bit pattern first (count % 8 == 0, count > 0,
@@ -95,6 +107,13 @@ int nvfp4_test_dequant_table(uint32_t* f32route, uint32_t* f16route, uint32_t* f
   if (!f32route || !f16route || !f16s || !pow2bf16 || !e2 || !mu) return -1;
   hipLaunchKernelGGL(dequant_table_kernel, dim3(127), dim3(256), 0, (hipStream_t)stream, f32route, f16route, f16s,
                      pow2bf16, e2, mu);
+  return (int)hipGetLastError();
+}
+
+// outputs sized 65536 words each
+int nvfp4_test_e4m3_bf16_table(uint32_t* lo, uint32_t* hi, void* stream) {
+  if (!lo || !hi) return -1;
+  hipLaunchKernelGGL(e4m3_bf16_table_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, lo, hi);
   return (int)hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ def lib():
     lib.nvfp4_test_e2m1_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p]
     lib.nvfp4_test_dequant_table.argtypes = [ctypes.c_void_p] * 7
+    lib.nvfp4_test_e4m3_bf16_table.argtypes = [ctypes.c_void_p] * 3
     return lib
 
 
@@ -129,3 +130,29 @@ def test_dequant_routes_exact_for_all_codes_and_scales(lib):
     assert np.all(np.isfinite(got_p2)), "a zero scale (e2 = 0) must still give finite values (they are times mu = 0)"
     # signs: negative codes give negative values, and code 8 (-0) gives a zero
     assert np.all(np.signbit(got32[:, 0x08, 0]) | (got32[:, 0x08, 0] == 0))
+
+
+def test_e4m3_pair_to_bf16_exact_for_every_byte_pair(lib):
+    """The FP8 dot kernel's converter (bytes 2 SEL, 2 SEL + 1 of a word -> two
+    bf16): every pair of e4m3fn bytes, in both halves of a word, against the
+    oracle's e4m3 decoding (vLLM modelopt.py, KFp8StaticChannel: the
+    float8_e4m3fn format), rounded to bf16 (exact for every finite value);
+    the NaN bytes 0x7F and 0xFF give NaN."""
+    import oracle.fp8_oracle as F
+
+    stream = torch.cuda.current_stream().cuda_stream
+    lo = torch.empty(65536, dtype=torch.int32, device="cuda")
+    hi = torch.empty_like(lo)
+    assert lib.nvfp4_test_e4m3_bf16_table(lo.data_ptr(), hi.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    t = np.arange(65536, dtype=np.uint32)
+    b = np.stack([t & 0xFF, t >> 8], axis=1).astype(np.uint8)          # [pair, element]
+    nan = (b & 0x7F) == 0x7F
+    want = np.where(nan, 0.0, F.e4m3_decode_signed(np.where(nan, 0, b)))
+    assert np.array_equal(want.astype(np.float32).astype(np.float64), want)   # exact in float32
+    for name, got_t in (("low half", lo), ("high half", hi)):
+        u = got_t.cpu().numpy().view(np.uint32)
+        got = np.stack([(u & 0xFFFF) << 16, u & 0xFFFF0000], axis=1).astype(np.uint32).view(np.float32)
+        assert np.all(np.isnan(got[nan])), f"{name}: NaN bytes"
+        g, w = got[~nan].astype(np.float64), want[~nan]
+        assert np.array_equal(g, w), f"{name}: {int(np.sum(g != w))} byte values differ"

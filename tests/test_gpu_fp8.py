@@ -65,9 +65,12 @@ def test_quantize_rows_special_rows():
     assert q[1, 3] == 0x80 and q[1, 5] == 0x7E
 
 
-@pytest.mark.parametrize("m", [1, 4, 17, 32, 64, 65, 130, 300])
+@pytest.mark.parametrize("m", [1, 2, 4, 17, 32, 64, 65, 130, 300])
 @pytest.mark.parametrize("n,k", [(1027, 512), (128, 48), (300, 1040), (2053, 4096)])
 def test_gemm_matches_oracle(m, n, k):
+    """M = 1 (K <= 4096) and M = 2 (K <= 2048) run the VALU dot kernel
+    (segments past K in the last 64-lane round: K = 48, 1040), the rest the
+    MFMA kernels."""
     w = wl.random_weight_bits(n, k, sigma=0.02, seed=n + k)
     x = wl.random_activation_bits(m, k, seed=m + 7)
     wq, ws = F.quantize_rows(w)
