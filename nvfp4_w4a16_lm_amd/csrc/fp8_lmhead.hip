@@ -409,6 +409,217 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp8_ring_kernel<MT, R>: 3 <= M <= 16 MT activation rows (MT = 1, 2, 4),
+// K % 512 == 0.  The streaming structure of the NVFP4 register-ring decode
+// kernel, with e4m3 operands and nothing to dequantize:
+//  * a workgroup of 8 wavefronts owns blocks of 128 R weight rows, R tiles of
+//    16 rows per wavefront; a chunk is 128 k (128 bytes of a row); each
+//    wavefront keeps two chunks of its tiles in registers in flight, loaded
+//    8 lanes per row segment (whole 128-byte lines, nontemporal), and moves
+//    each chunk into the operand layout through its own 2 R KiB of LDS
+//    (16-byte pieces XOR-swizzled by row, no barrier);
+//  * one v_mfma_scale_f32_16x16x128_f8f6f4 per tile, activation tile and
+//    chunk (unit block scales; lane (r, g) = (l % 16, l / 16) supplies the
+//    32 bytes [32 g, 32 g + 32) of row r of the chunk for both operands);
+//  * x is copied into LDS in panels of 32 KiB (pk bytes of 16 MT rows, rows
+//    past M repeating row M - 1) by direct-to-LDS loads, double buffered,
+//    one workgroup barrier per panel;
+//  * loads complete in issue order, so every wait is an exact vmcnt.
+// Epilogue: acc * s_x[m] * s_w[n] (+ bias[n]) in float32, one bf16
+// rounding.  Rows past N read as zero through the buffer resource and are
+// never stored.
+// ---------------------------------------------------------------------------
+constexpr int kF8RingNW = 8;                           // wavefronts per workgroup (two per SIMD)
+
+template <int MT>
+struct F8RingGeom {
+  static constexpr int rows = 16 * MT;                          // x rows in a panel
+  static constexpr int pk = MT == 1 ? 2048 : MT == 2 ? 1024 : 512;   // panel columns (k = bytes)
+  static constexpr int pchunks = pk / 128;                      // chunks per panel: 16, 8, 4
+  static constexpr int xbytes = rows * pk;                      // one panel buffer: 32 KiB
+  static constexpr int xcopies = xbytes / 1024 / kF8RingNW;     // 1 KiB copies per wavefront per panel
+  static_assert(xbytes % (1024 * kF8RingNW) == 0, "panel copies must split evenly over the wavefronts");
+  static_assert(pchunks % 4 == 0, "panels start on the unrolled 4-chunk steps");
+};
+
+// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt bits [3:0] and [15:14])
+template <int N>
+__device__ __forceinline__ void f8_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int MT, int R>
+__global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t* __restrict__ xq,
+                                                                const float* __restrict__ xs, int M, int K,
+                                                                const uint8_t* __restrict__ wq,
+                                                                const float* __restrict__ ws, int N,
+                                                                const uint16_t* __restrict__ bias,
+                                                                uint16_t* __restrict__ y) {
+  using G = F8RingGeom<MT>;
+  constexpr int NW = kF8RingNW;
+  constexpr int kBatch = 2 * R;                         // loads per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t xsl[2][G::xbytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wt[NW][R * 2048];
+  // the wavefront index is uniform: keeping it in a scalar register keeps the
+  // buffer resources below scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int nchunks = K / 128;
+  const int npanels = K / G::pk;
+  // transpose write: load lane l holds row 8 j + l / 8, piece l % 8 (slot piece ^ (row & 7))
+  const int wwr = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+  // operand read: row r, pieces 2 g and 2 g + 1
+  const int wrd0 = 128 * r + 16 * ((2 * g) ^ (r & 7)), wrd1 = 128 * r + 16 * ((2 * g + 1) ^ (r & 7));
+  uint8_t* const wmine = wt[wave];
+  const int wlane = (lane >> 3) * K + 16 * (lane & 7);   // byte offset within this wavefront's rows
+  constexpr int kRowsWG = NW * R * 16;
+  const int nblocks = (N + kRowsWG - 1) / kRowsWG;
+
+  for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const int n_wave = blk * kRowsWG + wave * (R * 16);
+    // rows past N lie outside the resource and read as zero (never stored);
+    // every field passes readfirstlane so that the resource stays scalar
+    const int rows_in = __builtin_amdgcn_readfirstlane(max(0, min(R * 16, N - n_wave)));
+    const int row0 = __builtin_amdgcn_readfirstlane(min(n_wave, N - 1));
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(wq + (int64_t)row0 * K), (short)0, __builtin_amdgcn_readfirstlane(rows_in * K), 0x00020000);
+
+    u32x4 wr[2][R][2];                                  // the ring: chunks c (slot c % 2) and c + 1
+    f32x4 acc[R][MT];
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int c, auto SLOT) {
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          wr[decltype(SLOT)::value][t][j] =
+              __builtin_amdgcn_raw_buffer_load_b128(wres, wlane + (16 * t + 8 * j) * K, 128 * c, 2 /* nontemporal */);
+    };
+    // x panel P into buffer P % 2: copy i of this wavefront fills panel bytes [1 KiB (i NW + wave), + 1 KiB)
+    auto x_copy = [&](int P) {
+      uint8_t* const buf = xsl[P & 1];
+#pragma unroll
+      for (int i = 0; i < G::xcopies; ++i) {
+        const int off = 1024 * (i * NW + wave) + 16 * lane;
+        const int m = off / G::pk, slot = (off % G::pk) >> 4;
+        const int piece = slot ^ (m & 7);
+        __builtin_amdgcn_global_load_lds((const void*)(xq + (int64_t)min(m, M - 1) * K + P * G::pk + 16 * piece),
+                                         (fp8_lds_ptr_t)(buf + 1024 * (i * NW + wave)), 16, 0, 0);
+      }
+    };
+
+    // one chunk; U = c % 4 (the loop below steps c by 4; panels start at U = 0)
+    auto step = [&](int c, auto U_) {
+      constexpr int u = decltype(U_)::value;
+      const int cc = c % G::pchunks;                    // chunk within its panel
+      const int P = c / G::pchunks;
+      // wait for batch(c); batch(c + 1) and, after a panel start, the copies
+      // of panel P + 1 (issued after batch(c)) may stay in flight
+      if (c + 1 < nchunks) {
+        if (u == 1 && cc == 1 && P + 1 < npanels) f8_wait_vmcnt<kBatch + G::xcopies>();
+        else f8_wait_vmcnt<kBatch>();
+      } else {
+        f8_wait_vmcnt<0>();
+      }
+      if constexpr (u == 0) {
+        if (cc == 0) {
+          asm volatile("s_barrier" ::: "memory");       // panel P is complete; panel P - 1 is no longer read
+          if (P + 1 < npanels) x_copy(P + 1);
+        }
+      }
+      // chunk c: registers -> this wavefront's LDS, then refill the slot with batch(c + 2)
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          *reinterpret_cast<u32x4*>(wmine + 2048 * t + 1024 * j + wwr) = wr[u & 1][t][j];
+      if (c + 2 < nchunks) issue(c + 2, std::integral_constant<int, u & 1>{});
+      fp8_i32x8 bx[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = 16 * mt + r;
+        const uint8_t* const xr = xsl[P & 1] + row * G::pk;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(xr + 16 * ((8 * cc + 2 * g) ^ (row & 7)));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(xr + 16 * ((8 * cc + 2 * g + 1) ^ (row & 7)));
+        bx[mt] = fp8_i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + wrd0);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + wrd1);
+        const fp8_i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[t][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bx[mt], acc[t][mt], 0, 0, 0, kFp8UnitScales,
+                                                                       0, kFp8UnitScales);
+        // keep later tiles' operand reads from being hoisted here (register pressure)
+        if constexpr (MT >= 2) __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    x_copy(0);
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    for (int c = 0; c < nchunks; c += 4) {
+      step(c, std::integral_constant<int, 0>{});
+      step(c + 1, std::integral_constant<int, 1>{});
+      step(c + 2, std::integral_constant<int, 2>{});
+      step(c + 3, std::integral_constant<int, 3>{});
+    }
+
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int n0 = n_wave + 16 * t + 4 * g;
+      float sw[4], bv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int nn = min(n0 + v, N - 1);
+        sw[v] = ws[nn];
+        bv[v] = bias != nullptr ? __uint_as_float((uint32_t)bias[nn] << 16) : 0.0f;
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + r;
+        if (m >= M) continue;
+        const float sx = xs[m];
+        uint16_t* yrow = y + (int64_t)m * N;
+        uint32_t o[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float val = acc[t][mt][v] * sx * sw[v];
+          if (bias != nullptr) val += bv[v];
+          o[v] = f32_to_bf16_rne(val);
+        }
+        if ((N & 3) == 0 && n0 + 3 < N) {
+          *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n0 + v < N) yrow[n0 + v] = (uint16_t)o[v];
+        }
+      }
+    }
+    __syncthreads();                                    // the x buffers are reused by the next block
+  }
+}
+
+template <int MT, int R>
+static hipError_t fp8_ring_launch(const uint8_t* xq, const float* xs, int M, int K, const uint8_t* wq,
+                                  const float* ws, int N, const void* bias, void* y, hipStream_t stream) {
+  const void* fn = (const void*)fp8_ring_kernel<MT, R>;
+  const int nblocks = (N + kF8RingNW * R * 16 - 1) / (kF8RingNW * R * 16);
+  const int dev = current_device();
+  const dim3 grid(std::min(nblocks, device_cus(dev) * blocks_per_cu(fn, dev, 64 * kF8RingNW, 0)));
+  return launch_kernel(fn, grid, dim3(64 * kF8RingNW), stream, xq, xs, M, K, wq, ws, N, (const uint16_t*)bias,
+                       (uint16_t*)y);
+}
+
 hipError_t launch_fp8_quant_rows(const void* a, int64_t R, int64_t K, uint8_t* q, float* scales,
                                  hipStream_t stream) {
   const int64_t blocks = std::min<int64_t>((R + 3) / 4, 65536);
@@ -566,6 +777,11 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_
   if (K % 16 == 0 && ((M == 1 && K <= 4096) || (M == 2 && K <= 2048))) {
     if (M == 1) return fp8_dot_dispatch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     return fp8_dot_dispatch<2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+  }
+  if (K % 512 == 0 && M >= 3 && M <= 64) {
+    if (M <= 16) return fp8_ring_launch<1, 4>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+    if (M <= 32) return fp8_ring_launch<2, 2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+    return fp8_ring_launch<4, 2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
   }
   switch (std::min<int64_t>((M + 15) / 16, 8)) {
     case 1: return fp8_gemm_launch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);

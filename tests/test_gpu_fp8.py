@@ -79,6 +79,23 @@ def test_gemm_matches_oracle(m, n, k):
     check_fp8_gemm(host_bits(y), xq, xs, wq, ws, label=f"M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m,n,k,with_bias", [(3, 140000, 512, True), (20, 70000, 512, False), (16, 1300, 8192, False),
+                                             (24, 1030, 8192, True), (40, 2100, 1024, False), (64, 900, 8192, True)])
+def test_ring_kernel_panels_blocks_and_bias(m, n, k, with_bias):
+    """3 <= M <= 64 with K % 512 == 0 runs the register-ring kernel: several x
+    panels per block at K = 8192 (4 at M <= 16, 8 at M <= 32, 16 beyond),
+    more 512-row (M <= 16) or 256-row blocks than compute units at N =
+    140000 / 70000, rows past N and M in the last tiles, and the bias."""
+    w = wl.random_weight_bits(n, k, sigma=0.02, seed=n + 3 * k)
+    x = wl.random_activation_bits(m, k, seed=m + 11)
+    wq, ws = F.quantize_rows(w)
+    xq, xs = F.quantize_rows(x)
+    bias = wl.random_weight_bits(1, n, sigma=0.5, seed=5)[0] if with_bias else None
+    y = B.nvfp4_fp8_gemm(dev_u8(xq), torch.from_numpy(xs).to(DEV), dev_u8(wq), torch.from_numpy(ws).to(DEV),
+                         bias=dev_bf16(bias) if with_bias else None)
+    check_fp8_gemm(host_bits(y), xq, xs, wq, ws, bias_bits=bias, label=f"ring M={m} N={n} K={k}")
+
+
 def test_gemm_with_bias_end_to_end():
     """GPU quantization of both operands, then the GEMM with a bias."""
     n, k, m = 515, 320, 9
