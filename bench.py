@@ -60,8 +60,6 @@ def decode_kernel_name(m: int, k: int) -> str:
         deep = k % 1024 == 0
         if (deep and (fits(8, 2) or fits(16, 2))) or fits(16, 0) or (not deep and fits(8, 0)):
             return "gemv_xres_kernel"
-    if k % 1024 == 0:
-        return "gemv_ring_kernel"
     return "gemv_panel_kernel" if k % 512 == 0 else "gemv_mfma_kernel"
 
 

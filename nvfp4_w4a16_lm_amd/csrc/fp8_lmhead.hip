@@ -411,8 +411,8 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
 
 // ---------------------------------------------------------------------------
 // fp8_ring_kernel<MT, R>: 3 <= M <= 16 MT activation rows (MT = 1, 2, 4),
-// K % 512 == 0.  The streaming structure of the NVFP4 register-ring decode
-// kernel, with e4m3 operands and nothing to dequantize:
+// K % 512 == 0.  Weights stream through registers, with e4m3 operands and
+// nothing to dequantize:
 //  * a workgroup of 8 wavefronts owns blocks of 128 R weight rows, R tiles of
 //    16 rows per wavefront; a chunk is 128 k (128 bytes of a row); each
 //    wavefront keeps two chunks of its tiles in registers in flight, loaded

@@ -21,10 +21,10 @@
 // registers (code * scale is exact in either type):
 // gemv_xres_kernel (3 <= M <= 16 when x fits in LDS): x resident in LDS as
 //   f16 rows scaled by a power of two, weights copied straight to LDS.
-// gemv_ring_kernel (other M <= 64, K % 1024 == 0): weights in a register
-//   ring two chunks deep, x in LDS panels.
-// gemv_panel_kernel (other M, K % 512 == 0), gemv_mfma_kernel (K % 256 == 0)
-//   and gemv_mfma_ragged_kernel (any K % 16 == 0): the general forms.
+// gemv_panel_kernel (other M <= 64, K % 512 == 0): weights copied straight
+//   to per-wavefront LDS one chunk ahead, x in LDS panels.
+// gemv_mfma_kernel (K % 256 == 0) and gemv_mfma_ragged_kernel (any K % 16
+//   == 0): the general forms.
 // The x-resident and panel kernels also run the expert layer's grouped GEMM
 // on gathered activation rows (kMoe).
 #include <type_traits>
@@ -37,7 +37,6 @@ namespace nvfp4 {
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(0) alone / lgkmcnt(0) alone
 constexpr int kWaitVm0 = 0x0F70, kWaitLgkm0 = 0xC07F;
-constexpr int kWaitVm2 = 0x0F72, kWaitVm3 = 0x0F73;   // vmcnt(2) / vmcnt(3) alone
 constexpr int kCachePolicyNT = 2;   // cache-policy operand of direct-to-LDS loads: nontemporal
 constexpr int kScaleGroup = 4;      // chunks of scales per direct-to-LDS scale copy
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -904,241 +903,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// gemv_ring_kernel<MT, R>: 3 <= M <= 16 MT activation rows, K % 1024 == 0.
-//
-// The weights land in registers, not LDS, so that each wavefront keeps two
-// 256-k chunks of its R 16-row tiles in flight (R = 4: 16 KiB per wavefront,
-// 128 KiB per compute unit) while it computes a third:
-//  * weight loads take whole 128-byte lines, 8 lanes per row segment
-//    (lane l: row 8 j + l / 8, bytes 16 (l % 8) of the chunk), nontemporal;
-//  * each chunk is moved into the 16x16x32 operand layout through the
-//    wavefront's own 8 KiB of LDS (two 16-byte writes and two 16-byte reads
-//    per lane and tile; 16-byte pieces XOR-swizzled by row, no barrier);
-//  * block scales arrive 4 chunks at a time, one 16-byte load per lane and
-//    tile (lane (r, g) = (l % 16, l / 16): row r, the 16 scales of chunk 4q + g),
-//    written once into the wavefront's 4 KiB scale region; each chunk, lane
-//    (r, g) reads the 4 scales of its own k range (4 bytes per tile);
-//  * x is copied into LDS in panels of 32 KiB (pk columns of 16 MT rows; rows
-//    past M repeat row M - 1) by direct-to-LDS loads, double buffered: panel
-//    P + 1 is copied while panel P is used, with one workgroup barrier per
-//    panel;
-//  * loads complete in issue order, so every wait is an exact vmcnt: the
-//    batch of chunk c (the 4 scale loads first when c % 4 == 0, then 2 R
-//    weight loads) is issued two chunks ahead, and the x copies of panel P + 1
-//    right after the barrier that starts panel P.
-// Arithmetic as in gemv_panel_kernel: fp32-route dequantization (exact
-// code * scale in bf16) and bf16 MFMA with fp32 accumulation; each MFMA step's
-// activation fragments serve all R tiles.  Rows past N are read from row N - 1
-// and never stored.
-// ---------------------------------------------------------------------------
-constexpr int kRingNW = 8;                              // wavefronts per workgroup (two per SIMD)
-
-template <int MT>
-struct RingGeom {
-  static constexpr int rows = 16 * MT;                           // x rows in a panel (M rounded up)
-  static constexpr int pk = MT == 1 ? 1024 : MT == 2 ? 512 : 256;   // panel columns
-  static constexpr int pchunks = pk / kChunk;                    // chunks per panel: 4, 2, 1, 1
-  static constexpr int xbytes = rows * pk * 2;                   // one panel buffer (<= 32 KiB)
-  static constexpr int xcopies = xbytes / 1024 / kRingNW;        // 1 KiB copies per wavefront per panel
-  static_assert(xbytes % (1024 * kRingNW) == 0, "panel copies must split evenly over the wavefronts");
-  static_assert(4 % pchunks == 0, "panel boundaries must fall on the unrolled 4-chunk steps");
-};
-
-// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt bits [3:0] and [15:14])
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Workgroup barrier without the implicit wait for outstanding loads that
-// __syncthreads adds (callers wait for what they need first).
-__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int V>
-using Ic = std::integral_constant<int, V>;
-
-template <int MT, int R>
-__global__ __launch_bounds__(64 * kRingNW) void gemv_ring_kernel(const uint16_t* __restrict__ x, int M, int K,
-                                                               const uint8_t* __restrict__ packed,
-                                                               const uint8_t* __restrict__ scales,
-                                                               const float* __restrict__ gs_ptr, int N,
-                                                               const uint16_t* __restrict__ bias,
-                                                               uint16_t* __restrict__ y) {
-  using G = RingGeom<MT>;
-  constexpr int NW = kRingNW;
-  constexpr int kBatchW = 2 * R;                        // weight loads per chunk
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][G::xbytes];
-  __shared__ __attribute__((aligned(16))) uint8_t wt[NW][R * 2048];
-  __shared__ __attribute__((aligned(16))) uint8_t st[NW][R * 1024];   // [tile][chunk of group][row][16 scales]
-  // the wavefront index is uniform: keeping it in a scalar register keeps the
-  // buffer resources below scalar (a per-lane resource costs a loop per load)
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, g = lane >> 4;
-  const int nchunks = K / kChunk;
-  const int npanels = K / G::pk;
-  const int64_t prow = K >> 1, srow = K >> 4;
-  const float gs = *gs_ptr;
-  constexpr int kRowsWG = NW * R * 16;
-  const int nblocks = (N + kRowsWG - 1) / kRowsWG;
-  // transpose write: load lane l holds row 8 j + l / 8, piece l % 8 (slot piece ^ (row & 7))
-  const int wwr = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
-  // operand read: row r, pieces 2 g and 2 g + 1
-  const int wrd0 = 128 * r + 16 * ((2 * g) ^ (r & 7)), wrd1 = 128 * r + 16 * ((2 * g + 1) ^ (r & 7));
-  uint8_t* const wmine = wt[wave];
-  uint8_t* const smine = st[wave];
-  const int srd = 16 * r + 4 * g;                       // this lane's 4 scales of a chunk: + 1024 t + 256 (c % 4)
-
-  // byte offsets within this wavefront's rows: weight load lane (row 8 j + l / 8 of a
-  // tile, piece l % 8), scale load lane (row r, 16 bytes of chunk 4 q + g)
-  const int wlane = (lane >> 3) * (int)prow + 16 * (lane & 7);
-  const int slane = r * (int)srow + 16 * g;
-
-  for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
-    const int n_wave = blk * kRowsWG + wave * (R * 16);
-    // buffer resources over this wavefront's rows: rows past N lie outside
-    // them and read as zero (their outputs are never stored)
-    // (every field passes readfirstlane: a resource the compiler cannot prove
-    // uniform is wrapped in a loop around each load)
-    const int rows_in = __builtin_amdgcn_readfirstlane(max(0, min(R * 16, N - n_wave)));
-    const int row0 = __builtin_amdgcn_readfirstlane(min(n_wave, N - 1));
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(packed + (int64_t)row0 * prow), (short)0, __builtin_amdgcn_readfirstlane(rows_in * (int)prow),
-        0x00020000);
-    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(scales + (int64_t)row0 * srow), (short)0, __builtin_amdgcn_readfirstlane(rows_in * (int)srow),
-        0x00020000);
-
-    u32x4 wr[2][R][2];                                  // the ring: chunks c (slot c % 2) and c + 1
-    u32x4 sraw[R];                                      // scales of the next 4-chunk group, as loaded
-    f32x4 acc[R][MT];
-#pragma unroll
-    for (int t = 0; t < R; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // batch(c) into ring slot `slot`: the scales of group c / 4 first (c % 4 == 0), then the weights
-    auto issue = [&](int c, auto SLOT, auto GROUP_START) {
-      if constexpr (decltype(GROUP_START)::value) {
-#pragma unroll
-        for (int t = 0; t < R; ++t)
-          sraw[t] = __builtin_amdgcn_raw_buffer_load_b128(sres, slane + 16 * t * (int)srow, 64 * (c >> 2), 0);
-      }
-#pragma unroll
-      for (int t = 0; t < R; ++t)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          wr[decltype(SLOT)::value][t][j] = __builtin_amdgcn_raw_buffer_load_b128(
-              wres, wlane + (16 * t + 8 * j) * (int)prow, 128 * c, kCachePolicyNT);
-    };
-    // x panel P into buffer P % 2: copy i of this wavefront fills panel bytes [1 KiB (i NW + wave), + 1 KiB)
-    auto x_copy = [&](int P) {
-      uint8_t* const buf = xs[P & 1];
-#pragma unroll
-      for (int i = 0; i < G::xcopies; ++i) {
-        const int off = 1024 * (i * NW + wave) + 16 * lane;
-        const int m = off / (2 * G::pk), slot = (off % (2 * G::pk)) >> 4;
-        const int piece = slot ^ (m & 7);
-        __builtin_amdgcn_global_load_lds((const void*)(x + (int64_t)min(m, M - 1) * K + P * G::pk + 8 * piece),
-                                         (lds_ptr_t)(buf + 1024 * (i * NW + wave)), 16, 0, 0);
-      }
-    };
-
-    // one chunk; U = c % 4 (the loop below steps c by 4)
-    auto step = [&](int c, auto U_) {
-      constexpr int u = decltype(U_)::value;
-      constexpr int cc = u % G::pchunks;                 // chunk within its panel
-      const int P = c / G::pchunks;
-      // wait for batch(c) (and, at a panel start, this wavefront's copies of panel P):
-      // everything issued after it may stay in flight
-      constexpr int nnext = kBatchW + (((u + 1) & 3) == 0 ? R : 0);   // size of batch(c + 1)
-      const bool has_next = c + 1 < nchunks;
-      const bool x_after = (G::pchunks >= 2 && cc == 1) && (P + 1 < npanels);   // copies of P + 1 follow batch(c)
-      if (has_next) {
-        if (x_after) wait_vmcnt<nnext + G::xcopies>();
-        else wait_vmcnt<nnext>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      if constexpr (cc == 0) {
-        ring_barrier();                                   // panel P is complete; panel P - 1 is no longer read
-        if (P + 1 < npanels) x_copy(P + 1);
-      }
-      // chunk c: registers -> this wavefront's LDS, then refill the slot with batch(c + 2)
-#pragma unroll
-      for (int t = 0; t < R; ++t)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          *reinterpret_cast<u32x4*>(wmine + 2048 * t + 1024 * j + wwr) = wr[u & 1][t][j];
-      if (c + 2 < nchunks) issue(c + 2, Ic<u & 1>{}, std::integral_constant<bool, ((u + 2) & 3) == 0>{});
-      if constexpr (u == 0) {
-        // the group's scales as loaded (lane (r, g): row r, chunk g) into this wavefront's region
-#pragma unroll
-        for (int t = 0; t < R; ++t) *reinterpret_cast<u32x4*>(smine + 1024 * t + 16 * lane) = sraw[t];
-      }
-      uint32_t sw[R];
-#pragma unroll
-      for (int t = 0; t < R; ++t) sw[t] = *reinterpret_cast<const uint32_t*>(smine + 1024 * t + 256 * u + srd);
-      const uint8_t* const xb = xs[P & 1] + r * (2 * G::pk) + 16 * (32 * cc + 8 * g);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {                       // the two 16-byte halves of each tile's operand
-        u32x4 wd[R];
-#pragma unroll
-        for (int t = 0; t < R; ++t) wd[t] = *reinterpret_cast<const u32x4*>(wmine + 2048 * t + (h ? wrd1 : wrd0));
-#pragma unroll
-        for (int s = 4 * h; s < 4 * h + 4; ++s) {
-          bf16x8 bx[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            bx[mt] = *reinterpret_cast<const bf16x8*>(xb + mt * 16 * (2 * G::pk) + 16 * (s ^ (r & 7)));
-#pragma unroll
-          for (int t = 0; t < R; ++t) {
-            const float sv = (s >> 1) == 0 ? NVFP4_E4M3_TO_F32(sw[t], 0) : (s >> 1) == 1 ? NVFP4_E4M3_TO_F32(sw[t], 1)
-                           : (s >> 1) == 2 ? NVFP4_E4M3_TO_F32(sw[t], 2) : NVFP4_E4M3_TO_F32(sw[t], 3);
-            const bf16x8 a = dequant8(wd[t][s & 3], sv);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[mt], acc[t][mt]);
-          }
-          // keep later steps' operand reads from being hoisted here (register pressure at MT = 4)
-          if constexpr (MT >= 4) __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-
-    x_copy(0);
-    issue(0, Ic<0>{}, std::true_type{});
-    issue(1, Ic<1>{}, std::false_type{});
-    for (int c = 0; c < nchunks; c += 4) {
-      step(c, Ic<0>{});
-      step(c + 1, Ic<1>{});
-      step(c + 2, Ic<2>{});
-      step(c + 3, Ic<3>{});
-    }
-
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      const int n0 = n_wave + 16 * t + 4 * g;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + r;
-        if (m >= M) continue;
-        uint16_t* yrow = y + (int64_t)m * N;
-        if ((N & 3) == 0 && n0 + 3 < N) {
-          const uint32_t lo = out_bf16(acc[t][mt][0], gs, bias, n0) | (out_bf16(acc[t][mt][1], gs, bias, n0 + 1) << 16);
-          const uint32_t hi = out_bf16(acc[t][mt][2], gs, bias, n0 + 2) | (out_bf16(acc[t][mt][3], gs, bias, n0 + 3) << 16);
-          *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(acc[t][mt][v], gs, bias, n0 + v);
-        }
-      }
-    }
-    __syncthreads();                                    // the x buffers are reused by the next block
-  }
-}
-
-// ---------------------------------------------------------------------------
 // gemv_mfma_ragged_kernel<MT>: the same MFMA arithmetic for K % 256 != 0,
 // where rows are not whole 128-byte lines.  One wavefront per 16 rows, the x
 // chunk staged in LDS per workgroup, and per-block 8-byte weight loads from
@@ -1435,23 +1199,12 @@ hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int
 #undef NVFP4_MOE_PANEL
 }
 
-template <int MT, int R>
-static hipError_t ring_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
-                              const float* gs, int N, const void* bias, void* y, hipStream_t stream) {
-  const void* fn = (const void*)gemv_ring_kernel<MT, R>;
-  const int nblocks = (N + kRingNW * R * 16 - 1) / (kRingNW * R * 16);
-  const int dev = current_device();
-  const dim3 grid(std::min(nblocks, device_cus(dev) * blocks_per_cu(fn, dev, 64 * kRingNW, 0)));
-  return launch_kernel(fn, grid, dim3(64 * kRingNW), stream, (const uint16_t*)x, M, K, packed, scales, gs, N,
-                       (const uint16_t*)bias, (uint16_t*)y);
-}
-
 // x-resident configuration for (M, K): 10 * wavefronts + pipeline depth (2
 // or 3 regions, K % 1024 == 0; 0 for the single-region form), or 0 to leave
 // (M, K) to the streaming kernels.  Measured on the 8B shape (K = 4096): 8
 // wavefronts with two regions are fastest up to M = 8 (three regions are no
-// faster), 16 beyond; when only 8 single-region wavefronts fit,
-// gemv_ring_kernel (K % 1024 == 0) is faster (M = 16: 58 vs 67 us).
+// faster), 16 beyond; when only 8 single-region wavefronts fit and K %
+// 1024 == 0, the panel kernel is faster (M = 16: 58-60 vs 67 us).
 static int xres_config(int64_t M, int64_t K) {
   if (M < 3 || M > 16 || K % kChunk != 0) return 0;
   const bool deep = K % (4 * kChunk) == 0;
@@ -1480,14 +1233,6 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     case 160: return xres_launch<16, 0>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 80: return xres_launch<8, 0>(x, M, K, packed, scales, gs, N, bias, y, stream);
     default: break;
-  }
-  if (K % 1024 == 0) {
-    switch ((M + 15) / 16) {
-      case 1: return ring_launch<1, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
-      case 2: return ring_launch<2, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
-      case 3: return ring_launch<3, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
-      default: return ring_launch<4, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    }
   }
   if (K % 512 == 0) {
     switch ((M + 15) / 16) {
