@@ -787,9 +787,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
   uint8_t* const smine = sl[wave];
 
   for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x)
-  for (int m_pass = 0; m_pass < m_all; m_pass += 16 * MT) {
-    M = min(16 * MT, m_all - m_pass);
-    first = first_all + m_pass;
+  for (int m_pass = 0; m_pass < (kMoe ? m_all : 1); m_pass += 16 * MT) {
+    if constexpr (kMoe) {
+      M = min(16 * MT, m_all - m_pass);
+      first = first_all + m_pass;
+    }
     const int n_wave = blk * (NW * kRows) + wave * kRows;
     auto w_copy = [&](int c) {
 #pragma unroll
