@@ -760,7 +760,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
     // the widest panel that a pass over the expert's rows (at most 16 MT) fits
     pk = min(K, (kPanelXBytes / min(M, 16 * MT) / 2) / 512 * 512);
   }
-  // expert layer: more than 16 MT pairs are taken in passes of 16 MT rows over each weight block
+  // expert layer (MT <= 2): more than 16 MT pairs are taken in passes of 16 MT rows over each weight block
   const int m_all = M;
   const int64_t first_all = first;
   static_assert(kPanelXBytes >= 16 * MT * 512 * 2, "a panel must hold 512 columns of 16 MT rows");
@@ -786,9 +786,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
   uint8_t* const wmine = wl[wave];
   uint8_t* const smine = sl[wave];
 
+  constexpr bool kPasses = kMoe && MT <= 2;             // the 64-row form takes at most 64 pairs (one pass)
   for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x)
-  for (int m_pass = 0; m_pass < (kMoe ? m_all : 1); m_pass += 16 * MT) {
-    if constexpr (kMoe) {
+  for (int m_pass = 0; m_pass < (kPasses ? m_all : 1); m_pass += 16 * MT) {
+    if constexpr (kPasses) {
       M = min(16 * MT, m_all - m_pass);
       first = first_all + m_pass;
     }
@@ -1004,8 +1005,9 @@ static hipError_t dot_dispatch(const void* x, int M, int K, const uint8_t* packe
   switch ((K + 2047) / 2048) {
     case 1: return dot_launch<MR, 1>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 2: return dot_launch<MR, 2>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    case 3: return dot_launch<MR, 3>(x, M, K, packed, scales, gs, N, bias, y, stream);
-    default: return dot_launch<MR, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    // two rows only reach here with K <= 4096 (decode_uses_dot)
+    case 3: return dot_launch<1, 3>(x, M, K, packed, scales, gs, N, bias, y, stream);
+    default: return dot_launch<1, 4>(x, M, K, packed, scales, gs, N, bias, y, stream);
   }
 }
 
@@ -1168,6 +1170,7 @@ static hipError_t moe_panel_launch(const void* x, int row_div, int K, const int3
                                    int mmin, int mcap, int64_t P, const uint8_t* packed, const uint8_t* scales,
                                    const float* gs, int E, int N, void* y, bool zero_rows, hipStream_t stream) {
   const void* fn = (const void*)gemv_panel_kernel<MT, 8, R, true>;
+  if (MT > 2) mcap = std::min(mcap, 16 * MT);          // the 64-row form runs one pass
   const int dev = current_device();
   const int cus = device_cus(dev), per_cu = blocks_per_cu(fn, dev, 64 * 8, 0);
   // at most P / mmin experts fall in the class: give each twice the workgroups

@@ -158,9 +158,9 @@ hipError_t launch_moe_xres(const void* x, int64_t row_div, int64_t K, const int3
                            const MoeXresPlan& plan, int64_t P, const uint8_t* packed, const uint8_t* scales,
                            const float* gs, int64_t E, int64_t N, void* y, hipStream_t stream);
 // The panel decode kernel over the experts with mmin..mcap pairs, `rows`
-// (16, 32 or 64) activation rows per pass over an expert's weights (experts
-// with more pairs take several passes); K % 512 == 0, otherwise nothing is
-// launched.  With zero_rows it also writes the zero rows of the pairs whose
+// (16, 32 or 64) activation rows per pass over an expert's weights (at 16 or
+// 32, experts with more pairs take several passes; at 64, mcap is at most
+// 64); K % 512 == 0, otherwise nothing is launched.  With zero_rows it also writes the zero rows of the pairs whose
 // id is outside [0, E).
 hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int32_t* offsets, const int32_t* order,
                             int mmin, int mcap, int rows, int64_t P, const uint8_t* packed, const uint8_t* scales,
