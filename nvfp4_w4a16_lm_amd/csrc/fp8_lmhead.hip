@@ -778,7 +778,8 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_
     if (M == 1) return fp8_dot_dispatch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     return fp8_dot_dispatch<2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
   }
-  if (K % 512 == 0 && M >= 3 && M <= 64) {
+  // (the ring kernel's buffer offsets within a wavefront's 64 rows are 32-bit)
+  if (K % 512 == 0 && K <= (1 << 24) && M >= 3 && M <= 64) {
     if (M <= 16) return fp8_ring_launch<1, 4>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     if (M <= 32) return fp8_ring_launch<2, 2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     return fp8_ring_launch<4, 2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
