@@ -124,8 +124,11 @@ class TimingEvent:
         return float(ms.value)
 
     def __del__(self):
-        if getattr(self, "_h", None) is not None and self._h.value and TimingEvent._hip is not None:
-            TimingEvent._hip.hipEventDestroy(self._h)
+        # through the instance's class: at interpreter shutdown the module's
+        # globals (this class's name included) may already be None
+        hip = getattr(type(self), "_hip", None)
+        if getattr(self, "_h", None) is not None and self._h.value and hip is not None:
+            hip.hipEventDestroy(self._h)
             self._h = None
 
 
