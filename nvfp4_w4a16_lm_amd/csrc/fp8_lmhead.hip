@@ -781,7 +781,9 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_
   // (the ring kernel's buffer offsets within a wavefront's 64 rows are 32-bit)
   if (K % 512 == 0 && K <= (1 << 24) && M >= 3 && M <= 64) {
     if (M <= 16) return fp8_ring_launch<1, 4>(xq, xs, m, k, wq, ws, n, bias, y, stream);
-    if (M <= 32) return fp8_ring_launch<2, 2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+    // four tiles per wavefront up to 32 rows (two more weight chunks in
+    // flight per wavefront); at 64 rows four would spill, so two
+    if (M <= 32) return fp8_ring_launch<2, 4>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     return fp8_ring_launch<4, 2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
   }
   switch (std::min<int64_t>((M + 15) / 16, 8)) {
