@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void fp8_prefill_kernel(const uint8_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// fp8_ring_kernel<MT, R>: 3 <= M <= 16 MT activation rows (MT = 1, 2, 4),
+// fp8_ring_kernel<MT, R>: 1 <= M <= 16 MT activation rows (MT = 1, 2, 4),
 // K % 512 == 0.  Weights stream through registers, with e4m3 operands and
 // nothing to dequantize:
 //  * a workgroup of 8 wavefronts owns blocks of 128 R weight rows, R tiles of
@@ -778,8 +778,11 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_
     if (M == 1) return fp8_dot_dispatch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     return fp8_dot_dispatch<2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
   }
-  // (the ring kernel's buffer offsets within a wavefront's 64 rows are 32-bit)
-  if (K % 512 == 0 && K <= (1 << 24) && M >= 3 && M <= 64) {
+  // any other M <= 64 with K % 512 == 0: the register-ring kernel (at one
+  // row with K = 8192, 222 against the slab kernel's 241 us; the dot kernel
+  // stays ahead where it applies: 95 against 115 us at K = 4096).  The ring
+  // kernel's buffer offsets within a wavefront's 64 rows are 32-bit.
+  if (K % 512 == 0 && K <= (1 << 24) && M <= 64) {
     if (M <= 16) return fp8_ring_launch<1, 4>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     // four tiles per wavefront up to 32 rows (two more weight chunks in
     // flight per wavefront); at 64 rows four would spill, so two

@@ -79,12 +79,14 @@ def test_gemm_matches_oracle(m, n, k):
     check_fp8_gemm(host_bits(y), xq, xs, wq, ws, label=f"M={m} N={n} K={k}")
 
 
-@pytest.mark.parametrize("m,n,k,with_bias", [(3, 140000, 512, True), (20, 70000, 512, False), (28, 140000, 512, True),
+@pytest.mark.parametrize("m,n,k,with_bias", [(1, 3000, 8192, True), (2, 2100, 8192, False),
+                                             (3, 140000, 512, True), (20, 70000, 512, False), (28, 140000, 512, True),
                                              (16, 1300, 8192, False), (24, 1030, 8192, True), (40, 2100, 1024, False),
                                              (40, 70000, 512, True), (64, 900, 8192, True)])
 def test_ring_kernel_panels_blocks_and_bias(m, n, k, with_bias):
-    """3 <= M <= 64 with K % 512 == 0 runs the register-ring kernel: several x
-    panels per block at K = 8192 (4 at M <= 16, 8 at M <= 32, 16 beyond),
+    """M <= 64 with K % 512 == 0 runs the register-ring kernel (at M = 1, 2
+    beyond the dot kernel's K): several x panels per block at K = 8192 (4 at
+    M <= 16, 8 at M <= 32, 16 beyond),
     more 512-row (M <= 32) or 256-row (M > 32) blocks than compute units at
     N = 140000 / 70000, rows past N and M in the last tiles, and the bias."""
     w = wl.random_weight_bits(n, k, sigma=0.02, seed=n + 3 * k)
