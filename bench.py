@@ -50,16 +50,19 @@ def gemm_flops(m: int, n: int, k: int) -> float:
 
 
 def decode_kernel_name(m: int, k: int) -> str:
-    """Which decode kernel the library dispatches for (M, K) (mirrors its dispatch rule)."""
+    """Which decode kernel the library dispatches for (M, K) (mirrors its
+    dispatch rule, for N up to 262144)."""
     if k % 32 == 0 and ((m == 1 and k <= 8192) or (m == 2 and k <= 4096)):
         return "gemv_dot_kernel"
     if k % 256 != 0:
         return "gemv_mfma_ragged_kernel"
     if 3 <= m <= 16:
-        fits = lambda nw, depth: m * (2 * k + 16) + nw * (2048 * max(depth, 1) + 1024) + 64 <= 160 * 1024
+        fits = lambda cols, nw, depth: m * (2 * cols + 16) + nw * (2048 * max(depth, 1) + 1024) + 64 <= 160 * 1024
         deep = k % 1024 == 0
-        if (deep and (fits(8, 2) or fits(16, 2))) or fits(16, 0) or (not deep and fits(8, 0)):
+        if (deep and (fits(k, 8, 2) or fits(k, 16, 2))) or fits(k, 16, 0) or (not deep and fits(k, 8, 0)):
             return "gemv_xres_kernel"
+        if any(k % np_ == 0 and (k // np_) % 1024 == 0 and fits(k // np_, 16, 2) for np_ in (2, 4, 8)):
+            return "gemv_xphase_kernel"
     return "gemv_panel_kernel" if k % 512 == 0 else "gemv_mfma_kernel"
 
 

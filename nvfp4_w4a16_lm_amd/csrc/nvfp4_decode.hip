@@ -21,6 +21,10 @@
 // registers (code * scale is exact in either type):
 // gemv_xres_kernel (3 <= M <= 16 when x fits in LDS): x resident in LDS as
 //   f16 rows scaled by a power of two, weights copied straight to LDS.
+// gemv_xphase_kernel (3 <= M <= 16 when x does not fit in LDS whole but a
+//   range of K / 2, K / 4 or K / 8 columns of it, a multiple of 1024, does):
+//   the same with x held one column range at a time and every wavefront's
+//   tiles accumulated in registers across the ranges.
 // gemv_panel_kernel (other M <= 64, K % 512 == 0): weights copied straight
 //   to per-wavefront LDS one chunk ahead, x in LDS panels.
 // gemv_mfma_kernel (K % 256 == 0) and gemv_mfma_ragged_kernel (any K % 16
@@ -707,6 +711,218 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
+// gemv_xphase_kernel<NW, TW>: 2 < M <= 16 when the activation does not fit in
+// LDS whole but one of its column ranges of kp columns (a phase) does;
+// K % kp == 0, kp % 1024 == 0.  The arithmetic, LDS layouts and two-region
+// copy pipeline of gemv_xres_kernel, with K walked phase by phase:
+//  * wavefront w of workgroup b owns tiles b NW + w + i NW gridDim (i < TW)
+//    and keeps the accumulators of all of them in registers;
+//  * in phase q it streams chunks q cpp .. q cpp + cpp - 1 (cpp = kp / 256)
+//    of each of its tiles in turn; chunk copies run two chunks ahead of its
+//    sequence across tile and phase boundaries;
+//  * before each phase the workgroup converts that phase's columns of x into
+//    LDS (f16, scaled by the 2^-p_m taken from the whole row), between two
+//    barriers.
+// ---------------------------------------------------------------------------
+template <int NW, int TW, int D>
+__global__ __launch_bounds__(64 * NW) void gemv_xphase_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                            const uint8_t* __restrict__ packed,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ gs_ptr, int N,
+                                                            const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ y, int kp) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  static_assert(D == 2 || D == 3, "two or three chunk regions per wavefront");
+  constexpr int kRowsPerWave = (16 + NW - 1) / NW;  // x rows each wavefront converts
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int xpitch = 2 * kp + 16;                   // bytes per x row of a phase
+  uint8_t* const xl = lds;
+  uint8_t* const wmine = lds + M * xpitch + 2048 * D * wave;
+  uint8_t* const smine = lds + M * xpitch + 2048 * D * NW + 1024 * wave;   // 16 rows x 64 B of scales
+  float* const xup = reinterpret_cast<float*>(lds + M * xpitch + (2048 * D + 1024) * NW);   // 2^p_m
+  const int r = lane & 15, g = lane >> 4;
+  const int cpp = kp / kChunk;                      // chunks per phase, a multiple of 4
+  const int nphases = K / kp;
+  const int64_t prow = K >> 1, srow = K >> 4;
+  const int wpiece = (lane & 7) ^ (lane >> 3), spiece = (lane & 3) ^ ((lane >> 3) & 3);
+  const int wrd0 = r * 128 + 16 * ((2 * g) ^ (r & 7)), wrd1 = r * 128 + 16 * ((2 * g + 1) ^ (r & 7));
+  const int srd = r * 64 + 4 * g, skey = (r >> 1) & 3;
+  const int ntiles = (N + 15) / 16;
+  const int stride = gridDim.x * NW;
+  const int tile0 = blockIdx.x * NW + wave;
+  const int nt = tile0 < ntiles ? min(TW, (ntiles - 1 - tile0) / stride + 1) : 0;   // this wavefront's tiles
+
+  // copies of the chunk at sequence position (phase q, tile i, chunk cc of
+  // the phase) into region `slot`, with its scale group when `with_scales`;
+  // positions past the end copy the last chunk again (never read)
+  auto copy_pos = [&](int q, int i, int cc, int slot, bool with_scales) __attribute__((always_inline)) {
+    if (q >= nphases) {
+      q = nphases - 1;
+      i = nt - 1;
+      cc = cpp - 1;
+    }
+    const int t = tile0 + i * stride;
+    const int c = q * cpp + cc;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t row = min(16 * t + 8 * j + (lane >> 3), N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(packed + row * prow + 128 * c + 16 * wpiece),
+                                       (lds_ptr_t)(wmine + 2048 * slot + 1024 * j), 16, 0, kCachePolicyNT);
+    }
+    if (with_scales) {
+      const int64_t row = min(16 * t + (lane >> 2), N - 1);
+      const int64_t off = min((int64_t)16 * (kScaleGroup * (c / kScaleGroup) + spiece), srow - 16);
+      __builtin_amdgcn_global_load_lds((const void*)(scales + row * srow + off), (lds_ptr_t)smine, 16, 0, 0);
+    }
+  };
+  // the position D chunks ahead of the current one, advanced once per chunk
+  int qa = 0, ia = 0, ca = 0;
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (++ca == cpp) {
+      ca = 0;
+      if (++ia == nt) {
+        ia = 0;
+        ++qa;
+      }
+    }
+  };
+  if (nt > 0) {                                     // the first D chunks fly while x is read
+#pragma unroll
+    for (int c = 0; c < D; ++c) copy_pos(0, 0, c, c, c == 0);
+    ca = D;
+  }
+
+  // row scales from the whole row (bf16 magnitudes compare as integers):
+  // wavefront w takes rows w, w + NW, ...
+  float down[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int m = wave + NW * j;
+    down[j] = 1.0f;
+    if (m < M) {
+      const uint16_t* xr = x + (int64_t)m * K;
+      uint32_t mx = 0;
+      for (int kv = lane; kv < K / 8; kv += 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * kv);
+        mx = pk_max_u16(mx, pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
+                                       pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu)));
+      }
+      mx = max(mx & 0xFFFFu, mx >> 16);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+      const int p = (mx == 0u) ? 0 : max(-126, (int)(mx >> 7) - 141);   // biased exponent - 127 - 14
+      down[j] = __uint_as_float((uint32_t)(127 - p) << 23);
+      if (lane == 0) xup[m] = __uint_as_float((uint32_t)(127 + p) << 23);
+    }
+  }
+
+  const uint8_t* const xrow = xl + min(r, M - 1) * xpitch + 128 * g;   // this lane's k-group, chunk 0 of a phase
+  f32x4 acc[TW][2];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t swg[4];
+  int slot = 0;
+  // one chunk (cc % 4 == P) of the current tile: wait for its copies (those
+  // of the next D - 1 chunks, and the next scale group when its copy went out
+  // after them, may stay in flight), read it, refill the region with the
+  // chunk D ahead (with its scale group when that chunk starts one, i.e. at
+  // P == ps), then 8 MFMAs
+  auto step = [&](auto P, int cc, f32x4 (&a)[2]) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    constexpr int ps = (4 - D) % 4;
+    constexpr bool s_between = ((p - ps + 4) % 4) >= 1 && ((p - ps + 4) % 4) <= D - 1;
+    constexpr int vm = 2 * (D - 1) + (s_between ? 1 : 0);
+    __builtin_amdgcn_s_waitcnt((vm & 15) | 0x0F70);
+    uint8_t* const wreg = wmine + 2048 * slot;
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(wreg + wrd0);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(wreg + wrd1);
+    if (p == 0) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) swg[b] = *reinterpret_cast<const uint32_t*>(smine + srd + 16 * (b ^ skey));
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // the region (and the scales) may now be refilled
+    copy_pos(qa, ia, ca, slot, p == ps);
+    advance();
+    slot = (slot + 1 == D) ? 0 : slot + 1;
+    const uint32_t sw = swg[p];
+    float sb[4];
+    f16x2 mu[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sb[b] = b == 0 ? NVFP4_E4M3_TO_F32(sw, 0) : b == 1 ? NVFP4_E4M3_TO_F32(sw, 1)
+            : b == 2 ? NVFP4_E4M3_TO_F32(sw, 2) : NVFP4_E4M3_TO_F32(sw, 3);
+      mu[b] = scale_mantissa_f16(sb[b]);
+    }
+    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint8_t* const xc = xrow + 2 * kChunk * cc;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
+      a[s & 1] = mfma16x16x32_f16(dequant8_f16(wd[s], sb[s >> 1], mu[s >> 1]), bx, a[s & 1]);
+    }
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+
+  for (int q = 0; q < nphases; ++q) {
+    __syncthreads();                                // phase q - 1's x is no longer read
+    // phase q's columns of x -> f16 rows x * 2^-p_m
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int m = wave + NW * j;
+      if (m < M) {
+        const uint16_t* xr = x + (int64_t)m * K + (int64_t)q * kp;
+        for (int kv = lane; kv < kp / 8; kv += 64) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * kv);
+          u32x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f16x2 pair = {(_Float16)(bf16_lo(v[e]) * down[j]), (_Float16)(bf16_hi(v[e]) * down[j])};
+            h[e] = __builtin_bit_cast(uint32_t, pair);
+          }
+          *reinterpret_cast<u32x4*>(xl + m * xpitch + 16 * kv) = h;
+        }
+      }
+    }
+    __syncthreads();                                // phase q's x is in LDS
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      if (i < nt) {
+        for (int cc = 0; cc < cpp; cc += 4) {
+          step(P0{}, cc, acc[i]);
+          step(P1{}, cc + 1, acc[i]);
+          step(P2{}, cc + 2, acc[i]);
+          step(P3{}, cc + 3, acc[i]);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);            // the trailing copies land before the workgroup ends
+
+  const float gs = *gs_ptr;
+  const float up = xup[min(r, M - 1)];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) {
+    if (i < nt && r < M) {
+      const f32x4 tot = (acc[i][0] + acc[i][1]) * up;
+      const int n0 = (tile0 + i * stride) * 16 + 4 * g;
+      uint16_t* yrow = y + (int64_t)r * N;
+      if ((N & 3) == 0 && n0 + 3 < N) {
+        const uint32_t lo = out_bf16(tot[0], gs, bias, n0) | (out_bf16(tot[1], gs, bias, n0 + 1) << 16);
+        const uint32_t hi = out_bf16(tot[2], gs, bias, n0 + 2) | (out_bf16(tot[3], gs, bias, n0 + 3) << 16);
+        *reinterpret_cast<uint2*>(yrow + n0) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n0 + v < N) yrow[n0 + v] = (uint16_t)out_bf16(tot[v], gs, bias, n0 + v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // gemv_panel_kernel<MT, NW, R>: 2 < M <= 64 when the activation does not fit
 // in LDS whole; K % 512 == 0.  A workgroup of NW wavefronts owns blocks of
 // 16 NW R weight rows (R tiles of 16 rows per wavefront; 8 x 4 is used: two
@@ -1204,6 +1420,64 @@ hipError_t launch_moe_panel(const void* x, int64_t row_div, int64_t K, const int
 #undef NVFP4_MOE_PANEL
 }
 
+// Dynamic LDS of gemv_xphase_kernel<NW, TW> for M rows and phases of kp
+// columns: x rows, two weight regions and a scale region per wavefront, 16
+// row scales.
+static int64_t xphase_lds_bytes(int64_t M, int64_t kp, int nw, int depth) {
+  return M * (2 * kp + 16) + (int64_t)nw * (depth * 2048 + 1024) + 16 * sizeof(float);
+}
+
+// Phase width for the phased x-resident kernel (16 wavefronts, two regions
+// each): K / 2, K / 4 or K / 8, the widest whose x rows fit in LDS beside the
+// regions and that is a multiple of 1024 columns, or 0.  Measured against
+// the panel kernel (random codes, one box): 8B shape M = 16 55.7 against
+// 61.4 us; 70B shape M = 8 / 12 / 16 120.5 / 117.4 / 118.2 against 126.0 /
+// 121.4 / 120.9 us.  Eight wavefronts (two or three regions) and sixteen
+// with three regions were slower or no faster.
+constexpr int kXphaseNW = 16, kXphaseDepth = 2;
+static int64_t xphase_kp(int64_t M, int64_t K) {
+  if (M < 3 || M > 16) return 0;
+  for (int64_t np = 2; np <= 8; np *= 2)
+    if (K % np == 0 && (K / np) % 1024 == 0 && xphase_lds_bytes(M, K / np, kXphaseNW, kXphaseDepth) <= kXresLdsMax)
+      return K / np;
+  return 0;
+}
+
+template <int NW, int TW, int D>
+static hipError_t xphase_launch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
+                                const float* gs, int N, const void* bias, void* y, int kp, int grid,
+                                hipStream_t stream) {
+  const void* fn = (const void*)gemv_xphase_kernel<NW, TW, D>;
+  const hipError_t e = ensure_dynamic_lds(fn, current_device(), kXresLdsMax);
+  if (e != hipSuccess) return e;
+  return launch_kernel_lds(fn, dim3(grid), dim3(64 * NW), (size_t)xphase_lds_bytes(M, kp, NW, D), stream,
+                           (const uint16_t*)x, M, K, packed, scales, gs, N, (const uint16_t*)bias, (uint16_t*)y, kp);
+}
+
+// One workgroup per resident slot (at most one per NW tiles), each
+// wavefront taking up to TW = 1, 2 or 4 tiles; `grid` and `tw` give the
+// plan, or tw = 0 when more than 4 tiles per wavefront would be needed
+// (N > 262144 on 256 compute units: left to the panel kernel).
+static void xphase_plan(int M, int kp, int N, int* grid, int* tw) {
+  const int dev = current_device();
+  const void* fn = (const void*)gemv_xphase_kernel<kXphaseNW, 4, kXphaseDepth>;   // every TW takes the same LDS
+  const int ntiles = (N + 15) / 16;
+  const int resident = device_cus(dev) *
+                       blocks_per_cu(fn, dev, 64 * kXphaseNW, (size_t)xphase_lds_bytes(M, kp, kXphaseNW, kXphaseDepth));
+  *grid = std::max(1, std::min((ntiles + kXphaseNW - 1) / kXphaseNW, resident));
+  *tw = (ntiles + *grid * kXphaseNW - 1) / (*grid * kXphaseNW);
+  if (*tw > 4) *tw = 0;
+}
+
+static hipError_t xphase_dispatch(const void* x, int M, int K, const uint8_t* packed, const uint8_t* scales,
+                                  const float* gs, int N, const void* bias, void* y, int kp, int grid, int tw,
+                                  hipStream_t stream) {
+  constexpr int NW = kXphaseNW, D = kXphaseDepth;
+  if (tw <= 1) return xphase_launch<NW, 1, D>(x, M, K, packed, scales, gs, N, bias, y, kp, grid, stream);
+  if (tw <= 2) return xphase_launch<NW, 2, D>(x, M, K, packed, scales, gs, N, bias, y, kp, grid, stream);
+  return xphase_launch<NW, 4, D>(x, M, K, packed, scales, gs, N, bias, y, kp, grid, stream);
+}
+
 // x-resident configuration for (M, K): 10 * wavefronts + pipeline depth (2
 // or 3 regions, K % 1024 == 0; 0 for the single-region form), or 0 to leave
 // (M, K) to the streaming kernels.  Measured on the 8B shape (K = 4096): 8
@@ -1238,6 +1512,11 @@ hipError_t launch_gemv(const void* x, int64_t M64, int64_t K64, const uint8_t* p
     case 160: return xres_launch<16, 0>(x, M, K, packed, scales, gs, N, bias, y, stream);
     case 80: return xres_launch<8, 0>(x, M, K, packed, scales, gs, N, bias, y, stream);
     default: break;
+  }
+  if (const int64_t kp = xphase_kp(M, K)) {
+    int grid = 0, tw = 0;
+    xphase_plan(M, (int)kp, N, &grid, &tw);
+    if (tw > 0) return xphase_dispatch(x, M, K, packed, scales, gs, N, bias, y, (int)kp, grid, tw, stream);
   }
   if (K % 512 == 0) {
     switch ((M + 15) / 16) {

@@ -49,8 +49,10 @@ def test_shapes(m, n, k):
 
 
 # M <= 16 with x too large for LDS (and M <= 2 past the dot kernel's K): the
-# panel kernel, several 512-row blocks with a ragged last one, K of 20 and
-# 32 K columns, bias on one row count
+# panel kernel, or the phased x-resident kernel where a phase of x fits (M =
+# 5 at K = 16384: two phases; M = 16 at K = 16384: eight), several 512-row
+# blocks with a ragged last one, K of 20 and 32 K columns, bias on one row
+# count
 @pytest.mark.parametrize("m", [1, 2, 5, 12, 16])
 @pytest.mark.parametrize("n,k", [(1100, 16384), (700, 10240)])
 def test_decode_panel_rows_up_to_16(m, n, k):
@@ -59,6 +61,25 @@ def test_decode_panel_rows_up_to_16(m, n, k):
     bias = wl.bias_bits(n, seed=m, sigma=0.5) if m == 12 else None
     y = gemm_gpu(x, q, bias)
     check_gemm(y, x, packed, scales, gs, bias_bits=bias, label=f"panel m={m} n={n} k={k}")
+
+
+# 3 <= M <= 16 with x too large for LDS whole but K a multiple of 2048: the
+# phased x-resident kernel (x held one column range at a time, 16
+# wavefronts).  Two phases at K = 4096, four at K = 8192; up to 2 tiles per
+# wavefront at N = 70000, up to 4 (3 used) at N = 131100, one at N = 40000,
+# wavefronts without tiles at N = 3001; bias
+@pytest.mark.parametrize("m,n,k,with_bias", [(15, 131100, 4096, False), (16, 70000, 4096, True),
+                                             (16, 40000, 8192, True), (9, 3001, 8192, False),
+                                             (16, 3001, 4096, True)])
+def test_decode_x_in_phases(m, n, k, with_bias):
+    w = wl.random_weight_bits(n, k, sigma=0.02, seed=m + 3)
+    gs = O.global_scale(O.weight_amax(w))
+    packed, scales = oracle_quantize_threaded(w, gs)
+    q = upload_quant(packed, scales, gs)
+    x = wl.random_activation_bits(m, k, seed=n + 5)
+    bias = wl.bias_bits(n, seed=m, sigma=0.5) if with_bias else None
+    y = gemm_gpu(x, q, bias)
+    check_gemm(y, x, packed, scales, gs, bias_bits=bias, label=f"phases m={m} n={n} k={k}")
 
 
 # decode with more 512-row blocks than the GPU has compute units, so that
@@ -200,8 +221,9 @@ def test_decode_activation_rows_of_extreme_magnitude(m, k):
     a mix of 2^20 and 2^-20 within one row, one huge element among tiny ones,
     and rows whose largest elements come only in the last (or only in the
     first) columns.  M = 8 keeps x resident in LDS (f16 products with a
-    per-row exponent); M = 40 (two 512-column panels) and M = 16 at K = 8192
-    (four 2048-column panels) take the panel kernel."""
+    per-row exponent); M = 16 at K = 8192 holds it in four 2048-column
+    phases with the exponent taken from the whole row; M = 40 (two
+    512-column panels) takes the panel kernel."""
     n = 1027
     _, packed, scales, gs, q = setup(n, k, seed=12)
     rng = np.random.default_rng(13)
