@@ -120,12 +120,13 @@ nvfp4_status nvfp4_refresh_inplace(const void* W, int64_t N, int64_t K,
  * M <= 64 runs the streaming decode kernels, larger M the MFMA prefill kernel.
  *
  * Products: the prefill kernel and most decode kernels multiply the bf16
- * activations as given, so every product is exact in fp32.  The decode kernel
- * for 3 <= M <= 16 that holds the whole activation in LDS (K a multiple of
- * 256 and M * (2K + 16) bytes small enough) stages each activation row
- * m in f16 as x * 2^-p_m, with the power of two chosen from the row's largest
- * magnitude so that it lands in [2^14, 2^15), and multiply the f16 results by
- * 2^p_m in fp32.  An activation with |x| >= 2^-28 * max_k |x[m,k]| converts
+ * activations as given, so every product is exact in fp32.  The decode
+ * kernels for 3 <= M <= 16 that hold the activation in LDS, whole (K a
+ * multiple of 256 and M * (2K + 16) bytes small enough) or one range of K/2,
+ * K/4 or K/8 columns (a multiple of 1024) at a time, stage each activation
+ * row m in f16 as x * 2^-p_m, with the power of two chosen from the whole
+ * row's largest magnitude so that it lands in [2^14, 2^15), and multiply the
+ * f16 results by 2^p_m in fp32.  An activation with |x| >= 2^-28 * max_k |x[m,k]| converts
  * exactly (bf16's 8 significant bits fit f16's 11); a smaller one may move by
  * at most max(2^-39 * max_k |x[m,k]|, 2^-151), half the f16 subnormal spacing
  * at that scale.  Each y[m, n] may therefore differ from the exact-product
