@@ -487,10 +487,45 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
   }
 
   // x -> f16 rows in LDS: wavefront w handles rows w, w + NW, ...: the row's
-  // largest |x| (bf16 magnitudes compare as integers), then x * 2^-p_m
+  // largest |x| (bf16 magnitudes compare as integers), then x * 2^-p_m.  A
+  // row of at most 4096 values is read once, into registers; longer rows
+  // are read twice.
   const int xvec = K / 8;                           // 16-byte vectors per x row
+  constexpr int kXRegVec = 8;                       // 16-byte vectors per lane held in registers
   for (int m = wave; m < M; m += NW) {
     const uint16_t* xr = x + (kMoe ? (int64_t)(moe.order[first + m] / moe.row_div) : (int64_t)m) * K;
+    if (xvec <= 64 * kXRegVec) {
+      u32x4 v[kXRegVec];
+      uint32_t mx = 0;
+#pragma unroll
+      for (int j = 0; j < kXRegVec; ++j) {          // clamped, unconditional loads; vectors past the row are zero
+        const int kv = lane + 64 * j;
+        const u32x4 t = *reinterpret_cast<const u32x4*>(xr + 8 * min(kv, xvec - 1));
+        v[j] = kv < xvec ? t : u32x4{0u, 0u, 0u, 0u};
+        mx = pk_max_u16(mx, pk_max_u16(pk_max_u16(v[j].x & 0x7FFF7FFFu, v[j].y & 0x7FFF7FFFu),
+                                       pk_max_u16(v[j].z & 0x7FFF7FFFu, v[j].w & 0x7FFF7FFFu)));
+      }
+      mx = max(mx & 0xFFFFu, mx >> 16);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+      const int p = (mx == 0u) ? 0 : max(-126, (int)(mx >> 7) - 141);   // biased exponent - 127 - 14
+      const float down = __uint_as_float((uint32_t)(127 - p) << 23);
+      if (lane == 0) xup[m] = __uint_as_float((uint32_t)(127 + p) << 23);
+#pragma unroll
+      for (int j = 0; j < kXRegVec; ++j) {
+        const int kv = lane + 64 * j;
+        if (kv < xvec) {
+          u32x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f16x2 pair = {(_Float16)(bf16_lo(v[j][e]) * down), (_Float16)(bf16_hi(v[j][e]) * down)};
+            h[e] = __builtin_bit_cast(uint32_t, pair);
+          }
+          *reinterpret_cast<u32x4*>(xl + m * xpitch + 16 * kv) = h;
+        }
+      }
+      continue;
+    }
     uint32_t mx = 0;
     for (int kv = lane; kv < xvec; kv += 64) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * kv);
