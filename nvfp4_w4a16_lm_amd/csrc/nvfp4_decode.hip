@@ -1098,19 +1098,28 @@ __global__ __launch_bounds__(64 * NW) void gemv_panel_kernel(const uint16_t* __r
         w_copy(c + 1);
         if (c4 == kScaleGroup - 1) s_copy((c + 1) / kScaleGroup);
       }
+      // activation fragments one step ahead: step s + 1's LDS reads are in
+      // flight while step s's MFMAs issue
+      bf16x8 bx[2][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        bx[0][mt] = *reinterpret_cast<const bf16x8*>(xp + xrow[mt] + 512 * cc + 16 * (0 ^ xkey[mt]));
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        bf16x8 bx[MT];
+        if (s + 1 < 8) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          bx[mt] = *reinterpret_cast<const bf16x8*>(xp + xrow[mt] + 512 * cc + 16 * (s ^ xkey[mt]));
+          for (int mt = 0; mt < MT; ++mt)
+            bx[(s + 1) & 1][mt] =
+                *reinterpret_cast<const bf16x8*>(xp + xrow[mt] + 512 * cc + 16 * ((s + 1) ^ xkey[mt]));
+          __builtin_amdgcn_sched_barrier(0);           // keep them ahead of this step's MFMAs
+        }
 #pragma unroll
         for (int t = 0; t < kPanelR; ++t) {
           const float sv = (s >> 1) == 0 ? NVFP4_E4M3_TO_F32(sw[t], 0) : (s >> 1) == 1 ? NVFP4_E4M3_TO_F32(sw[t], 1)
                          : (s >> 1) == 2 ? NVFP4_E4M3_TO_F32(sw[t], 2) : NVFP4_E4M3_TO_F32(sw[t], 3);
           const bf16x8 a = dequant8(wd[t][s >> 2][s & 3], sv);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[mt], acc[t][mt]);
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(a, bx[s & 1][mt], acc[t][mt]);
         }
       }
     };
