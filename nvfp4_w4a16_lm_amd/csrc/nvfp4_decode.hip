@@ -585,11 +585,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
           }
           const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
           const uint8_t* const xc = xrow + 2 * kChunk * c;
+          f16x8 bx[8];                                // read together: one LDS latency per chunk
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
-            acc = mfma16x16x32_f16(dequant8_f16(wd[s], e2[s >> 1], mu[s >> 1]), bx, acc);
-          }
+          for (int s = 0; s < 8; ++s) bx[s] = *reinterpret_cast<const f16x8*>(xc + 16 * s);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc = mfma16x16x32_f16(dequant8_f16(wd[s], e2[s >> 1], mu[s >> 1]), bx[s], acc);
         }
       }
       red[wave * 64 + lane] = acc;
@@ -648,11 +649,15 @@ __global__ __launch_bounds__(64 * NW) void gemv_xres_kernel(const uint16_t* __re
       mu[b] = scale_mantissa_f16(sb[b]);
     }
     const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    // the chunk's 8 activation fragments are read together, so that one
+    // LDS latency is waited for instead of one per MFMA
+    f16x8 bx[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
-      acc[s & 1] = mfma16x16x32_f16(dequant8_f16(wd[s], sb[s >> 1], mu[s >> 1]), bx, acc[s & 1]);
-    }
+    for (int s = 0; s < 8; ++s) bx[s] = *reinterpret_cast<const f16x8*>(xc + 16 * s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      acc[s & 1] = mfma16x16x32_f16(dequant8_f16(wd[s], sb[s >> 1], mu[s >> 1]), bx[s], acc[s & 1]);
   };
 
   if constexpr (kDepth > 0) {
@@ -890,11 +895,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_xphase_kernel(const uint16_t* __
     }
     const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     const uint8_t* const xc = xrow + 2 * kChunk * cc;
+    f16x8 bx[8];                                    // read together: one LDS latency per chunk
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 bx = *reinterpret_cast<const f16x8*>(xc + 16 * s);
-      a[s & 1] = mfma16x16x32_f16(dequant8_f16(wd[s], sb[s >> 1], mu[s >> 1]), bx, a[s & 1]);
-    }
+    for (int s = 0; s < 8; ++s) bx[s] = *reinterpret_cast<const f16x8*>(xc + 16 * s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) a[s & 1] = mfma16x16x32_f16(dequant8_f16(wd[s], sb[s >> 1], mu[s >> 1]), bx[s], a[s & 1]);
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
