@@ -450,7 +450,7 @@ __device__ __forceinline__ void f8_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int MT, int R>
+template <int MT, int R, bool kUniform>
 __global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t* __restrict__ xq,
                                                                 const float* __restrict__ xs, int M, int K,
                                                                 const uint8_t* __restrict__ wq,
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t*
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int nchunks = K / 128;
-  const int npanels = K / G::pk;
+  const int npanels = (K + G::pk - 1) / G::pk;         // the last one partial when K % pk != 0
   // transpose write: load lane l holds row 8 j + l / 8, piece l % 8 (slot piece ^ (row & 7))
   const int wwr = 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
   // operand read: row r, pieces 2 g and 2 g + 1
@@ -501,15 +501,17 @@ __global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t*
           wr[decltype(SLOT)::value][t][j] =
               __builtin_amdgcn_raw_buffer_load_b128(wres, wlane + (16 * t + 8 * j) * K, 128 * c, 2 /* nontemporal */);
     };
-    // x panel P into buffer P % 2: copy i of this wavefront fills panel bytes [1 KiB (i NW + wave), + 1 KiB)
-    auto x_copy = [&](int P) {
-      uint8_t* const buf = xsl[P & 1];
+    // x panel P into buffer b: copy i of this wavefront fills panel bytes [1 KiB (i NW + wave), + 1 KiB);
+    // columns past K (a partial last panel) read the row's last 16 (never used)
+    auto x_copy = [&](int P, int b) {
+      uint8_t* const buf = xsl[b];
 #pragma unroll
       for (int i = 0; i < G::xcopies; ++i) {
         const int off = 1024 * (i * NW + wave) + 16 * lane;
         const int m = off / G::pk, slot = (off % G::pk) >> 4;
         const int piece = slot ^ (m & 7);
-        __builtin_amdgcn_global_load_lds((const void*)(xq + (int64_t)min(m, M - 1) * K + P * G::pk + 16 * piece),
+        const int col = min(P * G::pk + 16 * piece, K - 16);
+        __builtin_amdgcn_global_load_lds((const void*)(xq + (int64_t)min(m, M - 1) * K + col),
                                          (fp8_lds_ptr_t)(buf + 1024 * (i * NW + wave)), 16, 0, 0);
       }
     };
@@ -519,18 +521,32 @@ __global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t*
       constexpr int u = decltype(U_)::value;
       const int cc = c % G::pchunks;                    // chunk within its panel
       const int P = c / G::pchunks;
-      // wait for batch(c); batch(c + 1) and, after a panel start, the copies
-      // of panel P + 1 (issued after batch(c)) may stay in flight
-      if (c + 1 < nchunks) {
-        if (u == 1 && cc == 1 && P + 1 < npanels) f8_wait_vmcnt<kBatch + G::xcopies>();
+      if constexpr (kUniform) {
+        // wait for batch(c); batch(c + 1) and, one step after a u = 0 step,
+        // the x copies that step issued (after batch(c)) may stay in flight.
+        // Every step issues the same loads whatever c is (past the end they
+        // repeat the last chunk or panel, never used), so the count of loads
+        // issued after each one is fixed, these waits are exact, and the
+        // compiler's own waits need not assume the worst.
+        if constexpr (u == 1) f8_wait_vmcnt<kBatch + G::xcopies>();
         else f8_wait_vmcnt<kBatch>();
+        if constexpr (u == 0) {
+          if (cc == 0) asm volatile("s_barrier" ::: "memory");   // panel P is complete; panel P - 1 is no longer read
+        }
       } else {
-        f8_wait_vmcnt<0>();
-      }
-      if constexpr (u == 0) {
-        if (cc == 0) {
-          asm volatile("s_barrier" ::: "memory");       // panel P is complete; panel P - 1 is no longer read
-          if (P + 1 < npanels) x_copy(P + 1);
+        // wait for batch(c); batch(c + 1) and, after a panel start, the copies
+        // of panel P + 1 (issued after batch(c)) may stay in flight
+        if (c + 1 < nchunks) {
+          if (u == 1 && cc == 1 && P + 1 < npanels) f8_wait_vmcnt<kBatch + G::xcopies>();
+          else f8_wait_vmcnt<kBatch>();
+        } else {
+          f8_wait_vmcnt<0>();
+        }
+        if constexpr (u == 0) {
+          if (cc == 0) {
+            asm volatile("s_barrier" ::: "memory");     // panel P is complete; panel P - 1 is no longer read
+            if (P + 1 < npanels) x_copy(P + 1, (P + 1) & 1);
+          }
         }
       }
       // chunk c: registers -> this wavefront's LDS, then refill the slot with batch(c + 2)
@@ -539,7 +555,15 @@ __global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t*
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           *reinterpret_cast<u32x4*>(wmine + 2048 * t + 1024 * j + wwr) = wr[u & 1][t][j];
-      if (c + 2 < nchunks) issue(c + 2, std::integral_constant<int, u & 1>{});
+      if constexpr (kUniform) {
+        // every u = 0 step copies panel P + 1 into the other buffer (again
+        // when not a panel start: the same bytes to the same place; that
+        // buffer's panel P - 1 is no longer read after panel P's barrier)
+        if constexpr (u == 0) x_copy(min(P + 1, npanels - 1), (P + 1) & 1);
+        issue(min(c + 2, nchunks - 1), std::integral_constant<int, u & 1>{});
+      } else {
+        if (c + 2 < nchunks) issue(c + 2, std::integral_constant<int, u & 1>{});
+      }
       fp8_i32x8 bx[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -563,7 +587,7 @@ __global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t*
       }
     };
 
-    x_copy(0);
+    x_copy(0, 0);
     issue(0, std::integral_constant<int, 0>{});
     issue(1, std::integral_constant<int, 1>{});
     for (int c = 0; c < nchunks; c += 4) {
@@ -609,10 +633,10 @@ __global__ __launch_bounds__(64 * kF8RingNW) void fp8_ring_kernel(const uint8_t*
   }
 }
 
-template <int MT, int R>
+template <int MT, int R, bool kUniform>
 static hipError_t fp8_ring_launch(const uint8_t* xq, const float* xs, int M, int K, const uint8_t* wq,
                                   const float* ws, int N, const void* bias, void* y, hipStream_t stream) {
-  const void* fn = (const void*)fp8_ring_kernel<MT, R>;
+  const void* fn = (const void*)fp8_ring_kernel<MT, R, kUniform>;
   const int nblocks = (N + kF8RingNW * R * 16 - 1) / (kF8RingNW * R * 16);
   const int dev = current_device();
   const dim3 grid(std::min(nblocks, device_cus(dev) * blocks_per_cu(fn, dev, 64 * kF8RingNW, 0)));
@@ -783,11 +807,14 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* xs, int64_t M, int64_
   // stays ahead where it applies: 95 against 115 us at K = 4096).  The ring
   // kernel's buffer offsets within a wavefront's 64 rows are 32-bit.
   if (K % 512 == 0 && K <= (1 << 24) && M <= 64) {
-    if (M <= 16) return fp8_ring_launch<1, 4>(xq, xs, m, k, wq, ws, n, bias, y, stream);
     // four tiles per wavefront up to 32 rows (two more weight chunks in
-    // flight per wavefront); at 64 rows four would spill, so two
-    if (M <= 32) return fp8_ring_launch<2, 4>(xq, xs, m, k, wq, ws, n, bias, y, stream);
-    return fp8_ring_launch<4, 2>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+    // flight per wavefront); at 64 rows four would spill, so two.  The
+    // 17-32-row form issues the same loads every step (120 -> 95 us at the
+    // 8B shape, M = 32; it no longer spills); the others measured 2-4 %
+    // slower that way and keep their loads conditional.
+    if (M <= 16) return fp8_ring_launch<1, 4, false>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+    if (M <= 32) return fp8_ring_launch<2, 4, true>(xq, xs, m, k, wq, ws, n, bias, y, stream);
+    return fp8_ring_launch<4, 2, false>(xq, xs, m, k, wq, ws, n, bias, y, stream);
   }
   switch (std::min<int64_t>((M + 15) / 16, 8)) {
     case 1: return fp8_gemm_launch<1>(xq, xs, m, k, wq, ws, n, bias, y, stream);

@@ -80,6 +80,8 @@ def test_gemm_matches_oracle(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k,with_bias", [(1, 3000, 8192, True), (2, 2100, 8192, False),
+                                             (5, 3000, 2560, True), (3, 1100, 7168, False), (20, 2100, 1536, True),
+                                             (4, 1027, 512, False),
                                              (3, 140000, 512, True), (20, 70000, 512, False), (28, 140000, 512, True),
                                              (16, 1300, 8192, False), (24, 1030, 8192, True), (40, 2100, 1024, False),
                                              (40, 70000, 512, True), (64, 900, 8192, True)])
@@ -88,7 +90,9 @@ def test_ring_kernel_panels_blocks_and_bias(m, n, k, with_bias):
     beyond the dot kernel's K): several x panels per block at K = 8192 (4 at
     M <= 16, 8 at M <= 32, 16 beyond),
     more 512-row (M <= 32) or 256-row (M > 32) blocks than compute units at
-    N = 140000 / 70000, rows past N and M in the last tiles, and the bias."""
+    N = 140000 / 70000, rows past N and M in the last tiles, and the bias;
+    K not a multiple of the panel width (a partial last panel: K = 2560 and
+    7168 at M <= 16, 1536 at M <= 32) and K below it (K = 512 at M <= 16)."""
     w = wl.random_weight_bits(n, k, sigma=0.02, seed=n + 3 * k)
     x = wl.random_activation_bits(m, k, seed=m + 11)
     wq, ws = F.quantize_rows(w)
